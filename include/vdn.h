@@ -1,0 +1,175 @@
+/*
+ * vdn.h — C ABI of the MI355X (gfx950) Video DeltaNet hybrid video-to-video
+ * attention layer, forward pass.
+ *
+ * The layer (sources cited by page title and section):
+ *  - Softmax branch: latent frames form chunks of `chunk_frames` (five); a query
+ *    chunk sees its own chunk and `window_chunks` chunks either side; every
+ *    frame also sees the first and last frame, those two anchors see the whole
+ *    sequence, and text tokens stay visible as softmax keys.
+ *    [PaperDaily "伯克利与Impossible视频生成:14.3秒视频6.70秒去噪" §二;
+ *     arXiv listing "Video DeltaNet: A Video-Native Hybrid Attention for
+ *     Livestream Video Generation", abstract]
+ *  - Linear branch (Video Delta Attention): per frame the state is updated
+ *    once, jointly over all the frame's tokens, by
+ *    S <- (alpha_f S + B_f)(I + A_f)^-1 with A_f = sum beta k k^T and
+ *    B_f = sum beta v k^T.  A forward and a backward state start from half of
+ *    the text write, skip the anchors, and each frame reads only the far
+ *    frames outside its window; the two reads are summed.
+ *    [deepmagic blog "生成比播放還快：Video DeltaNet 用 11 秒產出 14 秒 768p
+ *     影片", section 用兩條分支取代一條; PaperDaily §三, §四]
+ *  - Merge: the summed read is RMS-normalised, then each branch is scaled by
+ *    its own sigmoid gate and the two are added.  [PaperDaily §三]
+ *
+ * Conventions for every entry point:
+ *  - All tensors are dense, row-major, innermost dimension unit-stride, in
+ *    device memory owned by the caller.  Token-major "BNHD" layout:
+ *      q, k, v, o        [B, T*P, H, d]           (layout->dtype)
+ *      text_k, text_v    [B, L, H, d]             (layout->dtype)
+ *      beta              [B, T*P + L, H]          float32, video tokens then text
+ *      alpha             [B, T, H]                float32, one decay per frame
+ *      gate_logits       [B, T*P, H, 2]           float32, [...,0] softmax gate,
+ *                                                 [...,1] linear gate
+ *  - Device pointers must be 16-byte aligned.  text_k/text_v may be NULL when
+ *    L == 0.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    leave every output untouched.  Work is enqueued on `stream`; the call
+ *    never synchronises the host.  Kernel faults surface through the stream.
+ *  - The library never allocates device memory in these calls; scratch memory
+ *    is the caller's `workspace`.
+ *  - Calls are re-entrant; concurrent calls must use distinct workspaces.
+ */
+#ifndef VDN_H
+#define VDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDN_VERSION 100   /* 1.0.0 */
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  VDN_ERR_BAD_SHAPE = 2,           /* a size is out of range */
+  VDN_ERR_UNSUPPORTED = 3,         /* dtype / head size not implemented */
+  VDN_ERR_MISALIGNED = 4,          /* a device pointer is not 16-byte aligned */
+  VDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the required size */
+  VDN_ERR_HIP = 6                  /* a HIP launch failed; see vdn_last_hip_error */
+} vdn_status_t;
+
+typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype_t;
+
+/* Shape and geometry of one call.
+ *  batch, heads        B, H >= 1
+ *  head_dim_k/_v       d; equal, in {16, 32, 64, 128}
+ *  frames              T >= 1 latent frames
+ *  tokens_per_frame    P >= 1 (frame t holds video tokens t*P .. t*P+P-1)
+ *  chunk_frames        C >= 1 (five in the pages)
+ *  window_chunks       w >= 0 (one in the pages: previous and next chunk)
+ *  anchor_first/_last  0/1: frame 0 / frame T-1 is a boundary anchor
+ *  text_tokens         L >= 0 text tokens, visible softmax keys for every query
+ *  dtype               vdn_dtype_t of q, k, v, text_k, text_v, o
+ *  softmax_scale       0 -> 1/sqrt(d)
+ *  rms_eps             0 -> 1e-6
+ * Limits: B*T*P*H*d and (T*P+L)*H*d below 2^31 elements per batch entry set. */
+typedef struct {
+  int32_t batch, heads, head_dim_k, head_dim_v;
+  int32_t frames, tokens_per_frame;
+  int32_t chunk_frames, window_chunks;
+  int32_t anchor_first, anchor_last;
+  int32_t text_tokens;
+  int32_t dtype;
+  float softmax_scale;
+  float rms_eps;
+} vdn_layout_t;
+
+/* Library version (VDN_VERSION of the built library). */
+int vdn_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* vdn_status_str(vdn_status_t status);
+
+/* hipError_t of the most recent VDN_ERR_HIP on the calling thread (0 if none). */
+int vdn_last_hip_error(void);
+
+/* Host-only check of a layout: returns VDN_OK, VDN_ERR_NULL_ARG,
+ * VDN_ERR_BAD_SHAPE or VDN_ERR_UNSUPPORTED.  Touches no device. */
+vdn_status_t vdn_validate_layout(const vdn_layout_t* layout);
+
+/* Number of chunks ceil(T / C); slot index of the text-only state in the
+ * per-chunk state arrays below.  0 for an invalid layout.  Host only. */
+int32_t vdn_num_chunks(const vdn_layout_t* layout);
+
+/* Bytes of workspace vdn_hybrid_attn_fwd needs for `layout` (0 if the layout is
+ * invalid).  Host only. */
+size_t vdn_hybrid_attn_workspace_size(const vdn_layout_t* layout);
+
+/* The whole layer: O = sigmoid(g0) * O_soft + sigmoid(g1) * RMSNorm(R q), with
+ * O_soft the block-sparse softmax branch and R the summed forward/backward
+ * VDA states of the query's chunk (the text write alone for anchor frames).
+ * o must not alias any input.  workspace: device memory of at least
+ * vdn_hybrid_attn_workspace_size(layout) bytes, 256-byte aligned; its contents
+ * on entry are ignored.  [all sections cited above] */
+vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
+                                 const void* text_k, const void* text_v,
+                                 const float* beta, const float* alpha,
+                                 const float* gate_logits,
+                                 const vdn_layout_t* layout, void* o,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* ---- Per-stage entry points: the same kernels the layer runs, one stage at
+ * ---- a time (for checking and profiling each stage). ---- */
+
+/* Softmax branch alone: o_soft [B, T*P, H, d] (layout->dtype) gets, for every
+ * video query, one softmax over the keys of its visible frames together with
+ * all text keys, times the matching values.  [PaperDaily §二; arXiv abstract] */
+vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v,
+                             const void* text_k, const void* text_v,
+                             const vdn_layout_t* layout, void* o_soft,
+                             hipStream_t stream);
+
+/* Frame statistics: for every frame f < T and for the text block (slot T),
+ * A[b,h,slot] = sum_i beta_i k_i k_i^T and B[b,h,slot] = sum_i beta_i v_i k_i^T
+ * over the slot's tokens.  A_out, B_out: float32 [B, H, T+1, d, d] (row index
+ * first).  The text slot is zero when L == 0.
+ * [deepmagic blog, 用兩條分支取代一條; PaperDaily §四] */
+vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k,
+                          const void* text_v, const float* beta,
+                          const vdn_layout_t* layout, float* A_out, float* B_out,
+                          hipStream_t stream);
+
+/* Bytes of workspace vdn_vda_factor_scan needs (0 if invalid).  Host only. */
+size_t vdn_vda_factor_scan_workspace_size(const vdn_layout_t* layout);
+
+/* Factor and scan: A_io holds the frame Grams from vdn_vda_gram and is
+ * overwritten with (I + A)^-1 for the frames the scan uses (Cholesky
+ * I + A = L L^T, then L^-T L^-1) and for the text slot.  B is read only.
+ * R_out: float32 [B, H, nc+1, d, d] with nc = vdn_num_chunks(layout);
+ * R_out[c] = S_fwd(c) + S_bwd(c), the summed states a non-anchor query frame of
+ * chunk c reads, and R_out[nc] = S_x, the full text write (what anchor frames
+ * read).  Both states start at S_x / 2 and skip anchor frames.
+ * [deepmagic blog, 用兩條分支取代一條; PaperDaily §三, §四] */
+vdn_status_t vdn_vda_factor_scan(float* A_io, const float* B, const float* alpha,
+                                 const vdn_layout_t* layout, float* R_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Read + RMSNorm + gates + merge: o = sigmoid(g0) * o_soft
+ *   + sigmoid(g1) * RMSNorm(R[c] q), with R from vdn_vda_factor_scan
+ * (slot nc for anchor frames).  o may equal o_soft (in place); otherwise no
+ * aliasing.  [PaperDaily §三] */
+vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R,
+                       const float* gate_logits, const vdn_layout_t* layout,
+                       void* o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_H */

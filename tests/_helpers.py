@@ -1,0 +1,67 @@
+"""Shared helpers for the parity tests: device transfer, oracle layouts and
+error metrics (relative Frobenius error, the tolerance metric of the tests)."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import vdn_oracle as O
+from video_diffusion_hybrid_block_amd import synth
+
+# Output tolerances: relative Frobenius error of O against the oracle.
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from video_diffusion_hybrid_block_amd import binding
+    binding.lib()   # must load on a GPU machine: no fallback
+
+
+def workload(name, **over) -> synth.Workload:
+    return dataclasses.replace(synth.WORKLOADS[name], **over) if over else synth.WORKLOADS[name]
+
+
+def custom(name, *, batch, heads, head_dim, frames, tokens_per_frame, text_tokens, dtype,
+           seed=7, chunk_frames=5, window_chunks=1, **kw) -> synth.Workload:
+    return synth.Workload(name, batch, heads, head_dim, frames, tokens_per_frame, text_tokens,
+                          dtype, seed, chunk_frames=chunk_frames, window_chunks=window_chunks, **kw)
+
+
+def oracle_layout(w: synth.Workload, **over) -> O.Layout:
+    kw = synth.layout_kwargs(w)
+    kw.update(over)
+    return O.Layout(**kw)
+
+
+def to_dev(inp: dict, dtype: str) -> dict:
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for key, arr in inp.items():
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+        if key in ("q", "k", "v", "text_k", "text_v"):
+            t = t.to(tdt)
+        out[key] = t.cuda()
+    return out
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def sample_tokens(w: synth.Workload, rng) -> np.ndarray:
+    """Tokens spanning anchor, edge and interior frames, tile starts and the
+    ragged tail of every frame."""
+    T, P = w.frames, w.tokens_per_frame
+    frames = sorted({f for f in (0, 1, 4, 5, 9, 10, T // 2, T - 6, T - 5, T - 2, T - 1) if 0 <= f < T})
+    local = {0, 1, 31, 32, 127, 128, P - 113, P - 33, P - 2, P - 1}
+    local |= set(rng.integers(0, P, size=4).tolist())
+    local = sorted(x for x in local if 0 <= x < P)
+    return np.array([f * P + x for f in frames for x in local], dtype=np.int64)

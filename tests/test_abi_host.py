@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI (CPU only, no kernel launches): exported
+symbols, layout validation and error codes, workspace sizing, and the
+kernels' frame geometry against the oracle's definitions."""
+import ctypes
+import itertools
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from oracle import vdn_oracle as O
+from video_diffusion_hybrid_block_amd import binding as V
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "vdn.h")).read()
+    return set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(vdn_\w+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = V.lib()
+    declared = _header_functions()
+    assert declared == set(V.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert V.version() == 100
+
+
+def _lay(**kw):
+    base = dict(batch=1, heads=24, head_dim=128, frames=60, tokens_per_frame=1008,
+                text_tokens=512, dtype="bf16")
+    base.update(kw)
+    return V.make_layout(**base)
+
+
+def test_validate_layout_error_codes():
+    assert V.validate_layout(_lay()) == 0
+    assert V.validate_layout(_lay(dtype="f32", head_dim=16)) == 0
+    assert V.validate_layout(_lay(frames=0)) == 2
+    assert V.validate_layout(_lay(tokens_per_frame=0)) == 2
+    assert V.validate_layout(_lay(text_tokens=-1)) == 2
+    assert V.validate_layout(_lay(chunk_frames=0)) == 2
+    assert V.validate_layout(_lay(window_chunks=-1)) == 2
+    assert V.validate_layout(_lay(head_dim=48)) == 3
+    assert V.validate_layout(_lay(head_dim=256)) == 3
+    bad = _lay()
+    bad.dtype = 7
+    assert V.validate_layout(bad) == 3
+    bad = _lay()
+    bad.head_dim_v = 64
+    assert V.validate_layout(bad) == 3
+    bad = _lay()
+    bad.softmax_scale = float("nan")
+    assert V.validate_layout(bad) == 2
+    assert V.validate_layout(_lay(frames=1 << 20, tokens_per_frame=1 << 12)) == 2
+    assert V.lib().vdn_validate_layout(None) == 1
+
+
+def test_status_strings():
+    lib = V.lib()
+    for code in range(7):
+        assert lib.vdn_status_str(code)
+    assert lib.vdn_status_str(99) == b"unknown status"
+
+
+def test_workspace_size_and_chunks():
+    lay = _lay()
+    assert V.num_chunks(lay) == 12
+    ws = V.workspace_size(lay)
+    d2 = 128 * 128 * 4
+    assert ws >= 24 * (2 * 61 + 3 * 13) * d2
+    assert V.workspace_size(_lay(frames=120)) > ws
+    assert V.workspace_size(_lay(frames=0)) == 0
+    assert V.num_chunks(_lay(frames=61)) == 13
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="argument-error paths are checked without a GPU")
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = V.lib()
+    lay = _lay(batch=1, heads=1, frames=2, tokens_per_frame=4, text_tokens=0, head_dim=16)
+    ok = ctypes.c_void_p(0x10000)         # aligned fake pointers: never dereferenced
+    odd = ctypes.c_void_p(0x10004)
+    nul = None
+    ref = ctypes.byref(lay)
+    args = [ok, ok, ok, nul, nul, ok, ok, ok, ref, ok, ok, 1 << 40, nul]
+    a = list(args); a[0] = nul
+    assert lib.vdn_hybrid_attn_fwd(*a) == 1
+    a = list(args); a[9] = odd
+    assert lib.vdn_hybrid_attn_fwd(*a) == 4
+    a = list(args); a[11] = 16
+    assert lib.vdn_hybrid_attn_fwd(*a) == 5
+    bad = _lay(head_dim=48)
+    a = list(args); a[8] = ctypes.byref(bad)
+    assert lib.vdn_hybrid_attn_fwd(*a) == 3
+    lay_t = _lay(batch=1, heads=1, frames=2, tokens_per_frame=4, text_tokens=3, head_dim=16)
+    a = list(args); a[8] = ctypes.byref(lay_t)
+    assert lib.vdn_hybrid_attn_fwd(*a) == 1            # text tensors missing
+    assert lib.vdn_softmax_fwd(ok, ok, nul, nul, nul, ref, ok, nul) == 1
+    assert lib.vdn_vda_gram(ok, ok, nul, nul, odd, ref, ok, ok, nul) == 4
+    assert lib.vdn_vda_factor_scan(ok, ok, ok, ref, ok, ok, 0, nul) == 5
+    assert lib.vdn_merge(ok, ok, ok, ok, ref, nul, nul) == 1
+
+
+@pytest.fixture(scope="module")
+def geometry_probe(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("geo") / "geometry_probe")
+    cmd = ["hipcc", "-O1", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "video_diffusion_hybrid_block_amd", "csrc"),
+           os.path.join(ROOT, "tests", "geometry_probe.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out
+
+
+def _segments_from_oracle(lay, t):
+    """Visible video frames of t as merged token ranges."""
+    P = lay.tokens_per_frame
+    frames = O.visible_frames(lay, t)
+    segs = []
+    for f in frames:
+        if segs and segs[-1][0] + segs[-1][1] == f * P:
+            segs[-1][1] += P
+        else:
+            segs.append([f * P, P])
+    return [tuple(s) for s in segs]
+
+
+@pytest.mark.parametrize("C,w", [(5, 1), (2, 1), (3, 2), (1, 1), (4, 0), (5, 9)])
+def test_kernel_geometry_matches_oracle(geometry_probe, C, w):
+    for T, (af, al) in itertools.product(range(1, 31), [(1, 1), (0, 0), (1, 0), (0, 1)]):
+        P = 3
+        r = subprocess.run([geometry_probe, str(T), str(C), str(w), str(af), str(al), str(P)],
+                           capture_output=True, text=True, check=True)
+        lines = r.stdout.split("\n")
+        lay = O.Layout(batch=1, heads=1, head_dim=16, frames=T, tokens_per_frame=P, text_tokens=0,
+                       chunk_frames=C, window_chunks=w, anchor_first=bool(af), anchor_last=bool(al))
+        segs = {}
+        slots = None
+        for ln in lines:
+            f = ln.split()
+            if not f:
+                continue
+            if f[0] == "seg":
+                vals = list(map(int, f[2:]))
+                segs[int(f[1])] = [tuple(vals[i:i + 2]) for i in range(0, len(vals), 2)]
+            elif f[0] == "slots":
+                slots = list(map(int, f[1:]))
+        for t in range(T):
+            assert segs[t] == _segments_from_oracle(lay, t), (T, C, w, af, al, t)
+        # frames whose statistics the scans need = union of the far sets
+        needed = sorted(set().union(*[set(O.far_forward(lay, t)) | set(O.far_backward(lay, t))
+                                      for t in range(T)]))
+        assert slots == needed + [T], (T, C, w, af, al)

@@ -1,0 +1,331 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every comparison uses the same seeded inputs on both sides.  Metric: relative
+Frobenius error ||got - ref|| / ||ref||; bounds: 1e-4 (fp32 tensors) and 2e-2
+(bf16 tensors) on the layer output, tighter on the fp32 intermediate stages
+(derivations next to each bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import vdn_oracle as O
+from video_diffusion_hybrid_block_amd import binding as V
+from video_diffusion_hybrid_block_amd import synth
+
+from _helpers import TOL, custom, oracle_layout, rel_err, require_gpu, sample_tokens, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def geo_kw(w):
+    return dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+                window_chunks=w.window_chunks)
+
+
+def run_layer(w, dev, **kw):
+    L = w.text_tokens
+    out = V.hybrid_attn(dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+                        dev["text_v"] if L else None, dev["beta"], dev["alpha"],
+                        dev["gate_logits"], **geo_kw(w), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer, full tensors
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16"])
+def test_layer_full_parity(name):
+    require_gpu()
+    w = workload(name)
+    _announce(f"layer full {name}")
+    inp = synth.make_inputs(w)
+    ref = O.hybrid_attn(inp, oracle_layout(w))
+    out = run_layer(w, to_dev(inp, w.dtype)).float().cpu().numpy()
+    err = rel_err(out, ref)
+    worst = max(rel_err(out[b, :, h], ref[b, :, h]) for b in range(w.batch) for h in range(w.heads))
+    print(f"{name}: rel err {err:.3e}, worst head {worst:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[w.dtype]
+
+
+EDGE = [
+    # ragged frames over several chunks, batch 2, head count not a multiple of 8
+    dict(name="ragged", batch=2, heads=3, head_dim=64, frames=7, tokens_per_frame=50,
+         text_tokens=5, dtype="bf16", chunk_frames=2),
+    # one frame: both anchors coincide, every query is an anchor query, no text
+    dict(name="one_frame", batch=1, heads=2, head_dim=128, frames=1, tokens_per_frame=130,
+         text_tokens=0, dtype="bf16"),
+    dict(name="two_frames", batch=1, heads=2, head_dim=128, frames=2, tokens_per_frame=33,
+         text_tokens=7, dtype="bf16"),
+    dict(name="no_anchor_d32", batch=1, heads=4, head_dim=32, frames=12, tokens_per_frame=70,
+         text_tokens=3, dtype="bf16", chunk_frames=3, anchor_first=False, anchor_last=False),
+    dict(name="first_anchor_only", batch=1, heads=2, head_dim=64, frames=14, tokens_per_frame=40,
+         text_tokens=6, dtype="bf16", chunk_frames=2, anchor_last=False),
+    # window wider than the video: dense softmax, linear read = text write
+    dict(name="dense_window", batch=1, heads=2, head_dim=128, frames=9, tokens_per_frame=40,
+         text_tokens=9, dtype="bf16", chunk_frames=3, window_chunks=5),
+    dict(name="one_token_frames", batch=1, heads=2, head_dim=128, frames=13, tokens_per_frame=1,
+         text_tokens=1, dtype="bf16", chunk_frames=2),
+    dict(name="no_text", batch=1, heads=2, head_dim=128, frames=15, tokens_per_frame=64,
+         text_tokens=0, dtype="bf16"),
+    dict(name="long_window_tail", batch=1, heads=1, head_dim=128, frames=23, tokens_per_frame=129,
+         text_tokens=130, dtype="bf16", chunk_frames=4),
+    dict(name="bf16_d16_valu", batch=1, heads=2, head_dim=16, frames=8, tokens_per_frame=24,
+         text_tokens=4, dtype="bf16", chunk_frames=2),
+    dict(name="f32_d64", batch=1, heads=2, head_dim=64, frames=11, tokens_per_frame=20,
+         text_tokens=4, dtype="f32", chunk_frames=2),
+    dict(name="f32_d128_chunk1", batch=1, heads=1, head_dim=128, frames=6, tokens_per_frame=9,
+         text_tokens=2, dtype="f32", chunk_frames=1, window_chunks=2),
+    dict(name="f32_d32", batch=2, heads=2, head_dim=32, frames=10, tokens_per_frame=12,
+         text_tokens=0, dtype="f32", chunk_frames=3),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c["name"] for c in EDGE])
+def test_layer_edge_cases(case):
+    require_gpu()
+    case = dict(case)
+    af = case.pop("anchor_first", True)
+    al = case.pop("anchor_last", True)
+    w = custom(**case)
+    _announce(f"edge {case['name']}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w, anchor_first=af, anchor_last=al)
+    ref = O.hybrid_attn(inp, lay)
+    out = run_layer(w, to_dev(inp, w.dtype), anchor_first=af, anchor_last=al)
+    out = out.float().cpu().numpy()
+    err = rel_err(out, ref)
+    print(f"{case['name']}: rel err {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# Whole layer at full size, sampled outputs
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["768p", "long_120f", "stress_lowrank"])
+def test_layer_full_size_sampled(name):
+    require_gpu()
+    w = workload(name)
+    _announce(f"layer sampled {name}")
+    inp = synth.make_inputs(w)
+    out = run_layer(w, to_dev(inp, w.dtype))
+    lay = oracle_layout(w)
+    rng = np.random.default_rng(0)
+    got_all, ref_all = [], []
+    for b in range(w.batch):
+        for h in sorted({0, w.heads // 2, w.heads - 1}):
+            tok = sample_tokens(w, rng)
+            ref = O.hybrid_attn_rows(inp, lay, b, h, tok)
+            got = out[b, torch.from_numpy(tok).cuda(), h].float().cpu().numpy()
+            e = rel_err(got, ref)
+            print(f"{name} b{b} h{h}: {len(tok)} tokens rel err {e:.3e}")
+            got_all.append(got)
+            ref_all.append(ref)
+    err = rel_err(np.concatenate(got_all), np.concatenate(ref_all))
+    assert torch.isfinite(out).all().item()
+    assert err <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# Stages through the per-stage entry points
+# ---------------------------------------------------------------------------
+STAGE_CASES = ["tiny_f32", "small_bf16"]
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["768p"])
+def test_stage_gram(name):
+    """A and B per frame and for the text block.  fp32 accumulation of hi/lo
+    bf16 products: error ~2^-16 relative per product, so 2e-5 relative."""
+    require_gpu()
+    w = workload(name)
+    _announce(f"gram {name}")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    A, B = V.vda_gram(dev["k"], dev["v"], dev["text_k"] if L else None,
+                      dev["text_v"] if L else None, dev["beta"], **geo_kw(w))
+    torch.cuda.synchronize()
+    P, N = w.tokens_per_frame, w.video_tokens
+    slots = list(range(w.frames)) + [w.frames]
+    if w.frames > 20:
+        slots = [0, 1, 2, w.frames // 2, w.frames - 2, w.frames - 1, w.frames]
+    heads = range(w.heads) if w.heads <= 8 else [0, w.heads // 2, w.heads - 1]
+    errs = []
+    for b in range(w.batch):
+        for h in heads:
+            for s in slots:
+                if s == w.frames:
+                    rA, rB = O.frame_stats(inp["text_k"][b, :, h], inp["text_v"][b, :, h],
+                                           inp["beta"][b, N:, h])
+                else:
+                    rows = slice(s * P, (s + 1) * P)
+                    rA, rB = O.frame_stats(inp["k"][b, rows, h], inp["v"][b, rows, h],
+                                           inp["beta"][b, rows, h])
+                errs.append(rel_err(A[b, h, s].cpu().numpy(), rA))
+                errs.append(rel_err(B[b, h, s].cpu().numpy(), rB))
+    print(f"{name}: gram worst rel err {max(errs):.3e}")
+    assert max(errs) <= 2e-5
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["768p", "stress_lowrank"])
+def test_stage_factor_scan(name):
+    """Summed states per chunk and the text write, from the GPU statistics.
+    fp32 Cholesky/inverse (error ~cond * 6e-8) and, for bf16 layouts, a
+    three-pass bf16 product in the scan (~2^-16 per step): bound 1e-4 for fp32
+    layouts, 2e-3 for bf16 layouts (checked against the fp64 oracle on the same
+    statistics)."""
+    require_gpu()
+    w = workload(name)
+    _announce(f"factor_scan {name}")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    A, B = V.vda_gram(dev["k"], dev["v"], dev["text_k"] if L else None,
+                      dev["text_v"] if L else None, dev["beta"], **geo_kw(w))
+    A_host, B_host = A.double().cpu().numpy(), B.double().cpu().numpy()
+    R = V.vda_factor_scan(A, B, dev["alpha"], dtype=w.dtype, text_tokens=L, **geo_kw(w))
+    torch.cuda.synchronize()
+    R = R.cpu().numpy()
+    lay = oracle_layout(w)
+    nc = lay.num_chunks
+    heads = range(w.heads) if w.heads <= 8 else [0, w.heads - 1]
+    errs = []
+    for b in range(w.batch):
+        for h in heads:
+            # oracle folds on the GPU's own statistics
+            stats = {f: (A_host[b, h, f], B_host[b, h, f]) for f in range(w.frames)}
+            S0 = 0.5 * O.vda_update(np.zeros_like(B_host[b, h, w.frames]), A_host[b, h, w.frames],
+                                    B_host[b, h, w.frames]) if L else np.zeros_like(R[0, 0, 0])
+            alpha_bh = inp["alpha"][b, :, h].astype(np.float64)
+            errs.append(rel_err(R[b, h, nc], 2 * S0))
+            for c in range(nc):
+                t = [f for f in range(c * lay.chunk_frames, min((c + 1) * lay.chunk_frames, w.frames))
+                     if f not in O.anchor_frames(lay)]
+                if not t:
+                    continue
+                ref = O.forward_state(S0, lay, t[0], stats, alpha_bh) + \
+                    O.backward_state(S0, lay, t[0], stats, alpha_bh)
+                errs.append(rel_err(R[b, h, c], ref))
+    tol = 1e-4 if w.dtype == "f32" else 2e-3
+    print(f"{name}: factor/scan worst rel err {max(errs):.3e}")
+    assert max(errs) <= tol
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["768p"])
+def test_stage_softmax(name):
+    """Softmax branch alone: bf16 P and bf16 output rounding (~2^-9) bound the
+    error well below 2e-2; fp32 path 1e-5."""
+    require_gpu()
+    w = workload(name)
+    _announce(f"softmax {name}")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    o = V.softmax_fwd(dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+                      dev["text_v"] if L else None, **geo_kw(w))
+    torch.cuda.synchronize()
+    lay = oracle_layout(w)
+    rng = np.random.default_rng(1)
+    heads = range(w.heads) if w.heads <= 8 else [0, w.heads // 2, w.heads - 1]
+    got_all, ref_all = [], []
+    for b in range(w.batch):
+        for h in heads:
+            tok = np.arange(w.video_tokens) if w.video_tokens <= 4000 else sample_tokens(w, rng)
+            ref_all.append(O.softmax_rows(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"],
+                                          lay, b, h, tok))
+            got_all.append(o[b, torch.from_numpy(tok).cuda(), h].float().cpu().numpy())
+    err = rel_err(np.concatenate(got_all), np.concatenate(ref_all))
+    print(f"{name}: softmax rel err {err:.3e}")
+    assert err <= (1e-5 if w.dtype == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("name", STAGE_CASES)
+def test_stage_merge(name):
+    """Merge given the oracle's states (as fp32) and softmax output (rounded
+    to the tensor dtype): isolates read + RMSNorm + gates."""
+    require_gpu()
+    w = workload(name)
+    _announce(f"merge {name}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    nc = lay.num_chunks
+    d = w.head_dim
+    o_soft = O.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
+    o_soft = o_soft.astype(np.float32)
+    if w.dtype == "bf16":
+        o_soft = synth.round_bf16(o_soft)
+    R = np.zeros((w.batch, w.heads, nc + 1, d, d), np.float32)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            per_frame = O.chunk_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], inp["beta"],
+                                       inp["alpha"], lay, b, h)
+            for c in range(nc):
+                R[b, h, c] = per_frame[min(c * lay.chunk_frames + 1, w.frames - 1)]
+            R[b, h, nc] = per_frame[0]            # anchor frame 0 reads the text write
+    # reference: merge with exactly these R and o_soft
+    ref = np.zeros(inp["q"].shape)
+    P = w.tokens_per_frame
+    for t in range(w.frames):
+        slot = nc if t in O.anchor_frames(lay) else t // lay.chunk_frames
+        rows = slice(t * P, (t + 1) * P)
+        for b in range(w.batch):
+            for h in range(w.heads):
+                o_lin = inp["q"][b, rows, h].astype(np.float64) @ R[b, h, slot].astype(np.float64).T
+                n = O.rms_norm(o_lin, lay.rms_eps)
+                ref[b, rows, h] = O.merge(o_soft[b, rows, h].astype(np.float64), n,
+                                          inp["gate_logits"][b, rows, h])
+    dev = to_dev(inp, w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    os_dev = torch.from_numpy(o_soft).to(tdt).cuda()
+    out = V.merge(dev["q"], os_dev, torch.from_numpy(R).cuda(), dev["gate_logits"], **geo_kw(w),
+                  text_tokens=w.text_tokens)
+    torch.cuda.synchronize()
+    err = rel_err(out.float().cpu().numpy(), ref)
+    print(f"{name}: merge rel err {err:.3e}")
+    assert err <= (1e-5 if w.dtype == "f32" else 1e-2)
+
+
+# ---------------------------------------------------------------------------
+# Robustness
+# ---------------------------------------------------------------------------
+def test_bitwise_deterministic_and_workspace_independent():
+    """No atomics: repeated calls agree bit for bit, also with a workspace
+    poisoned with NaN before the call."""
+    require_gpu()
+    w = workload("small_bf16")
+    _announce("determinism small_bf16")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    a = run_layer(w, dev).clone()
+    lay = V.make_layout(batch=w.batch, heads=w.heads, head_dim=w.head_dim, frames=w.frames,
+                        tokens_per_frame=w.tokens_per_frame, text_tokens=w.text_tokens, dtype="bf16")
+    ws = torch.full((V.workspace_size(lay) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    b_ = run_layer(w, dev, workspace=ws.view(torch.uint8)).clone()
+    c = run_layer(w, dev).clone()
+    assert torch.equal(a, b_) and torch.equal(a, c)
+
+
+def test_output_guard_bands_untouched():
+    """Writes stay inside O: a larger buffer around it keeps its sentinel."""
+    require_gpu()
+    w = custom("guard", batch=1, heads=3, head_dim=128, frames=6, tokens_per_frame=77,
+               text_tokens=5, dtype="bf16", chunk_frames=2)
+    _announce("guard bands")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    n = dev["q"].numel()
+    pad = 4096
+    big = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[pad:pad + n].view(dev["q"].shape)
+    run_layer(w, dev, out=out)
+    assert torch.all(big[:pad] == 7.0).item() and torch.all(big[pad + n:] == 7.0).item()
+    ref = O.hybrid_attn(inp, oracle_layout(w))
+    assert rel_err(out.float().cpu().numpy(), ref) <= TOL["bf16"]

@@ -1,0 +1,288 @@
+"""ctypes binding of ``libvdn.so`` (the C ABI in ``include/vdn.h``).
+
+Argument marshalling only: shapes are checked against the layout, tensor data
+pointers and the current HIP stream are passed to the library, and every step
+of the layer runs in the library's gfx950 kernels.  There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "VdnError", "Layout", "lib", "library_path", "version", "validate_layout",
+    "num_chunks", "workspace_size", "factor_scan_workspace_size", "hybrid_attn",
+    "softmax_fwd", "vda_gram", "vda_factor_scan", "merge", "make_layout",
+    "EXPORTED_SYMBOLS",
+]
+
+VDN_F32, VDN_BF16 = 0, 1
+_STATUS = {
+    0: "ok", 1: "null argument", 2: "bad shape", 3: "unsupported dtype or head size",
+    4: "device pointer not 16-byte aligned", 5: "workspace too small", 6: "HIP launch error",
+}
+
+EXPORTED_SYMBOLS = (
+    "vdn_version", "vdn_status_str", "vdn_last_hip_error", "vdn_validate_layout",
+    "vdn_num_chunks", "vdn_hybrid_attn_workspace_size", "vdn_hybrid_attn_fwd",
+    "vdn_softmax_fwd", "vdn_vda_gram", "vdn_vda_factor_scan_workspace_size",
+    "vdn_vda_factor_scan", "vdn_merge",
+)
+
+
+class VdnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
+        ("chunk_frames", ctypes.c_int32), ("window_chunks", ctypes.c_int32),
+        ("anchor_first", ctypes.c_int32), ("anchor_last", ctypes.c_int32),
+        ("text_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdn.so")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(path)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        lp = ctypes.POINTER(Layout)
+        L.vdn_version.restype = ctypes.c_int
+        L.vdn_status_str.restype = ctypes.c_char_p
+        L.vdn_status_str.argtypes = [ctypes.c_int]
+        L.vdn_last_hip_error.restype = ctypes.c_int
+        L.vdn_validate_layout.restype = ctypes.c_int
+        L.vdn_validate_layout.argtypes = [lp]
+        L.vdn_num_chunks.restype = i32
+        L.vdn_num_chunks.argtypes = [lp]
+        L.vdn_hybrid_attn_workspace_size.restype = sz
+        L.vdn_hybrid_attn_workspace_size.argtypes = [lp]
+        L.vdn_vda_factor_scan_workspace_size.restype = sz
+        L.vdn_vda_factor_scan_workspace_size.argtypes = [lp]
+        L.vdn_hybrid_attn_fwd.restype = ctypes.c_int
+        L.vdn_hybrid_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, lp, vp, vp, sz, vp]
+        L.vdn_softmax_fwd.restype = ctypes.c_int
+        L.vdn_softmax_fwd.argtypes = [vp, vp, vp, vp, vp, lp, vp, vp]
+        L.vdn_vda_gram.restype = ctypes.c_int
+        L.vdn_vda_gram.argtypes = [vp, vp, vp, vp, vp, lp, vp, vp, vp]
+        L.vdn_vda_factor_scan.restype = ctypes.c_int
+        L.vdn_vda_factor_scan.argtypes = [vp, vp, vp, lp, vp, vp, sz, vp]
+        L.vdn_merge.restype = ctypes.c_int
+        L.vdn_merge.argtypes = [vp, vp, vp, vp, lp, vp, vp]
+        _LIB = L
+    return _LIB
+
+
+def version() -> int:
+    return lib().vdn_version()
+
+
+def make_layout(*, batch, heads, head_dim, frames, tokens_per_frame, text_tokens,
+                dtype, chunk_frames=5, window_chunks=1, anchor_first=True,
+                anchor_last=True, softmax_scale=0.0, rms_eps=0.0) -> Layout:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.bfloat16: VDN_BF16, torch.float32: VDN_F32}.get(dtype, -1)
+    elif isinstance(dtype, str):
+        dtype = {"bf16": VDN_BF16, "f32": VDN_F32}[dtype]
+    return Layout(batch, heads, head_dim, head_dim, frames, tokens_per_frame, chunk_frames,
+                  window_chunks, int(bool(anchor_first)), int(bool(anchor_last)), text_tokens,
+                  dtype, float(softmax_scale), float(rms_eps))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise VdnError(status, what)
+
+
+def validate_layout(layout: Layout) -> int:
+    return lib().vdn_validate_layout(ctypes.byref(layout))
+
+
+def num_chunks(layout: Layout) -> int:
+    return lib().vdn_num_chunks(ctypes.byref(layout))
+
+
+def workspace_size(layout: Layout) -> int:
+    return lib().vdn_hybrid_attn_workspace_size(ctypes.byref(layout))
+
+
+def factor_scan_workspace_size(layout: Layout) -> int:
+    return lib().vdn_vda_factor_scan_workspace_size(ctypes.byref(layout))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _layout_from(q, text_k, frames, tokens_per_frame, **kw) -> Layout:
+    B, N, H, d = q.shape
+    if frames * tokens_per_frame != N:
+        raise ValueError(f"q has {N} tokens, layout needs frames*tokens_per_frame = "
+                         f"{frames * tokens_per_frame}")
+    L = 0 if text_k is None else text_k.shape[1]
+    return make_layout(batch=B, heads=H, head_dim=d, frames=frames,
+                       tokens_per_frame=tokens_per_frame, text_tokens=L, dtype=q.dtype, **kw)
+
+
+def _check_inputs(lay: Layout, q, k, v, text_k, text_v):
+    B, H, d = lay.batch, lay.heads, lay.head_dim_k
+    N = lay.frames * lay.tokens_per_frame
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, (B, N, H, d), dt, name)
+    if lay.text_tokens:
+        for name, t in (("text_k", text_k), ("text_v", text_v)):
+            _expect(t, (B, lay.text_tokens, H, d), dt, name)
+
+
+def hybrid_attn(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, frames,
+                tokens_per_frame, chunk_frames=5, window_chunks=1, anchor_first=True,
+                anchor_last=True, softmax_scale=0.0, rms_eps=0.0, out=None,
+                workspace=None) -> torch.Tensor:
+    """The whole layer (``vdn_hybrid_attn_fwd``).  Tensors are BNHD (see
+    ``include/vdn.h``); returns O with the dtype and shape of q."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, _ = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    need = workspace_size(lay)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().vdn_hybrid_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_fwd")
+    return out
+
+
+def softmax_fwd(q, k, v, text_k, text_v, *, frames, tokens_per_frame, chunk_frames=5,
+                window_chunks=1, anchor_first=True, anchor_last=True, softmax_scale=0.0,
+                out=None) -> torch.Tensor:
+    """Softmax branch alone (``vdn_softmax_fwd``)."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    L = lay.text_tokens
+    _check(lib().vdn_softmax_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
+                                 _ptr(text_v if L else None), ctypes.byref(lay), _ptr(out),
+                                 _stream()), "vdn_softmax_fwd")
+    return out
+
+
+def vda_gram(k, v, text_k, text_v, beta, *, frames, tokens_per_frame, chunk_frames=5,
+             window_chunks=1, anchor_first=True, anchor_last=True):
+    """Frame statistics (``vdn_vda_gram``): returns (A, B), float32
+    [B, H, T+1, d, d] with the text block in slot T."""
+    lay = _layout_from(k, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, k, k, v, text_k, text_v)
+    B, N, H, d = k.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    A = torch.empty((B, H, frames + 1, d, d), dtype=torch.float32, device=k.device)
+    Bm = torch.empty_like(A)
+    _check(lib().vdn_vda_gram(_ptr(k), _ptr(v), _ptr(text_k if L else None),
+                              _ptr(text_v if L else None), _ptr(beta), ctypes.byref(lay),
+                              _ptr(A), _ptr(Bm), _stream()), "vdn_vda_gram")
+    return A, Bm
+
+
+def vda_factor_scan(A, Bm, alpha, *, dtype, text_tokens, frames, tokens_per_frame,
+                    chunk_frames=5, window_chunks=1, anchor_first=True, anchor_last=True):
+    """Factor + bidirectional scan (``vdn_vda_factor_scan``).  A is
+    overwritten with (I+A)^-1 for the slots the scan uses.  Returns R, float32
+    [B, H, nc+1, d, d] (slot nc = text write)."""
+    B, H, T1, d, _ = A.shape
+    lay = make_layout(batch=B, heads=H, head_dim=d, frames=frames,
+                      tokens_per_frame=tokens_per_frame, text_tokens=text_tokens, dtype=dtype,
+                      chunk_frames=chunk_frames, window_chunks=window_chunks,
+                      anchor_first=anchor_first, anchor_last=anchor_last)
+    _check(validate_layout(lay), "layout")
+    _expect(A, (B, H, frames + 1, d, d), torch.float32, "A")
+    _expect(Bm, (B, H, frames + 1, d, d), torch.float32, "B")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    nc = num_chunks(lay)
+    R = torch.empty((B, H, nc + 1, d, d), dtype=torch.float32, device=A.device)
+    ws = torch.empty(factor_scan_workspace_size(lay), dtype=torch.uint8, device=A.device)
+    _check(lib().vdn_vda_factor_scan(_ptr(A), _ptr(Bm), _ptr(alpha), ctypes.byref(lay), _ptr(R),
+                                     _ptr(ws), ws.numel(), _stream()), "vdn_vda_factor_scan")
+    return R
+
+
+def merge(q, o_soft, R, gate_logits, *, frames, tokens_per_frame, chunk_frames=5,
+          window_chunks=1, anchor_first=True, anchor_last=True, rms_eps=0.0,
+          text_tokens=0, out=None) -> torch.Tensor:
+    """Read + RMSNorm + gates + merge (``vdn_merge``); ``out`` may be o_soft."""
+    B, N, H, d = q.shape
+    lay = make_layout(batch=B, heads=H, head_dim=d, frames=frames,
+                      tokens_per_frame=tokens_per_frame, text_tokens=text_tokens, dtype=q.dtype,
+                      chunk_frames=chunk_frames, window_chunks=window_chunks,
+                      anchor_first=anchor_first, anchor_last=anchor_last, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _expect(q, (B, frames * tokens_per_frame, H, d), q.dtype, "q")
+    _expect(o_soft, q.shape, q.dtype, "o_soft")
+    nc = num_chunks(lay)
+    _expect(R, (B, H, nc + 1, d, d), torch.float32, "R")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    _check(lib().vdn_merge(_ptr(q), _ptr(o_soft), _ptr(R), _ptr(gate_logits), ctypes.byref(lay),
+                           _ptr(out), _stream()), "vdn_merge")
+    return out

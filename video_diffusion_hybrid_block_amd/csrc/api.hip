@@ -1,0 +1,184 @@
+// C ABI of the hybrid layer: argument validation, workspace planning and the
+// sequence of stage launches.  Everything is enqueued on the caller's stream;
+// nothing here allocates device memory or synchronises the host.
+#include <math.h>
+#include <string.h>
+
+#include "vdn_internal.h"
+
+using namespace vdn;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+vdn_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return VDN_OK;
+  g_last_hip_error = (int)e;
+  return VDN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+vdn_status_t check_layout(const vdn_layout_t* l) {
+  if (!l) return VDN_ERR_NULL_ARG;
+  if (l->batch < 1 || l->heads < 1 || l->frames < 1 || l->tokens_per_frame < 1 ||
+      l->chunk_frames < 1 || l->window_chunks < 0 || l->text_tokens < 0)
+    return VDN_ERR_BAD_SHAPE;
+  if (l->head_dim_k != l->head_dim_v) return VDN_ERR_UNSUPPORTED;
+  const int d = l->head_dim_k;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
+  if (l->dtype != VDN_F32 && l->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
+  if ((l->anchor_first != 0 && l->anchor_first != 1) || (l->anchor_last != 0 && l->anchor_last != 1))
+    return VDN_ERR_BAD_SHAPE;
+  if (!(l->softmax_scale >= 0.f) || !isfinite(l->softmax_scale)) return VDN_ERR_BAD_SHAPE;
+  if (!(l->rms_eps >= 0.f) || !isfinite(l->rms_eps)) return VDN_ERR_BAD_SHAPE;
+  // Index arithmetic inside the kernels uses 32-bit token indices and 32-bit
+  // grid sizes; element offsets are 64-bit.
+  const long long N = (long long)l->frames * l->tokens_per_frame;
+  if (N + l->text_tokens >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  const long long bh = (long long)l->batch * l->heads;
+  if (bh * l->frames * ((l->tokens_per_frame + 63) / 64) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  if (bh * (l->frames + 1) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  return VDN_OK;
+}
+
+float eff_scale(const vdn_layout_t& l) {
+  return l.softmax_scale > 0.f ? l.softmax_scale : 1.0f / sqrtf((float)l.head_dim_k);
+}
+float eff_eps(const vdn_layout_t& l) { return l.rms_eps > 0.f ? l.rms_eps : 1e-6f; }
+
+bool text_ok(const vdn_layout_t& l, const void* tk, const void* tv) {
+  return l.text_tokens == 0 || (tk != nullptr && tv != nullptr);
+}
+
+bool text_aligned(const void* tk, const void* tv) {
+  return (!tk || aligned16(tk)) && (!tv || aligned16(tv));
+}
+
+}  // namespace
+
+extern "C" {
+
+int vdn_version(void) { return VDN_VERSION; }
+
+const char* vdn_status_str(vdn_status_t s) {
+  switch (s) {
+    case VDN_OK: return "ok";
+    case VDN_ERR_NULL_ARG: return "null argument";
+    case VDN_ERR_BAD_SHAPE: return "bad shape";
+    case VDN_ERR_UNSUPPORTED: return "unsupported dtype or head size";
+    case VDN_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case VDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case VDN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int vdn_last_hip_error(void) { return g_last_hip_error; }
+
+vdn_status_t vdn_validate_layout(const vdn_layout_t* layout) { return check_layout(layout); }
+
+int32_t vdn_num_chunks(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return make_geo(*layout).nc;
+}
+
+size_t vdn_hybrid_attn_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return make_plan(*layout).total;
+}
+
+size_t vdn_vda_factor_scan_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return scan_ws_bytes(*layout);
+}
+
+vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v, const void* text_k,
+                             const void* text_v, const vdn_layout_t* layout, void* o_soft,
+                             hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!q || !k || !v || !o_soft || !text_ok(*layout, text_k, text_v)) return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_soft) ||
+      !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  return hip_status(launch_softmax(q, k, v, text_k, text_v, *layout, eff_scale(*layout), o_soft,
+                                   stream));
+}
+
+vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
+                          const float* beta, const vdn_layout_t* layout, float* A_out,
+                          float* B_out, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!k || !v || !beta || !A_out || !B_out || !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(A_out) ||
+      !aligned16(B_out) || !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  return hip_status(launch_gram(k, v, text_k, text_v, beta, *layout, true, A_out, B_out, stream));
+}
+
+vdn_status_t vdn_vda_factor_scan(float* A_io, const float* B, const float* alpha,
+                                 const vdn_layout_t* layout, float* R_out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!A_io || !B || !alpha || !R_out || !workspace) return VDN_ERR_NULL_ARG;
+  if (!aligned16(A_io) || !aligned16(B) || !aligned16(alpha) || !aligned16(R_out) ||
+      !aligned16(workspace))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < scan_ws_bytes(*layout)) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  Geo g = make_geo(*layout);
+  size_t snaps = align256((size_t)layout->batch * layout->heads * (g.nc + 1) *
+                          layout->head_dim_k * layout->head_dim_k * sizeof(float));
+  float* Sf = (float*)workspace;
+  float* Sb = (float*)((char*)workspace + snaps);
+  hipError_t e = launch_factor(A_io, *layout, false, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_scan(A_io, B, alpha, *layout, Sf, Sb, R_out, stream));
+}
+
+vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R, const float* gate_logits,
+                       const vdn_layout_t* layout, void* o, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!q || !o_soft || !R || !gate_logits || !o) return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(o_soft) || !aligned16(R) || !aligned16(gate_logits) ||
+      !aligned16(o))
+    return VDN_ERR_MISALIGNED;
+  return hip_status(launch_merge(q, o_soft, R, gate_logits, *layout, eff_eps(*layout), o, stream));
+}
+
+vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_k,
+                                 const void* text_v, const float* beta, const float* alpha,
+                                 const float* gate_logits, const vdn_layout_t* layout, void* o,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !o || !workspace ||
+      !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(o) || !aligned16(workspace) ||
+      !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  const Plan p = make_plan(*layout);
+  if (workspace_bytes < p.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = (char*)workspace;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* Sf = (float*)(ws + p.sf_off);
+  float* Sb = (float*)(ws + p.sb_off);
+  float* R = (float*)(ws + p.r_off);
+  const vdn_layout_t& l = *layout;
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  if (e == hipSuccess) e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, stream);
+  if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

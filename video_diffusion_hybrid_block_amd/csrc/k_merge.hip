@@ -1,0 +1,184 @@
+// Read + RMSNorm + gates + merge: o = sigmoid(g0) * o_soft
+//   + sigmoid(g1) * RMSNorm(R q), with R the summed forward/backward state of
+// the query's chunk (the full text write for anchor frames).  The linear read
+// is RMS-normalised (no weight) before its gate; each branch has its own
+// content-dependent sigmoid gate and the two are added.
+// [PaperDaily "伯克利与Impossible视频生成:14.3秒视频6.70秒去噪" §三 (read both
+//  states and add; gates per branch; RMS normalisation of the linear branch);
+//  deepmagic blog "生成比播放還快", section 用兩條分支取代一條 (sigmoid gates)]
+//
+// gfx950 design (bf16, d in {32, 64, 128}): one workgroup (4 waves) per
+// (batch, head, frame).  R (fp32) is split once into bf16 hi + lo in LDS; the
+// read is computed transposed, o^T = R q^T, on v_mfma_f32_32x32x16_bf16 (two
+// passes, hi and lo), so each lane owns one token column: the RMS reduction is
+// 64 local squares plus one exchange with lane l^32.  q rows are the B operand
+// straight from global memory (16-byte loads).  Memory-bound: q, o_soft and
+// the gate logits are read once and o is written once.
+#include "vdn_device.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+namespace {
+
+__device__ __forceinline__ int r_slot(const Geo& g, int t) {
+  return is_anchor(g, t) ? g.nc : t / g.C;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+merge_mfma_kernel(const bf16* __restrict__ q, const bf16* o_soft, const float* __restrict__ R,
+                  const float* __restrict__ gates, bf16* o, Geo g, int H, float eps) {
+  constexpr int NB = D / 32;
+  __shared__ __attribute__((aligned(16))) char rh[D * D * 2];
+  __shared__ __attribute__((aligned(16))) char rl[D * D * 2];
+  char VDN_LDS* Rh = (char VDN_LDS*)rh;
+  char VDN_LDS* Rl = (char VDN_LDS*)rl;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const int N = g.T * g.P;
+  const int task = blockIdx.x;
+  const int t = task % g.T;
+  const int bh = task / g.T;
+  const int b = bh / H, h = bh % H;
+  const float* Rs = R + ((size_t)bh * (g.nc + 1) + r_slot(g, t)) * D * D;
+  for (int i = tid; i < D * D / 4; i += 256) {
+    float4 x = ((const float4*)Rs)[i];
+    int r = (i * 4) / D, c = (i * 4) % D;
+    float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16 hi, lo;
+      split_bf16(xv[e], hi, lo);
+      int off = swz_off<D>(r, c + e);
+      *(bf16 VDN_LDS*)(Rh + off) = hi;
+      *(bf16 VDN_LDS*)(Rl + off) = lo;
+    }
+  }
+  __syncthreads();
+  const int ntiles = (g.P + 31) / 32;
+  for (int tile = wv; tile < ntiles; tile += 4) {
+    const int tl = tile * 32 + (lane & 31);
+    const bool valid = tl < g.P;
+    const int tok = t * g.P + (valid ? tl : 0);
+    const size_t rowoff = ((size_t)(b * (size_t)N + tok) * H + h) * D;
+    bf16x8 qv[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *(const bf16x8*)(q + rowoff + ks * 16 + half * 8);
+    f32x16 acc[NB];
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      acc[bi] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 ah = lds_row8<D>(Rh, bi * 32 + (lane & 31), ks * 2 + half);
+        bf16x8 al = lds_row8<D>(Rl, bi * 32 + (lane & 31), ks * 2 + half);
+        acc[bi] = mfma32(ah, qv[ks], acc[bi]);
+        acc[bi] = mfma32(al, qv[ks], acc[bi]);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss = fmaf(acc[bi][j], acc[bi][j], ss);
+    ss = xhalf_sum(ss);
+    const float inv = rsqrtf(ss * (1.0f / D) + eps);
+    const float2 gl = *(const float2*)(gates + ((size_t)(b * (size_t)N + tok) * H + h) * 2);
+    const float g0 = sigmoidf(gl.x), g1 = sigmoidf(gl.y) * inv;
+    if (valid) {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = bi * 32 + jj * 8 + half * 4;
+          bf16x4 os = *(const bf16x4*)(o_soft + rowoff + d);
+          bf16x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[e] = (bf16)fmaf(g0, (float)os[e], g1 * acc[bi][jj * 4 + e]);
+          *(bf16x4*)(o + rowoff + d) = out;
+        }
+    }
+  }
+}
+
+// Plain fp32 path: one workgroup per (batch, head, frame), one thread per token.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+merge_valu_kernel(const T* __restrict__ q, const T* o_soft, const float* __restrict__ R,
+                  const float* __restrict__ gates, T* o, Geo g, int H, float eps) {
+  __shared__ float Rsh[D * D];
+  const int tid = threadIdx.x;
+  const int N = g.T * g.P;
+  const int task = blockIdx.x;
+  const int t = task % g.T;
+  const int bh = task / g.T;
+  const int b = bh / H, h = bh % H;
+  const float* Rs = R + ((size_t)bh * (g.nc + 1) + r_slot(g, t)) * D * D;
+  for (int i = tid; i < D * D; i += 256) Rsh[i] = Rs[i];
+  __syncthreads();
+  for (int tl = tid; tl < g.P; tl += 256) {
+    const int tok = t * g.P + tl;
+    const size_t rowoff = ((size_t)(b * (size_t)N + tok) * H + h) * D;
+    float qv[D], ov[D];
+    for (int d = 0; d < D; ++d) qv[d] = Elem<T>::to_f(q[rowoff + d]);
+    float ss = 0.f;
+    for (int r = 0; r < D; ++r) {
+      float acc = 0.f;
+      for (int c = 0; c < D; ++c) acc = fmaf(Rsh[r * D + c], qv[c], acc);
+      ov[r] = acc;
+      ss = fmaf(acc, acc, ss);
+    }
+    const float inv = rsqrtf(ss / D + eps);
+    const size_t goff = ((size_t)(b * (size_t)N + tok) * H + h) * 2;
+    const float g0 = sigmoidf(gates[goff]), g1 = sigmoidf(gates[goff + 1]) * inv;
+    for (int d = 0; d < D; ++d)
+      o[rowoff + d] = Elem<T>::from_f(fmaf(g0, Elem<T>::to_f(o_soft[rowoff + d]), g1 * ov[d]));
+  }
+}
+
+template <int D>
+hipError_t launch_mfma(const void* q, const void* o_soft, const float* R, const float* gates,
+                       const vdn_layout_t& l, float eps, void* o, hipStream_t s) {
+  Geo g = make_geo(l);
+  long grid = (long)l.batch * l.heads * g.T;
+  merge_mfma_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+      (const bf16*)q, (const bf16*)o_soft, R, gates, (bf16*)o, g, l.heads, eps);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_valu(const void* q, const void* o_soft, const float* R, const float* gates,
+                       const vdn_layout_t& l, float eps, void* o, hipStream_t s) {
+  Geo g = make_geo(l);
+  long grid = (long)l.batch * l.heads * g.T;
+  merge_valu_kernel<T, D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+      (const T*)q, (const T*)o_soft, R, gates, (T*)o, g, l.heads, eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
+                        const vdn_layout_t& l, float eps, void* o, hipStream_t s) {
+  const int d = l.head_dim_k;
+  if (l.dtype == VDN_BF16) {
+    switch (d) {
+      case 128: return launch_mfma<128>(q, o_soft, R, gates, l, eps, o, s);
+      case 64: return launch_mfma<64>(q, o_soft, R, gates, l, eps, o, s);
+      case 32: return launch_mfma<32>(q, o_soft, R, gates, l, eps, o, s);
+      case 16: return launch_valu<bf16, 16>(q, o_soft, R, gates, l, eps, o, s);
+    }
+  } else {
+    switch (d) {
+      case 128: return launch_valu<float, 128>(q, o_soft, R, gates, l, eps, o, s);
+      case 64: return launch_valu<float, 64>(q, o_soft, R, gates, l, eps, o, s);
+      case 32: return launch_valu<float, 32>(q, o_soft, R, gates, l, eps, o, s);
+      case 16: return launch_valu<float, 16>(q, o_soft, R, gates, l, eps, o, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vdn

@@ -1,0 +1,235 @@
+// Bidirectional VDA state scan.  Both states start from half of the text write
+// S_x = B_x (I + A_x)^-1; the forward state folds the non-anchor frames in
+// ascending order, the backward state in descending order, each step being the
+// frame-wise joint update S <- (alpha_f S + B_f)(I + A_f)^-1 = (alpha_f S + B_f) G_f.
+// The state a chunk reads is the forward state before its window and the
+// backward state after it; snapshots are taken at those points and summed.
+// Anchor frames are never written (and do not decay the state).
+// [PaperDaily "伯克利与Impossible视频生成:14.3秒视频6.70秒去噪" §三 (two states,
+//  non-overlapping far regions, text written half into each), §四 pseudocode
+//  (decay, frame correlation, joint solve, both directions);
+//  deepmagic blog "生成比播放還快", section 用兩條分支取代一條 (×½ text write)]
+//
+// gfx950 design (bf16 layouts, d in {32, 64, 128}): the rows of S are
+// independent under right-multiplication, so each (batch, head, direction)
+// chain is split into d/32 workgroups of 32 rows.  A workgroup has d/32 waves;
+// wave w computes the 32 x 32 block of columns 32w..32w+31 of the new state
+// with v_mfma_f32_32x32x16_bf16 on a three-pass bf16 split of both operands
+// (X_hi G_hi + X_hi G_lo + X_lo G_hi, relative error ~2^-16).  G is symmetric,
+// so its B-operand columns are read as contiguous rows from global memory.
+// The state lives in LDS between steps (the MFMA result is column-owned, the
+// next A operand row-owned).
+#include "vdn_device.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+namespace {
+
+template <int D>
+__global__ void __launch_bounds__(2 * D)
+scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
+                 const float* __restrict__ alpha, float* __restrict__ Sf, float* __restrict__ Sb,
+                 Geo g, int H) {
+  constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
+  constexpr int NT = 64 * NRB;
+  constexpr int LDF = D + 4;            // fp32 state row stride (floats)
+  __shared__ float S[32 * LDF];
+  __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
+  char VDN_LDS* Xh = (char VDN_LDS*)xh;
+  char VDN_LDS* Xl = (char VDN_LDS*)xl;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const int rb = blockIdx.x % NRB;
+  const int chain = blockIdx.x / NRB;
+  const int dir = chain & 1;
+  const int bh = chain >> 1;
+  const int b = bh / H, h = bh % H;
+  const int row0 = rb * 32;
+  const size_t mat = (size_t)D * D;
+  const float* Gbh = G + (size_t)bh * (g.T + 1) * mat;
+  const float* Bbh = Bm + (size_t)bh * (g.T + 1) * mat;
+  float* snap = (dir == 0 ? Sf : Sb) + (size_t)bh * (g.nc + 1) * mat;
+
+  for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
+  __syncthreads();
+
+  // One update S <- (a S + B_slot[rows]) G_slot, times `post`.
+  auto step = [&](int slot, float a, float post) {
+    const float* Bs = Bbh + (size_t)slot * mat + (size_t)row0 * D;
+    for (int i = tid; i < 32 * D; i += NT) {
+      int r = i / D, c = i % D;
+      float x = fmaf(a, S[r * LDF + c], Bs[(size_t)r * D + c]);
+      bf16 hi, lo;
+      split_bf16(x, hi, lo);
+      int off = swz_off<D>(r, c);
+      *(bf16 VDN_LDS*)(Xh + off) = hi;
+      *(bf16 VDN_LDS*)(Xl + off) = lo;
+    }
+    __syncthreads();
+    const float* Gs = Gbh + (size_t)slot * mat + (size_t)(wv * 32 + (lane & 31)) * D;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const float4* gp = (const float4*)(Gs + ks * 16 + half * 8);
+      float4 g0 = gp[0], g1 = gp[1];
+      float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      bf16x8 gh, gl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 a_, c_;
+        split_bf16(gv[e], a_, c_);
+        gh[e] = a_;
+        gl[e] = c_;
+      }
+      bf16x8 ah = lds_row8<D>(Xh, lane & 31, ks * 2 + half);
+      bf16x8 al = lds_row8<D>(Xl, lane & 31, ks * 2 + half);
+      acc = mfma32(ah, gh, acc);
+      acc = mfma32(ah, gl, acc);
+      acc = mfma32(al, gh, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int r = (j >> 2) * 8 + half * 4 + (j & 3);
+      S[r * LDF + wv * 32 + (lane & 31)] = acc[j] * post;
+    }
+    __syncthreads();
+  };
+  auto snapshot = [&](int c) {
+    float* dst = snap + (size_t)c * mat + (size_t)row0 * D;
+    for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
+  };
+
+  if (g.L > 0) step(g.T, 0.0f, 0.5f);   // S0 = S_x / 2
+  snapshot(g.nc);
+  const float* al = alpha + (size_t)b * g.T * H + h;
+  if (dir == 0) {
+    const int fend = fwd_scan_end(g);
+    int c = 0;
+    for (int f = 0; f < fend; ++f) {
+      while (c < g.nc && win_lo(g, c) == f) snapshot(c++);
+      if (is_anchor(g, f)) continue;
+      step(f, al[(size_t)f * H], 1.0f);
+    }
+    while (c < g.nc) snapshot(c++);
+  } else {
+    const int fbeg = bwd_scan_begin(g);
+    int c = g.nc - 1;
+    for (int f = g.T - 1; f > fbeg; --f) {
+      while (c >= 0 && win_hi(g, c) == f) snapshot(c--);
+      if (is_anchor(g, f)) continue;
+      step(f, al[(size_t)f * H], 1.0f);
+    }
+    while (c >= 0) snapshot(c--);
+  }
+}
+
+// Plain fp32 path: one workgroup per (batch, head, direction), whole state.
+template <int D>
+__global__ void __launch_bounds__(256)
+scan_valu_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
+                 const float* __restrict__ alpha, float* __restrict__ Sf, float* __restrict__ Sb,
+                 Geo g, int H) {
+  __shared__ float S[D * D];
+  __shared__ float X[D * D];
+  const int tid = threadIdx.x;
+  const int chain = blockIdx.x;
+  const int dir = chain & 1;
+  const int bh = chain >> 1;
+  const int b = bh / H, h = bh % H;
+  const size_t mat = (size_t)D * D;
+  const float* Gbh = G + (size_t)bh * (g.T + 1) * mat;
+  const float* Bbh = Bm + (size_t)bh * (g.T + 1) * mat;
+  float* snap = (dir == 0 ? Sf : Sb) + (size_t)bh * (g.nc + 1) * mat;
+  for (int i = tid; i < D * D; i += 256) S[i] = 0.f;
+  __syncthreads();
+  auto step = [&](int slot, float a, float post) {
+    const float* Bs = Bbh + (size_t)slot * mat;
+    const float* Gs = Gbh + (size_t)slot * mat;
+    for (int i = tid; i < D * D; i += 256) X[i] = fmaf(a, S[i], Bs[i]);
+    __syncthreads();
+    for (int i = tid; i < D * D; i += 256) {
+      int r = i / D, c = i % D;
+      float acc = 0.f;
+      for (int kk = 0; kk < D; ++kk) acc = fmaf(X[r * D + kk], Gs[(size_t)kk * D + c], acc);
+      S[i] = acc * post;
+    }
+    __syncthreads();
+  };
+  auto snapshot = [&](int c) {
+    float* dst = snap + (size_t)c * mat;
+    for (int i = tid; i < D * D; i += 256) dst[i] = S[i];
+  };
+  if (g.L > 0) step(g.T, 0.0f, 0.5f);
+  snapshot(g.nc);
+  const float* al = alpha + (size_t)b * g.T * H + h;
+  if (dir == 0) {
+    const int fend = fwd_scan_end(g);
+    int c = 0;
+    for (int f = 0; f < fend; ++f) {
+      while (c < g.nc && win_lo(g, c) == f) snapshot(c++);
+      if (is_anchor(g, f)) continue;
+      step(f, al[(size_t)f * H], 1.0f);
+    }
+    while (c < g.nc) snapshot(c++);
+  } else {
+    const int fbeg = bwd_scan_begin(g);
+    int c = g.nc - 1;
+    for (int f = g.T - 1; f > fbeg; --f) {
+      while (c >= 0 && win_hi(g, c) == f) snapshot(c--);
+      if (is_anchor(g, f)) continue;
+      step(f, al[(size_t)f * H], 1.0f);
+    }
+    while (c >= 0) snapshot(c--);
+  }
+}
+
+// R = S_fwd + S_bwd for every chunk slot (slot nc: S_x/2 + S_x/2 = S_x).
+__global__ void __launch_bounds__(256)
+combine_kernel(const float4* __restrict__ Sf, const float4* __restrict__ Sb, float4* __restrict__ R,
+               size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    float4 a = Sf[i], c = Sb[i];
+    R[i] = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
+                    float* Sf, float* Sb, float* R, hipStream_t s) {
+  Geo g = make_geo(l);
+  long chains = (long)l.batch * l.heads * 2;
+  if (l.dtype == VDN_BF16 && D >= 32) {
+    if constexpr (D >= 32) {
+      scan_mfma_kernel<D><<<dim3((unsigned)(chains * (D / 32))), dim3(2 * D), 0, s>>>(
+          G, B, alpha, Sf, Sb, g, l.heads);
+    }
+  } else {
+    scan_valu_kernel<D><<<dim3((unsigned)chains), dim3(256), 0, s>>>(G, B, alpha, Sf, Sb, g,
+                                                                      l.heads);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  size_t n4 = (size_t)l.batch * l.heads * (g.nc + 1) * D * D / 4;
+  unsigned blocks = (unsigned)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  combine_kernel<<<dim3(blocks), dim3(256), 0, s>>>((const float4*)Sf, (const float4*)Sb,
+                                                     (float4*)R, n4);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
+                       float* Sf, float* Sb, float* R, hipStream_t s) {
+  switch (l.head_dim_k) {
+    case 128: return launch_d<128>(G, B, alpha, l, Sf, Sb, R, s);
+    case 64: return launch_d<64>(G, B, alpha, l, Sf, Sb, R, s);
+    case 32: return launch_d<32>(G, B, alpha, l, Sf, Sb, R, s);
+    case 16: return launch_d<16>(G, B, alpha, l, Sf, Sb, R, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vdn

@@ -1,0 +1,348 @@
+// Softmax branch of the hybrid layer: for every video query, one softmax over
+// the keys of its visible frames (own chunk +- window_chunks, plus the first
+// and last frame; an anchor frame sees every frame) together with all text
+// keys, times the matching values.
+// [PaperDaily "伯克利与Impossible视频生成:14.3秒视频6.70秒去噪" §二;
+//  arXiv listing "Video DeltaNet: ...", abstract: softmax is kept for every
+//  interaction that involves text]
+//
+// gfx950 design (bf16, d in {32, 64, 128}):
+//  * One workgroup (4 waves) per 128 query rows of one (batch, head, frame);
+//    query tiles never straddle frames, so every row of a tile shares one key
+//    set.  The key set is a list of <= 3 contiguous video token ranges plus
+//    the text block, walked as one virtual sequence in tiles of 64 keys; only
+//    the last tile is partial.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+//    so each lane owns one query column: row max / sum need one exchange with
+//    lane l^32 per tile instead of 32-lane reductions.  K rows are permuted
+//    inside each 32-key block so that the score registers already form the
+//    B operand of O^T += V^T P^T without any data movement.
+//  * K and V tiles go global -> LDS with 16-byte direct-to-LDS loads into an
+//    XOR-swizzled layout, double buffered; V is read transposed from its
+//    natural [key][d] layout with ds_read_b64_tr_b16.
+//  * exp2 with the scale * log2(e) folded into one FMA; fp32 statistics.
+//  * Work order: anchor-frame tiles (the heaviest) first; with B*H a multiple
+//    of 8 each XCD gets a fixed set of heads so K/V tiles are shared in its L2.
+#include "vdn_device.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int frame_in_order(const Geo& g, int vfr) {
+  int first = g.af ? 0 : -1;
+  int last = (g.al && !(g.af && g.T == 1)) ? g.T - 1 : -1;
+  int na = (first >= 0) + (last >= 0);
+  if (vfr < na) return (vfr == 0 && first >= 0) ? first : last;
+  return vfr - na + (g.af ? 1 : 0);
+}
+
+struct WorkItem {
+  int b, h, t, tile;
+};
+
+__device__ __forceinline__ WorkItem decode_work(const Geo& g, int B, int H, int tpf) {
+  int i = blockIdx.x;
+  int G = B * H;
+  int gi, rest;
+  if ((G & 7) == 0) {
+    int xcd = i & 7, j = i >> 3, gper = G >> 3;
+    gi = xcd * gper + j % gper;
+    rest = j / gper;
+  } else {
+    gi = i % G;
+    rest = i / G;
+  }
+  WorkItem w;
+  w.b = gi / H;
+  w.h = gi % H;
+  w.t = frame_in_order(g, rest / tpf);
+  w.tile = rest % tpf;
+  return w;
+}
+
+// Row permutation inside a 32-key block: MFMA row m holds key pi(m), so the
+// score registers of lane half h hold keys 8h..8h+7 and 16+8h..16+8h+7.
+__device__ __forceinline__ int perm32(int m) {
+  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+struct KeyMap {
+  int s0, n0, s1, n1, s2, n2, nvid, nkeys;
+};
+
+__device__ __forceinline__ KeyMap key_map(const Geo& g, int t) {
+  int ss[3] = {0, 0, 0}, sl[3] = {0, 0, 0};
+  key_segments(g, t, ss, sl);
+  KeyMap m;
+  m.s0 = ss[0]; m.n0 = sl[0];
+  m.s1 = ss[1]; m.n1 = sl[1];
+  m.s2 = ss[2]; m.n2 = sl[2];
+  m.nvid = m.n0 + m.n1 + m.n2;
+  m.nkeys = m.nvid + g.L;
+  return m;
+}
+
+// Element offset of virtual key kv of (b, h) in the video or text tensor;
+// keys past the end are clamped to the first visible key (their scores are
+// masked).  Returns true when the key is a text key.
+__device__ __forceinline__ bool key_src(const KeyMap& m, int kv, int b, int h, int H, int N,
+                                        int L, int D, size_t& off) {
+  if (kv < m.nvid) {
+    int tok = kv < m.n0 ? m.s0 + kv : (kv < m.n0 + m.n1 ? m.s1 + kv - m.n0 : m.s2 + kv - m.n0 - m.n1);
+    off = ((size_t)(b * (size_t)N + tok) * H + h) * D;
+    return false;
+  }
+  if (kv < m.nkeys) {
+    off = ((size_t)(b * (size_t)L + (kv - m.nvid)) * H + h) * D;
+    return true;
+  }
+  off = ((size_t)(b * (size_t)N + m.s0) * H + h) * D;
+  return false;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                    const bf16* __restrict__ v, const bf16* __restrict__ tk,
+                    const bf16* __restrict__ tv, bf16* __restrict__ o, Geo g, int B, int H,
+                    int tpf, float c) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int KCH = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = BN * D * 2;            // bytes of one K or V tile
+  constexpr int NI = BN * KCH / 256;          // DMA instructions per thread per tensor
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  char VDN_LDS* lds = (char VDN_LDS*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int N = g.T * g.P;
+  const WorkItem w = decode_work(g, B, H, tpf);
+  const KeyMap km = key_map(g, w.t);
+
+  // Query rows of this wave.
+  const int qlocal = w.tile * BM + wv * 32 + (lane & 31);
+  const bool qvalid = qlocal < g.P;
+  const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
+  const size_t qoff = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * D;
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+
+  auto issue_load = [&](int kbase, int buf) {
+    char VDN_LDS* kt = lds + buf * 2 * TILE;
+    char VDN_LDS* vt = kt + TILE;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      int blk = ii * 4 + wv;                   // 64-chunk block of the tile
+      int p = blk * 64 + lane;                 // physical chunk
+      int row = p / KCH, pch = p % KCH;
+      int ch = pch ^ swz<D>(row);
+      size_t off;
+      bool txt = key_src(km, kbase + row, w.b, w.h, H, N, g.L, D, off);
+      const bf16* ksrc = (txt ? tk : k) + off + ch * 8;
+      const bf16* vsrc = (txt ? tv : v) + off + ch * 8;
+      g2lds16(ksrc, kt + blk * 1024);
+      g2lds16(vsrc, vt + blk * 1024);
+    }
+  };
+
+  float m_run = -1e30f, l_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+
+  const int ntiles = (km.nkeys + BN - 1) / BN;
+  const int prow0 = perm32(lane & 31);
+  issue_load(0, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < ntiles) issue_load((it + 1) * BN, (it + 1) & 1);
+    const char VDN_LDS* kt = lds + (it & 1) * 2 * TILE;
+    const char VDN_LDS* vt = kt + TILE;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 a = lds_row8<D>(kt, kb * 32 + prow0, ks * 2 + half);
+        s[kb] = mfma32(a, qreg[ks], s[kb]);
+      }
+    }
+    if ((it + 1) * BN > km.nkeys) {
+      const int base = it * BN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          int key = base + kb * 32 + ((j >> 3) << 4) + half * 8 + (j & 7);
+          if (key >= km.nkeys) s[kb][j] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[0][j]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = fast_exp2((m_run - m_new) * c);
+    const float mc = m_new * c;
+    float rs = 0.f;
+    bf16x8 pk[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float p = fast_exp2(fmaf(s[kb][j], c, -mc));
+        rs += p;
+        pk[kb * 2 + (j >> 3)][j & 7] = (bf16)p;
+      }
+    l_run = l_run * corr + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        bf16x8 a = lds_col8<D>(vt, sp * 16, db * 32, lane);
+        oacc[db] = mfma32(a, pk[sp], oacc[db]);
+      }
+  }
+
+  const float inv = 1.0f / xhalf_sum(l_run);
+  if (qvalid) {
+    bf16* orow = o + qoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        int d = db * 32 + jj * 8 + half * 4;
+        bf16x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[db][jj * 4 + e] * inv);
+        *(bf16x4*)(orow + d) = val;
+      }
+  }
+}
+
+// Plain VALU path for float tensors and head sizes without an MFMA path: one
+// wave per 64 query rows of a frame, keys staged through LDS 32 at a time.
+template <typename T, int D>
+__global__ void __launch_bounds__(64)
+softmax_valu_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                    const T* __restrict__ tk, const T* __restrict__ tv, T* __restrict__ o, Geo g,
+                    int B, int H, int tpf, float scale) {
+  constexpr int BN = 32;
+  __shared__ float Ks[BN][D];
+  __shared__ float Vs[BN][D];
+  const int N = g.T * g.P;
+  int i = blockIdx.x;
+  int gi = i % (B * H), rest = i / (B * H);
+  int b = gi / H, h = gi % H;
+  int t = rest / tpf, tile = rest % tpf;
+  KeyMap km = key_map(g, t);
+  int ql = tile * 64 + threadIdx.x;
+  bool valid = ql < g.P;
+  int qrow = t * g.P + (valid ? ql : 0);
+  size_t qoff = ((size_t)(b * (size_t)N + qrow) * H + h) * D;
+  float qv[D], ov[D];
+  for (int d = 0; d < D; ++d) {
+    qv[d] = Elem<T>::to_f(q[qoff + d]) * scale;
+    ov[d] = 0.f;
+  }
+  float m_run = -1e30f, l_run = 0.f;
+  for (int kb = 0; kb < km.nkeys; kb += BN) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < BN * D; idx += 64) {
+      int r = idx / D, d = idx % D;
+      size_t off;
+      bool txt = key_src(km, kb + r, b, h, H, N, g.L, D, off);
+      Ks[r][d] = Elem<T>::to_f((txt ? tk : k)[off + d]);
+      Vs[r][d] = Elem<T>::to_f((txt ? tv : v)[off + d]);
+    }
+    __syncthreads();
+    int nk = km.nkeys - kb < BN ? km.nkeys - kb : BN;
+    float s[BN];
+    float mx = m_run;
+    for (int j = 0; j < BN; ++j) {
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qv[d], Ks[j][d], acc);
+      s[j] = j < nk ? acc : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    float corr = __expf(m_run - mx);
+    l_run *= corr;
+    for (int d = 0; d < D; ++d) ov[d] *= corr;
+    for (int j = 0; j < nk; ++j) {
+      float p = __expf(s[j] - mx);
+      l_run += p;
+      for (int d = 0; d < D; ++d) ov[d] = fmaf(p, Vs[j][d], ov[d]);
+    }
+    m_run = mx;
+  }
+  if (valid) {
+    float inv = 1.0f / l_run;
+    for (int d = 0; d < D; ++d) o[qoff + d] = Elem<T>::from_f(ov[d] * inv);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_valu(const void* q, const void* k, const void* v, const void* tk,
+                       const void* tv, const vdn_layout_t& l, float scale, void* o,
+                       hipStream_t s) {
+  Geo g = make_geo(l);
+  int tpf = (g.P + 63) / 64;
+  long grid = (long)l.batch * l.heads * g.T * tpf;
+  softmax_valu_kernel<T, D><<<dim3((unsigned)grid), dim3(64), 0, s>>>(
+      (const T*)q, (const T*)k, (const T*)v, (const T*)tk, (const T*)tv, (T*)o, g, l.batch,
+      l.heads, tpf, scale);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
+                       const void* tv, const vdn_layout_t& l, float scale, void* o,
+                       hipStream_t s) {
+  Geo g = make_geo(l);
+  int tpf = (g.P + 127) / 128;
+  long grid = (long)l.batch * l.heads * g.T * tpf;
+  softmax_mfma_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
+      (bf16*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_softmax(const void* q, const void* k, const void* v, const void* tk,
+                          const void* tv, const vdn_layout_t& l, float scale, void* o,
+                          hipStream_t s) {
+  const int d = l.head_dim_k;
+  if (l.dtype == VDN_BF16) {
+    switch (d) {
+      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, s);
+      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, s);
+      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, s);
+      case 16: return launch_valu<bf16, 16>(q, k, v, tk, tv, l, scale, o, s);
+    }
+  } else {
+    switch (d) {
+      case 128: return launch_valu<float, 128>(q, k, v, tk, tv, l, scale, o, s);
+      case 64: return launch_valu<float, 64>(q, k, v, tk, tv, l, scale, o, s);
+      case 32: return launch_valu<float, 32>(q, k, v, tk, tv, l, scale, o, s);
+      case 16: return launch_valu<float, 16>(q, k, v, tk, tv, l, scale, o, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vdn

@@ -1,0 +1,121 @@
+// Device helpers for the gfx950 (CDNA4) kernels: vector types, MFMA wrappers,
+// LDS swizzles and transposed LDS reads.
+//
+// MFMA operand layouts used throughout (checked on gfx950 hardware):
+//   v_mfma_f32_32x32x16_bf16: lane l supplies A[m = l%32][k = 8*(l/32) + e] and
+//     B[k = 8*(l/32) + e][n = l%32], e = 0..7; result register j of lane l is
+//     C[8*(j/4) + 4*(l/32) + j%4][l%32].
+//   ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives element
+//     j%4 of the 8-byte words addressed by lanes j/4 + 4*i, i = 0..3.  With lane
+//     s addressing row s/4, columns 4*(s%4)..+3 of a 16-wide block, lane j gets
+//     column j of the four rows: a 4x16 -> 16x4 transpose.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define VDN_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Element type traits: loads of 8 / 4 consecutive values as float.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+template <> struct Elem<bf16> {
+  static __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+  static __device__ __forceinline__ bf16 from_f(float x) { return (bf16)x; }
+};
+
+// Split a float into bf16 hi + bf16 lo with hi + lo == x up to 2^-16 relative.
+__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+// Exchange with lane l^32: returns max / sum of the value and its partner's.
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row of D bf16 values.
+// It makes (a) 16 consecutive rows read at one logical chunk by ds_read_b128
+// and (b) 4 consecutive rows x 64 bytes read by ds_read_b64_tr_b16 fall on
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else if constexpr (D == 64) {
+    int u = (r >> 1) & 7;
+    return u ^ ((u & 1) << 2);
+  } else {
+    static_assert(D == 32, "head size");
+    return (r >> 2) & 3;
+  }
+}
+
+// Byte offset of (row r, element col) in a swizzled [rows][D] bf16 LDS tile.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  int ch = (col >> 3) ^ swz<D>(r);
+  return r * (D * 2) + ch * 16 + (col & 7) * 2;
+}
+
+// 16-byte read of logical chunk `ch` of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const char VDN_LDS* base, int r, int ch) {
+  const char VDN_LDS* p = base + r * (D * 2) + ((ch ^ swz<D>(r)) << 4);
+  return *(const bf16x8 VDN_LDS*)p;
+}
+
+// MFMA operand with 8 consecutive *rows* of one column from a swizzled
+// [rows][D] bf16 tile, using two transposed reads: lane l gets
+// tile[row0 + 8*(l/32) + e][col0 + l%32], e = 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8(const char VDN_LDS* base, int row0, int col0, int lane) {
+  int g = lane >> 4, s = lane & 15;
+  int col = col0 + ((g & 1) << 4) + ((s & 3) << 2);
+  int r = row0 + ((g >> 1) << 3) + (s >> 2);
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (i16x4 VDN_LDS*)(base + swz_off<D>(r, col)));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (i16x4 VDN_LDS*)(base + swz_off<D>(r + 4, col)));
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Asynchronous 16-byte global -> LDS copy: this lane's 16 bytes land at
+// lds_wave_base + 16 * lane.
+__device__ __forceinline__ void g2lds16(const void* gptr, char VDN_LDS* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (void VDN_LDS*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace vdn

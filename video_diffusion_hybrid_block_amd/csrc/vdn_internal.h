@@ -1,0 +1,175 @@
+// Internal definitions shared by the host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vdn.h"
+
+namespace vdn {
+
+// ---------------------------------------------------------------------------
+// Frame geometry [PaperDaily "伯克利与Impossible视频生成" §二, §三].
+// Chunk c holds frames [c*C, min((c+1)*C, T)).  The window of chunk c is the
+// frame interval [win_lo(c), win_hi(c)] covering chunks c-w .. c+w.  Anchors
+// are frame 0 and frame T-1 (each optional).  A non-anchor query frame of
+// chunk c sees win ∪ anchors in softmax; its forward state folds the
+// non-anchor frames below win_lo(c) in ascending order, its backward state
+// the non-anchor frames above win_hi(c) in descending order.  Anchor query
+// frames see every frame and read the text write only.
+// ---------------------------------------------------------------------------
+struct Geo {
+  int T, P, C, w, af, al, L, nc;
+};
+
+__host__ __device__ inline Geo make_geo(const vdn_layout_t& l) {
+  Geo g;
+  g.T = l.frames; g.P = l.tokens_per_frame; g.C = l.chunk_frames; g.w = l.window_chunks;
+  g.af = l.anchor_first ? 1 : 0; g.al = l.anchor_last ? 1 : 0; g.L = l.text_tokens;
+  g.nc = (g.T + g.C - 1) / g.C;
+  return g;
+}
+
+__host__ __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+__host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+
+__host__ __device__ inline int win_lo(const Geo& g, int c) {
+  long v = (long)(c - g.w) * g.C;
+  return v < 0 ? 0 : (int)v;
+}
+__host__ __device__ inline int win_hi(const Geo& g, int c) {
+  long v = (long)(c + g.w + 1) * g.C;
+  return (v > g.T ? g.T : (int)v) - 1;
+}
+__host__ __device__ inline bool is_anchor(const Geo& g, int t) {
+  return (g.af && t == 0) || (g.al && t == g.T - 1);
+}
+
+// Video key segments (token ranges, merged where adjacent) visible to query
+// frame t.  Returns the number of segments (1..3); seg_start/seg_len in tokens.
+__host__ __device__ inline int key_segments(const Geo& g, int t, int seg_start[3], int seg_len[3]) {
+  if (is_anchor(g, t)) {
+    seg_start[0] = 0; seg_len[0] = g.T * g.P;
+    return 1;
+  }
+  int c = t / g.C;
+  int lo = win_lo(g, c), hi = win_hi(g, c);
+  int n = 0;
+  // frame 0 anchor, merged into the window when adjacent
+  if (g.af && lo > 0) {
+    if (lo == 1) lo = 0;
+    else { seg_start[n] = 0; seg_len[n] = g.P; ++n; }
+  }
+  bool tail = false;
+  if (g.al && hi < g.T - 1) {
+    if (hi == g.T - 2) hi = g.T - 1;
+    else tail = true;
+  }
+  seg_start[n] = lo * g.P; seg_len[n] = (hi - lo + 1) * g.P; ++n;
+  if (tail) { seg_start[n] = (g.T - 1) * g.P; seg_len[n] = g.P; ++n; }
+  return n;
+}
+
+// True when chunk c holds at least one non-anchor frame (a frame that reads
+// the linear states).  Only the first and last chunk can fail this.
+__host__ __device__ inline bool chunk_has_query(const Geo& g, int c) {
+  int first = c * g.C, last = imin(g.T, (c + 1) * g.C) - 1;
+  int n = last - first + 1;
+  int na = (g.af && first == 0) ? 1 : 0;
+  if (g.al && last == g.T - 1 && !(g.af && g.T - 1 == 0)) ++na;
+  return n > na;
+}
+
+// Frames the scans fold: forward uses non-anchor frames below the window
+// start of the last chunk that has query frames; backward uses non-anchor
+// frames above the window end of the first such chunk (both exclusive bounds).
+__host__ __device__ inline int fwd_scan_end(const Geo& g) {
+  for (int c = g.nc - 1; c >= 0; --c)
+    if (chunk_has_query(g, c)) return win_lo(g, c);
+  return 0;
+}
+__host__ __device__ inline int bwd_scan_begin(const Geo& g) {
+  for (int c = 0; c < g.nc; ++c)
+    if (chunk_has_query(g, c)) return win_hi(g, c);
+  return g.T - 1;
+}
+
+__host__ __device__ inline bool frame_needs_stats(const Geo& g, int f) {
+  if (is_anchor(g, f)) return false;
+  return f < fwd_scan_end(g) || f > bwd_scan_begin(g);
+}
+
+// Statistics slots of one (batch, head): frames the scans fold (or every
+// frame when `all_frames`), then the text block as slot T.  slot_of maps the
+// dense index 0..count_slots-1 to the slot.
+__host__ __device__ inline int slot_of(const Geo& g, int idx, bool all_frames) {
+  if (all_frames) return idx;
+  int lo_end = fwd_scan_end(g);
+  int hi_begin = bwd_scan_begin(g);
+  int f0 = g.af ? 1 : 0;                     // first non-anchor frame
+  int f1 = g.al ? g.T - 2 : g.T - 1;         // last non-anchor frame
+  int a = imin(lo_end, f1 + 1);
+  int n_lo = imax(0, a - f0);
+  if (idx < n_lo) return f0 + idx;
+  idx -= n_lo;
+  int start_hi = imax(hi_begin + 1, imax(f0, a));
+  int n_hi = imax(0, f1 + 1 - start_hi);
+  if (idx < n_hi) return start_hi + idx;
+  return g.T;
+}
+
+__host__ __device__ inline int count_slots(const Geo& g, bool all_frames) {
+  if (all_frames) return g.T + 1;
+  int n = 0;
+  for (int f = 0; f < g.T; ++f) n += frame_needs_stats(g, f) ? 1 : 0;
+  return n + 1;
+}
+
+// Workspace plan (bytes, each region 256-byte aligned).
+struct Plan {
+  size_t a_off, b_off, sf_off, sb_off, r_off, total;
+};
+
+__host__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ inline Plan make_plan(const vdn_layout_t& l) {
+  Geo g = make_geo(l);
+  size_t d = (size_t)l.head_dim_k;
+  size_t bh = (size_t)l.batch * l.heads;
+  size_t mat = d * d * sizeof(float);
+  size_t stats = bh * (size_t)(g.T + 1) * mat;
+  size_t snaps = bh * (size_t)(g.nc + 1) * mat;
+  Plan p;
+  p.a_off = 0;
+  p.b_off = align256(p.a_off + stats);
+  p.sf_off = align256(p.b_off + stats);
+  p.sb_off = align256(p.sf_off + snaps);
+  p.r_off = align256(p.sb_off + snaps);
+  p.total = align256(p.r_off + snaps);
+  return p;
+}
+
+__host__ inline size_t scan_ws_bytes(const vdn_layout_t& l) {
+  Geo g = make_geo(l);
+  size_t d = (size_t)l.head_dim_k;
+  size_t snaps = (size_t)l.batch * l.heads * (size_t)(g.nc + 1) * d * d * sizeof(float);
+  return 2 * align256(snaps);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (one translation unit each).  All return hipError_t of the
+// launch.  Pointers are device pointers; shapes were validated by the caller.
+// ---------------------------------------------------------------------------
+hipError_t launch_softmax(const void* q, const void* k, const void* v, const void* tk,
+                          const void* tv, const vdn_layout_t& l, float scale, void* o,
+                          hipStream_t s);
+hipError_t launch_gram(const void* k, const void* v, const void* tk, const void* tv,
+                       const float* beta, const vdn_layout_t& l, bool all_frames, float* A,
+                       float* B, hipStream_t s);
+hipError_t launch_factor(float* A, const vdn_layout_t& l, bool all_frames, hipStream_t s);
+hipError_t launch_scan(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
+                       float* Sf, float* Sb, float* R, hipStream_t s);
+hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
+                        const vdn_layout_t& l, float eps, void* o, hipStream_t s);
+
+}  // namespace vdn

@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of one Video DeltaNet hybrid video-to-video attention layer
+forward on one MI355X, at the 768p shape (B=1, H=24, d=128, 60 latent frames x
+1008 tokens = 60,480 video tokens, 512 text tokens, bf16).
+
+A step is one call of the whole layer (vdn_hybrid_attn_fwd: Gram/write,
+factor, scan, softmax, merge) on synthetic inputs already resident in HBM.
+Prints one JSON line: layer throughput in video tokens/s, the roofline of the
+dominant kernel (block-sparse softmax, timed alone with HIP events on its
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k1_softmax_768p_hbm_traffic.md")
+K1_SOURCES = ["video_diffusion_hybrid_block_amd/csrc/k_softmax.hip",
+              "video_diffusion_hybrid_block_amd/csrc/vdn_device.h",
+              "video_diffusion_hybrid_block_amd/csrc/vdn_internal.h"]
+
+
+def visible_keys_per_frame(w):
+    """Keys one query of frame t scores: video tokens of the visible frames
+    (own chunk +- window, plus the first/last frame; anchors see everything)
+    and all text tokens."""
+    T, C, wc = w.frames, w.chunk_frames, w.window_chunks
+    out = []
+    for t in range(T):
+        if t in (0, T - 1):
+            nf = T
+        else:
+            c = t // C
+            lo, hi = max(0, (c - wc) * C), min(T, (c + wc + 1) * C) - 1
+            vis = set(range(lo, hi + 1)) | {0, T - 1}
+            nf = len(vis)
+        out.append(nf * w.tokens_per_frame + w.text_tokens)
+    return out
+
+
+def softmax_flops(w):
+    """Algorithmic work of the softmax kernel: 4*d flops (q.k and p*v) per
+    visible (query, key) pair, all batches and heads."""
+    pairs = sum(k * w.tokens_per_frame for k in visible_keys_per_frame(w))
+    return 4.0 * w.head_dim * pairs * w.batch * w.heads
+
+
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per softmax launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sources_sha256_16") != sources_hash(K1_SOURCES):
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp):
+    """The float64 oracle on a bounded sample: every token of five frames
+    (both anchors and three interior frames) of head 0, batch 0."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import vdn_oracle as O
+    from video_diffusion_hybrid_block_amd import synth
+    lay = O.Layout(**synth.layout_kwargs(w))
+    frames = sorted({0, w.frames // 4, w.frames // 2, (3 * w.frames) // 4, w.frames - 1})
+    P = w.tokens_per_frame
+    import numpy as np
+    tokens = np.concatenate([np.arange(f * P, (f + 1) * P) for f in frames])
+    t0 = time.perf_counter()
+    O.hybrid_attn_rows(inp, lay, 0, 0, tokens)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    # one video token of the layer = all heads of that token
+    tok_equiv = len(tokens) / (w.heads * w.batch) * w.batch
+    return {"value": tok_equiv / dt, "unit": "video tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(tokens)} query tokens (frames {frames}) of one head, batch 0; "
+                      f"{dt:.1f} s; counted as {len(tokens)}/{w.heads} layer tokens"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="768p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the layer shards by head; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from video_diffusion_hybrid_block_amd import binding as V
+    from video_diffusion_hybrid_block_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = {}
+    for k, a in inp.items():
+        t = torch.from_numpy(a)
+        if k in ("q", "k", "v", "text_k", "text_v"):
+            t = t.to(tdt)
+        dev[k] = t.cuda()
+    L = w.text_tokens
+    geo = dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+               window_chunks=w.window_chunks)
+    lay = V.make_layout(batch=w.batch, heads=w.heads, head_dim=w.head_dim, frames=w.frames,
+                        tokens_per_frame=w.tokens_per_frame, text_tokens=L, dtype=w.dtype,
+                        chunk_frames=w.chunk_frames, window_chunks=w.window_chunks)
+    ws = torch.empty(V.workspace_size(lay), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    o_soft = torch.empty_like(dev["q"])
+    tk, tv = (dev["text_k"], dev["text_v"]) if L else (None, None)
+
+    def layer():
+        V.hybrid_attn(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"],
+                      dev["gate_logits"], **geo, out=out, workspace=ws)
+
+    def softmax_only():
+        V.softmax_fwd(dev["q"], dev["k"], dev["v"], tk, tv, **geo, out=o_soft)
+
+    stream = torch.cuda.current_stream()
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} layer steps", file=sys.stderr,
+          flush=True)
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        layer()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel alone, same stream, same launch configuration
+    for _ in range(2):
+        softmax_only()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        softmax_only()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k1_ms = e0.elapsed_time(e1) / args.steps
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    video_tokens = w.batch * w.video_tokens
+    value = video_tokens / (ms / 1e3)
+    k1_flops = softmax_flops(w)
+    achieved = k1_flops / (k1_ms / 1e3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": "hybrid-attn layer ms & video tokens/s at 768p shape; % MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "video tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, 768p-shaped: 24x42 latent grid per frame)",
+        "config": {"workload": f"{w.name}: B={w.batch} H={w.heads} d={w.head_dim} "
+                               f"T={w.frames} P={w.tokens_per_frame} L={w.text_tokens} "
+                               f"chunk={w.chunk_frames} window=+-{w.window_chunks}",
+                   "video_tokens": video_tokens, "parallelism": "single GPU"},
+        "roofline": {"kernel": "softmax_mfma_kernel<128>", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": k1_flops, "ms_per_launch": round(k1_ms, 4)},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,8 +13,11 @@
 // as a 16 x 16 grid; thread (ti, tk) keeps the (d/16) x (d/16) block of rows
 // ti, columns tk of the matrix in registers for the whole factorisation.  Each
 // elimination step broadcasts one column (Cholesky) or one row (substitution)
-// through LDS with double-buffered vectors: one barrier per step.  L is kept in
-// LDS for the substitution; X replaces it for the product.  All fp32.
+// through LDS with double-buffered vectors: one barrier per step.  The step
+// loop is unrolled by the block size so every register index is static (no
+// divergent selects), and waves own column groups so a wave whose columns are
+// finished skips the step.  L is kept in LDS for the substitution; X replaces
+// it for the product.  All fp32.
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
@@ -25,111 +28,112 @@ namespace {
 template <int D>
 __global__ void __launch_bounds__(256)
 factor_kernel(float* __restrict__ A, Geo g, int nslots, bool all_frames) {
-  constexpr int BS = D / 16;
+  constexpr int BS = D / 16;       // rows / columns per thread block
   constexpr int LD = D + 1;
   __shared__ float Ls[D * LD];
-  __shared__ float vec[2][D];
+  __shared__ __attribute__((aligned(16))) float vec[2][D];
 
   const int tid = threadIdx.x;
-  const int ti = tid >> 4, tk = tid & 15;
+  // Waves own column groups (tk = 4w .. 4w+3), so a wave whose columns are
+  // finished skips a step as a whole.
+  const int ti = tid & 15, tk = tid >> 4;
+  const int wq = tid >> 6;
   const int r0 = ti * BS, c0 = tk * BS;
   const int task = blockIdx.x;
   const int bh = task / nslots;
   const int slot = slot_of(g, task % nslots, all_frames);
   float* Mg = A + ((size_t)bh * (g.T + 1) + slot) * D * D;
 
-  // M = I + A, owned block in registers.
   float m[BS][BS];
 #pragma unroll
   for (int i = 0; i < BS; ++i)
 #pragma unroll
-    for (int j = 0; j < BS; ++j) {
-      float x = Mg[(size_t)(r0 + i) * D + c0 + j];
-      m[i][j] = x + ((r0 + i) == (c0 + j) ? 1.0f : 0.0f);
-    }
+    for (int j = 0; j < BS; ++j)
+      m[i][j] = Mg[(size_t)(r0 + i) * D + c0 + j] + ((r0 + i) == (c0 + j) ? 1.0f : 0.0f);
 
-  // ---- Cholesky, right-looking, one column per step ----
-  for (int j = 0; j < D; ++j) {
-    float* col = vec[j & 1];
-    if (tk == j / BS && ti >= j / BS) {
-      const int jm = j % BS;
+  // ---- Cholesky I + A = L L^T, right-looking, one column per step ----
+  // Step j: the owners of column j publish it; every thread then forms
+  // l_i = M[i][j] / sqrt(M[j][j]) for its rows (zero above j) and applies the
+  // rank-1 update to its columns > j.  Column j of L (zeros above the
+  // diagonal) goes to LDS.
+  for (int kb = 0; kb < 16; ++kb) {
 #pragma unroll
-      for (int i = 0; i < BS; ++i) {
-        float val = 0.f;
+    for (int km = 0; km < BS; ++km) {
+      const int j = kb * BS + km;
+      float* col = vec[j & 1];
+      if (tk == kb) {
 #pragma unroll
-        for (int c = 0; c < BS; ++c) val = (c == jm) ? m[i][c] : val;
-        if (r0 + i >= j) col[r0 + i] = val;
+        for (int i = 0; i < BS; ++i) col[r0 + i] = m[i][km];
       }
-    }
-    __syncthreads();
-    const float piv = col[j];
-    const float rs = rsqrtf(piv);
-    if (ti >= j / BS) {
-      float li[BS], lk[BS];
+      __syncthreads();
+      if (4 * wq + 3 >= kb) {
+        const float rs = rsqrtf(col[j]);
+        float li[BS], lk[BS];
 #pragma unroll
-      for (int i = 0; i < BS; ++i) li[i] = (r0 + i >= j) ? col[r0 + i] * rs : 0.f;
-#pragma unroll
-      for (int c = 0; c < BS; ++c) lk[c] = (c0 + c > j) ? col[c0 + c] * rs : 0.f;
-#pragma unroll
-      for (int i = 0; i < BS; ++i)
+        for (int i = 0; i < BS; ++i) {
+          const float v = col[r0 + i];
+          li[i] = (r0 + i >= j) ? v * rs : 0.f;
+        }
 #pragma unroll
         for (int c = 0; c < BS; ++c) {
-          if (c0 + c == j) {
-            if (r0 + i >= j) {
-              m[i][c] = li[i];               // final L[i][j]
-              Ls[(r0 + i) * LD + j] = li[i];
-            }
-          } else if (r0 + i >= c0 + c) {
-            m[i][c] = fmaf(-li[i], lk[c], m[i][c]);
-          }
+          const float v = col[c0 + c];
+          lk[c] = (c0 + c > j) ? v * rs : 0.f;
         }
+#pragma unroll
+        for (int i = 0; i < BS; ++i)
+#pragma unroll
+          for (int c = 0; c < BS; ++c) m[i][c] = fmaf(-li[i], lk[c], m[i][c]);
+        if (tk == kb) {
+#pragma unroll
+          for (int i = 0; i < BS; ++i) Ls[(r0 + i) * LD + j] = li[i];
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- X = L^-1 (lower), forward substitution, one row per step ----
+  // ---- X = L^-1 (lower triangular), forward substitution by rows ----
   float x[BS][BS];
 #pragma unroll
   for (int i = 0; i < BS; ++i)
 #pragma unroll
     for (int c = 0; c < BS; ++c) x[i][c] = (r0 + i == c0 + c) ? 1.0f : 0.0f;
-  for (int kk = 0; kk < D; ++kk) {
-    float* row = vec[kk & 1];
-    if (ti == kk / BS && tk <= ti) {
-      const float inv = 1.0f / Ls[kk * LD + kk];
-      const int im = kk % BS;
+  for (int kb = 0; kb < 16; ++kb) {
 #pragma unroll
-      for (int i = 0; i < BS; ++i) {
-        if (i != im) continue;
+    for (int km = 0; km < BS; ++km) {
+      const int k = kb * BS + km;
+      float* row = vec[k & 1];
+      if (ti == kb) {
+        const float inv = 1.0f / Ls[k * LD + k];
 #pragma unroll
         for (int c = 0; c < BS; ++c) {
-          if (c0 + c <= kk) {
-            x[i][c] *= inv;
-            row[c0 + c] = x[i][c];
-          }
+          x[km][c] *= inv;
+          row[c0 + c] = x[km][c];
         }
       }
-    }
-    __syncthreads();
-    if (tk <= ti && r0 + BS - 1 > kk && c0 <= kk) {
+      __syncthreads();
+      if (4 * wq <= kb) {
+        float lik[BS], rv[BS];
 #pragma unroll
-      for (int i = 0; i < BS; ++i) {
-        if (r0 + i > kk) {
-          const float lik = Ls[(r0 + i) * LD + kk];
-#pragma unroll
-          for (int c = 0; c < BS; ++c)
-            if (c0 + c <= kk) x[i][c] = fmaf(-lik, row[c0 + c], x[i][c]);
+        for (int i = 0; i < BS; ++i) {
+          const float v = Ls[(r0 + i) * LD + k];
+          lik[i] = (r0 + i > k) ? v : 0.f;
         }
+#pragma unroll
+        for (int c = 0; c < BS; ++c) rv[c] = row[c0 + c];
+#pragma unroll
+        for (int i = 0; i < BS; ++i)
+#pragma unroll
+          for (int c = 0; c < BS; ++c) x[i][c] = fmaf(-lik[i], rv[c], x[i][c]);
       }
     }
   }
   __syncthreads();
-  // X (lower, zeros above) replaces L in LDS.
+  // X (exactly lower triangular) replaces L in LDS.
 #pragma unroll
   for (int i = 0; i < BS; ++i)
 #pragma unroll
-    for (int c = 0; c < BS; ++c)
-      Ls[(r0 + i) * LD + c0 + c] = (tk <= ti && r0 + i >= c0 + c) ? x[i][c] : 0.0f;
+    for (int c = 0; c < BS; ++c) Ls[(r0 + i) * LD + c0 + c] = x[i][c];
   __syncthreads();
 
   // ---- G = X^T X, block (ti, tk) ----

@@ -23,7 +23,7 @@ namespace vdn {
 namespace {
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 gram_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
                  const bf16* __restrict__ tk, const bf16* __restrict__ tv,
                  const float* __restrict__ beta, float* __restrict__ Aout,
@@ -31,10 +31,12 @@ gram_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   constexpr int BT = 64;                     // tokens per tile
   constexpr int KCH = D / 8;
   constexpr int TILE = BT * D * 2;
-  constexpr int NI = BT * KCH / 256;         // DMA instructions per thread per tensor
+  constexpr int NW = 8;                      // waves per workgroup
+  constexpr int NT = 64 * NW;
+  constexpr int NI = BT * KCH / NT >= 1 ? BT * KCH / NT : 1;  // DMA instructions per thread
   constexpr int NB = D / 32;                 // 32-wide blocks per matrix side
   constexpr int NBLK = 2 * NB * NB;
-  constexpr int BLK_PER_WAVE = NBLK >= 4 ? NBLK / 4 : 1;
+  constexpr int BLK_PER_WAVE = NBLK >= NW ? NBLK / NW : 1;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   __shared__ float bsh[BT];
   char VDN_LDS* lds = (char VDN_LDS*)smem;
@@ -65,7 +67,8 @@ gram_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
     __syncthreads();                          // previous tile fully consumed
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-      int blk = ii * 4 + wv;
+      int blk = ii * NW + wv;
+      if (blk * 64 >= BT * KCH) break;
       int p = blk * 64 + lane;
       int row = p / KCH, pch = p % KCH;
       int ch = pch ^ swz<D>(row);
@@ -83,7 +86,8 @@ gram_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
     // beta*k -> bf16 hi / lo, same swizzled layout as K
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-      int p = (ii * 4 + wv) * 64 + lane;
+      if ((ii * NW + wv) * 64 >= BT * KCH) break;
+      int p = (ii * NW + wv) * 64 + lane;
       int row = p / KCH;
       const float bt = bsh[row];
       bf16x8 kv = *(const bf16x8 VDN_LDS*)(Kt + p * 16);
@@ -177,7 +181,7 @@ hipError_t launch_mfma(const void* k, const void* v, const void* tk, const void*
   Geo g = make_geo(l);
   int nslots = count_slots(g, all_frames);
   long grid = (long)l.batch * l.heads * nslots;
-  gram_mfma_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+  gram_mfma_kernel<D><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
       (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv, beta, A, B, g, l.heads,
       nslots, all_frames);
   return hipGetLastError();

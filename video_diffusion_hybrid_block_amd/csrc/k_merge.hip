@@ -65,6 +65,14 @@ merge_mfma_kernel(const bf16* __restrict__ q, const bf16* o_soft, const float* _
     bf16x8 qv[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *(const bf16x8*)(q + rowoff + ks * 16 + half * 8);
+    // o_soft and the gate logits are loaded with q: one memory latency per tile
+    bf16x4 os[NB][4];
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        os[bi][jj] = *(const bf16x4*)(o_soft + rowoff + bi * 32 + jj * 8 + half * 4);
+    const float2 gl = *(const float2*)(gates + ((size_t)(b * (size_t)N + tok) * H + h) * 2);
     f32x16 acc[NB];
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
@@ -84,7 +92,6 @@ merge_mfma_kernel(const bf16* __restrict__ q, const bf16* o_soft, const float* _
       for (int j = 0; j < 16; ++j) ss = fmaf(acc[bi][j], acc[bi][j], ss);
     ss = xhalf_sum(ss);
     const float inv = rsqrtf(ss * (1.0f / D) + eps);
-    const float2 gl = *(const float2*)(gates + ((size_t)(b * (size_t)N + tok) * H + h) * 2);
     const float g0 = sigmoidf(gl.x), g1 = sigmoidf(gl.y) * inv;
     if (valid) {
 #pragma unroll
@@ -92,11 +99,10 @@ merge_mfma_kernel(const bf16* __restrict__ q, const bf16* o_soft, const float* _
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d = bi * 32 + jj * 8 + half * 4;
-          bf16x4 os = *(const bf16x4*)(o_soft + rowoff + d);
           bf16x4 out;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            out[e] = (bf16)fmaf(g0, (float)os[e], g1 * acc[bi][jj * 4 + e]);
+            out[e] = (bf16)fmaf(g0, (float)os[bi][jj][e], g1 * acc[bi][jj * 4 + e]);
           *(bf16x4*)(o + rowoff + d) = out;
         }
     }

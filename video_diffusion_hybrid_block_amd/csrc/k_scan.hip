@@ -26,6 +26,22 @@ namespace vdn {
 
 namespace {
 
+// Next frame a chain folds after frame f (-1 when done); f = -1 asks for the
+// first one.  Forward: ascending non-anchor frames below fwd_scan_end;
+// backward: descending non-anchor frames above bwd_scan_begin.
+__device__ __forceinline__ int next_frame(const Geo& g, int dir, int f) {
+  if (dir == 0) {
+    const int fend = fwd_scan_end(g);
+    int n = f + 1;
+    while (n < fend && is_anchor(g, n)) ++n;
+    return n < fend ? n : -1;
+  }
+  const int fbeg = bwd_scan_begin(g);
+  int n = f < 0 ? g.T - 1 : f - 1;
+  while (n > fbeg && is_anchor(g, n)) --n;
+  return n > fbeg ? n : -1;
+}
+
 template <int D>
 __global__ void __launch_bounds__(2 * D)
 scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
@@ -34,6 +50,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
   constexpr int NT = 64 * NRB;
   constexpr int LDF = D + 4;            // fp32 state row stride (floats)
+  constexpr int NBV = 32 * D / NT;      // B values per thread per step
   __shared__ float S[32 * LDF];
   __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
@@ -52,30 +69,44 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   const float* Gbh = G + (size_t)bh * (g.T + 1) * mat;
   const float* Bbh = Bm + (size_t)bh * (g.T + 1) * mat;
   float* snap = (dir == 0 ? Sf : Sb) + (size_t)bh * (g.nc + 1) * mat;
+  const float* al = alpha + (size_t)b * g.T * H + h;
 
   for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
-  __syncthreads();
 
-  // One update S <- (a S + B_slot[rows]) G_slot, times `post`.
-  auto step = [&](int slot, float a, float post) {
+  // Per-step operands, prefetched one step ahead: this lane's G row (B
+  // operand, G symmetric) and its share of the B rows.
+  float4 gcur[D / 8], gnxt[D / 8];
+  float bcur[NBV], bnxt[NBV];
+  auto load = [&](int slot, float4* gr, float* br) {
+    const float4* gp = (const float4*)(Gbh + (size_t)slot * mat + (size_t)(wv * 32 + (lane & 31)) * D);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      gr[2 * ks] = gp[(ks * 16 + half * 8) / 4];
+      gr[2 * ks + 1] = gp[(ks * 16 + half * 8) / 4 + 1];
+    }
     const float* Bs = Bbh + (size_t)slot * mat + (size_t)row0 * D;
-    for (int i = tid; i < 32 * D; i += NT) {
-      int r = i / D, c = i % D;
-      float x = fmaf(a, S[r * LDF + c], Bs[(size_t)r * D + c]);
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) br[i] = Bs[tid + i * NT];
+  };
+  // S <- (a S + B) G, times `post`.
+  auto step = [&](float a, float post) {
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) {
+      const int e = tid + i * NT;
+      const int r = e / D, c = e % D;
+      const float x = fmaf(a, S[r * LDF + c], bcur[i]);
       bf16 hi, lo;
       split_bf16(x, hi, lo);
-      int off = swz_off<D>(r, c);
+      const int off = swz_off<D>(r, c);
       *(bf16 VDN_LDS*)(Xh + off) = hi;
       *(bf16 VDN_LDS*)(Xl + off) = lo;
     }
     __syncthreads();
-    const float* Gs = Gbh + (size_t)slot * mat + (size_t)(wv * 32 + (lane & 31)) * D;
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const float4* gp = (const float4*)(Gs + ks * 16 + half * 8);
-      float4 g0 = gp[0], g1 = gp[1];
-      float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float4 g0 = gcur[2 * ks], g1 = gcur[2 * ks + 1];
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       bf16x8 gh, gl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -84,15 +115,15 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
         gh[e] = a_;
         gl[e] = c_;
       }
-      bf16x8 ah = lds_row8<D>(Xh, lane & 31, ks * 2 + half);
-      bf16x8 al = lds_row8<D>(Xl, lane & 31, ks * 2 + half);
+      const bf16x8 ah = lds_row8<D>(Xh, lane & 31, ks * 2 + half);
+      const bf16x8 alo = lds_row8<D>(Xl, lane & 31, ks * 2 + half);
       acc = mfma32(ah, gh, acc);
       acc = mfma32(ah, gl, acc);
-      acc = mfma32(al, gh, acc);
+      acc = mfma32(alo, gh, acc);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      int r = (j >> 2) * 8 + half * 4 + (j & 3);
+      const int r = (j >> 2) * 8 + half * 4 + (j & 3);
       S[r * LDF + wv * 32 + (lane & 31)] = acc[j] * post;
     }
     __syncthreads();
@@ -102,26 +133,42 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
     for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
   };
 
-  if (g.L > 0) step(g.T, 0.0f, 0.5f);   // S0 = S_x / 2
+  int f = next_frame(g, dir, -1);
+  if (g.L > 0) {
+    load(g.T, gcur, bcur);
+    if (f >= 0) load(f, gnxt, bnxt);
+    __syncthreads();
+    step(0.0f, 0.5f);                    // S0 = S_x / 2
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) bcur[i] = bnxt[i];
+  } else {
+    if (f >= 0) load(f, gcur, bcur);
+    __syncthreads();
+  }
   snapshot(g.nc);
-  const float* al = alpha + (size_t)b * g.T * H + h;
-  if (dir == 0) {
-    const int fend = fwd_scan_end(g);
-    int c = 0;
-    for (int f = 0; f < fend; ++f) {
-      while (c < g.nc && win_lo(g, c) == f) snapshot(c++);
-      if (is_anchor(g, f)) continue;
-      step(f, al[(size_t)f * H], 1.0f);
+  int c = dir == 0 ? 0 : g.nc - 1;
+  while (f >= 0) {
+    const int fn = next_frame(g, dir, f);
+    if (fn >= 0) load(fn, gnxt, bnxt);
+    // chunks whose state is the one before frame f (anchors in between do
+    // not change the state)
+    if (dir == 0) {
+      while (c < g.nc && win_lo(g, c) <= f) snapshot(c++);
+    } else {
+      while (c >= 0 && win_hi(g, c) >= f) snapshot(c--);
     }
+    step(al[(size_t)f * H], 1.0f);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
+#pragma unroll
+    for (int i = 0; i < NBV; ++i) bcur[i] = bnxt[i];
+    f = fn;
+  }
+  if (dir == 0) {
     while (c < g.nc) snapshot(c++);
   } else {
-    const int fbeg = bwd_scan_begin(g);
-    int c = g.nc - 1;
-    for (int f = g.T - 1; f > fbeg; --f) {
-      while (c >= 0 && win_hi(g, c) == f) snapshot(c--);
-      if (is_anchor(g, f)) continue;
-      step(f, al[(size_t)f * H], 1.0f);
-    }
     while (c >= 0) snapshot(c--);
   }
 }

@@ -23,6 +23,8 @@
 //  * exp2 with the scale * log2(e) folded into one FMA; fp32 statistics.
 //  * Work order: anchor-frame tiles (the heaviest) first; with B*H a multiple
 //    of 8 each XCD gets a fixed set of heads so K/V tiles are shared in its L2.
+#include <type_traits>
+
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
@@ -104,8 +106,33 @@ __device__ __forceinline__ bool key_src(const KeyMap& m, int kv, int b, int h, i
   return false;
 }
 
+// Branch-free form for the MFMA kernel: element offset (relative to the
+// head's base pointer, in units of H*D elements per token) and text flag.
+struct KeyAddr {
+  int e0, e1, e2, nkeys;   // ends of the three video segments and of the text
+  int d0, d1, d2;          // token = kv + d_seg inside video segment seg
+  int clamp_tok;
+};
+
+__device__ __forceinline__ KeyAddr key_addr(const KeyMap& m) {
+  KeyAddr a;
+  a.e0 = m.n0; a.e1 = m.n0 + m.n1; a.e2 = m.nvid; a.nkeys = m.nkeys;
+  a.d0 = m.s0; a.d1 = m.s1 - m.n0; a.d2 = m.s2 - m.n0 - m.n1;
+  a.clamp_tok = m.s0;
+  return a;
+}
+
+// Token row of virtual key kv; `text` tells which tensor it indexes.
+// Returns the row, plus 0x40000000 when the key is a text key.
+__device__ __forceinline__ int key_row(KeyAddr a, int kv) {
+  int d = kv < a.e0 ? a.d0 : (kv < a.e1 ? a.d1 : a.d2);
+  bool text = (kv >= a.e2) & (kv < a.nkeys);
+  int vtok = kv < a.e2 ? kv + d : a.clamp_tok;
+  return text ? ((kv - a.e2) | 0x40000000) : vtok;
+}
+
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, const bf16* __restrict__ tk,
                     const bf16* __restrict__ tv, bf16* __restrict__ o, Geo g, int B, int H,
@@ -133,21 +160,27 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
 
-  auto issue_load = [&](int kbase, int buf) {
+  const KeyAddr ka = key_addr(km);
+  const int HD = H * D;
+  const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
+  const bf16* vbh = v + ((size_t)w.b * N * H + w.h) * D;
+  const bf16* tkbh = tk + ((size_t)w.b * g.L * H + w.h) * D;
+  const bf16* tvbh = tv + ((size_t)w.b * g.L * H + w.h) * D;
+  const int pch = lane % KCH;              // physical chunk of this lane (64 % KCH == 0)
+  auto issue_load = [=](int kbase, int buf) {
     char VDN_LDS* kt = lds + buf * 2 * TILE;
     char VDN_LDS* vt = kt + TILE;
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-      int blk = ii * 4 + wv;                   // 64-chunk block of the tile
-      int p = blk * 64 + lane;                 // physical chunk
-      int row = p / KCH, pch = p % KCH;
-      int ch = pch ^ swz<D>(row);
-      size_t off;
-      bool txt = key_src(km, kbase + row, w.b, w.h, H, N, g.L, D, off);
-      const bf16* ksrc = (txt ? tk : k) + off + ch * 8;
-      const bf16* vsrc = (txt ? tv : v) + off + ch * 8;
-      g2lds16(ksrc, kt + blk * 1024);
-      g2lds16(vsrc, vt + blk * 1024);
+      const int blk = ii * 4 + wv;             // 64-chunk block of the tile
+      const int row = (blk * 64 + lane) / KCH;
+      const int ch = pch ^ swz<D>(row);
+      const int r = key_row(ka, kbase + row);
+      const bool txt = (r & 0x40000000) != 0;
+      const int tok = r & 0x3FFFFFFF;
+      const size_t off = (size_t)(unsigned)(tok * HD) + ch * 8;
+      g2lds16((txt ? tkbh : kbh) + off, kt + blk * 1024);
+      g2lds16((txt ? tvbh : vbh) + off, vt + blk * 1024);
     }
   };
 
@@ -157,9 +190,12 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   const int ntiles = (km.nkeys + BN - 1) / BN;
+  const int nfull = km.nkeys / BN;            // tiles without padding keys
   const int prow0 = perm32(lane & 31);
-  issue_load(0, 0);
-  for (int it = 0; it < ntiles; ++it) {
+
+  // One 64-key tile: scores, online softmax, P V.  MASKED (the partial last
+  // tile only) sets scores of keys past the end to -inf.
+  auto tile = [&](int it, auto masked) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < ntiles) issue_load((it + 1) * BN, (it + 1) & 1);
@@ -176,7 +212,7 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         s[kb] = mfma32(a, qreg[ks], s[kb]);
       }
     }
-    if ((it + 1) * BN > km.nkeys) {
+    if constexpr (decltype(masked)::value) {
       const int base = it * BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -192,9 +228,18 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
     mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = fast_exp2((m_run - m_new) * c);
-    const float mc = m_new * c;
+    // Lazy rescale: the exponent offset m_run only moves when some query's
+    // max grows by more than 2^8 (in exp2 units); until then p <= 256, which
+    // bf16 P and the fp32 sums carry exactly as well.
+    if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2((m_run - m_new) * c);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
     float rs = 0.f;
     bf16x8 pk[4];
 #pragma unroll
@@ -205,10 +250,7 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         rs += p;
         pk[kb * 2 + (j >> 3)][j & 7] = (bf16)p;
       }
-    l_run = l_run * corr + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+    l_run += rs;
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp)
 #pragma unroll
@@ -216,7 +258,11 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         bf16x8 a = lds_col8<D>(vt, sp * 16, db * 32, lane);
         oacc[db] = mfma32(a, pk[sp], oacc[db]);
       }
-  }
+  };
+
+  issue_load(0, 0);
+  for (int it = 0; it < nfull; ++it) tile(it, std::false_type{});
+  if (nfull < ntiles) tile(nfull, std::true_type{});
 
   const float inv = 1.0f / xhalf_sum(l_run);
   if (qvalid) {

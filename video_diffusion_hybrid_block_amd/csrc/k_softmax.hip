@@ -131,6 +131,43 @@ __device__ __forceinline__ int key_row(KeyAddr a, int kv) {
   return text ? ((kv - a.e2) | 0x40000000) : vtok;
 }
 
+// Work order of the MFMA kernel.  Anchor-frame tiles (every key of the head)
+// come first.  When B*H is a multiple of 8, XCD x (blocks x, x+8, ...) owns
+// heads x*G/8 .. and walks them head by head, so the ~64 workgroups resident
+// on one XCD belong to a few neighbouring chunks of one head and stream the
+// same keys through that XCD's L2 at about the same time.
+__device__ __forceinline__ WorkItem decode_work_xcd(const Geo& g, int B, int H, int tpf) {
+  const int G = B * H;
+  if ((G & 7) != 0) return decode_work(g, B, H, tpf);
+  const int i = blockIdx.x;
+  const int xcd = i & 7, j = i >> 3, gper = G >> 3;
+  const int first = g.af ? 0 : -1;
+  const int last = (g.al && !(g.af && g.T == 1)) ? g.T - 1 : -1;
+  const int na = (first >= 0) + (last >= 0);
+  const int nanchor_items = na * tpf * gper;
+  int gl, t, tile;
+  if (j < nanchor_items) {
+    gl = j % gper;
+    const int r = j / gper;
+    t = (r / tpf == 0 && first >= 0) ? first : last;
+    tile = r % tpf;
+  } else {
+    const int jj = j - nanchor_items;
+    const int per_head = (g.T - na) * tpf;
+    gl = jj / per_head;
+    const int r = jj % per_head;
+    t = r / tpf + (g.af ? 1 : 0);
+    tile = r % tpf;
+  }
+  const int gi = xcd * gper + gl;
+  WorkItem w;
+  w.b = gi / H;
+  w.h = gi % H;
+  w.t = t;
+  w.tile = tile;
+  return w;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -138,20 +175,29 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ tv, bf16* __restrict__ o, Geo g, int B, int H,
                     int tpf, float c) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KCH = D / 8;                  // 16-byte chunks per row
-  constexpr int TILE = BN * D * 2;            // bytes of one K or V tile
-  constexpr int NI = BN * KCH / 256;          // DMA instructions per thread per tensor
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  constexpr int KCH = D / 8;                         // 16-byte data chunks per row
+  // LDS rows are padded (no XOR swizzle): with 64 banks, 16 consecutive K rows
+  // read at one 16-byte column and 4 consecutive V rows x 64 bytes read by
+  // ds_read_b64_tr_b16 both fall on distinct banks, and every read address is
+  // a per-lane base plus a compile-time offset.
+  constexpr int KST = 2 * D + 16;                    // K row stride, bytes
+  constexpr int VST = D == 32 ? 64 : 2 * D + 64;     // V row stride, bytes
+  constexpr int KSL = KST / 16, VSL = VST / 16;      // 16-byte slots per row
+  constexpr int KT = BN * KST, VT = BN * VST;
+  constexpr int BUFB = KT + VT;                      // one K+V buffer
+  constexpr int NIK = (KSL + 3) / 4, NIV = (VSL + 3) / 4;   // DMA instructions per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB];
   char VDN_LDS* lds = (char VDN_LDS*)smem;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int half = lane >> 5;
   const int N = g.T * g.P;
-  const WorkItem w = decode_work(g, B, H, tpf);
+  const WorkItem w = decode_work_xcd(g, B, H, tpf);
   const KeyMap km = key_map(g, w.t);
+  const KeyAddr ka = key_addr(km);
 
-  // Query rows of this wave.
+  // Query rows of this wave (B operand of S^T = K Q^T, kept in registers).
   const int qlocal = w.tile * BM + wv * 32 + (lane & 31);
   const bool qvalid = qlocal < g.P;
   const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
@@ -160,29 +206,76 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
 
-  const KeyAddr ka = key_addr(km);
   const int HD = H * D;
   const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
   const bf16* vbh = v + ((size_t)w.b * N * H + w.h) * D;
   const bf16* tkbh = tk + ((size_t)w.b * g.L * H + w.h) * D;
   const bf16* tvbh = tv + ((size_t)w.b * g.L * H + w.h) * D;
-  const int pch = lane % KCH;              // physical chunk of this lane (64 % KCH == 0)
-  auto issue_load = [=](int kbase, int buf) {
-    char VDN_LDS* kt = lds + buf * 2 * TILE;
-    char VDN_LDS* vt = kt + TILE;
+
+  // Per-lane DMA slots: instruction i of this wave fills LDS slot
+  // j = (4i + wv) * 64 + lane, i.e. row j / SLOTS, chunk j % SLOTS (pad slots
+  // repeat the row's last chunk).  koff / voff: element offset of that chunk
+  // relative to the row's token.
+  int krow[NIK], kch[NIK], vrow[NIV], vch[NIV];
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int blk = ii * 4 + wv;             // 64-chunk block of the tile
-      const int row = (blk * 64 + lane) / KCH;
-      const int ch = pch ^ swz<D>(row);
-      const int r = key_row(ka, kbase + row);
-      const bool txt = (r & 0x40000000) != 0;
-      const int tok = r & 0x3FFFFFFF;
-      const size_t off = (size_t)(unsigned)(tok * HD) + ch * 8;
-      g2lds16((txt ? tkbh : kbh) + off, kt + blk * 1024);
-      g2lds16((txt ? tvbh : vbh) + off, vt + blk * 1024);
+  for (int i = 0; i < NIK; ++i) {
+    const int j = (i * 4 + wv) * 64 + lane;
+    krow[i] = j / KSL;
+    kch[i] = imin(j % KSL, KCH - 1) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NIV; ++i) {
+    const int j = (i * 4 + wv) * 64 + lane;
+    vrow[i] = j / VSL;
+    vch[i] = imin(j % VSL, KCH - 1) * 8;
+  }
+
+  auto seg_of = [=](int kv) {
+    return (kv >= ka.e0) + (kv >= ka.e1) + (kv >= ka.e2) + (kv >= ka.nkeys);
+  };
+  auto issue_load = [=](int kb0, char VDN_LDS* kt) {
+    char VDN_LDS* vt = kt + KT;
+    const int s0 = seg_of(kb0), s1 = seg_of(kb0 + BN - 1);
+    if (s0 == s1 && s0 < 4) {
+      // whole tile inside one segment: token = kv + d (uniform)
+      const bool txt = s0 == 3;
+      const int d = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
+      const size_t tok0 = (size_t)(kb0 + d) * HD;
+      const bf16* kb = (txt ? tkbh : kbh) + tok0;
+      const bf16* vb = (txt ? tvbh : vbh) + tok0;
+#pragma unroll
+      for (int i = 0; i < NIK; ++i)
+        if (i * 4 + wv < KSL) g2lds16(kb + (krow[i] * HD + kch[i]), kt + (i * 4 + wv) * 1024);
+#pragma unroll
+      for (int i = 0; i < NIV; ++i)
+        if (i * 4 + wv < VSL) g2lds16(vb + (vrow[i] * HD + vch[i]), vt + (i * 4 + wv) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NIK; ++i) {
+        if (i * 4 + wv >= KSL) continue;
+        const int r = key_row(ka, kb0 + krow[i]);
+        const bool txt = (r & 0x40000000) != 0;
+        const size_t off = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + kch[i];
+        g2lds16((txt ? tkbh : kbh) + off, kt + (i * 4 + wv) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < NIV; ++i) {
+        if (i * 4 + wv >= VSL) continue;
+        const int r = key_row(ka, kb0 + vrow[i]);
+        const bool txt = (r & 0x40000000) != 0;
+        const size_t off = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + vch[i];
+        g2lds16((txt ? tvbh : vbh) + off, vt + (i * 4 + wv) * 1024);
+      }
     }
   };
+
+  // Per-lane LDS read bases.  K (A operand of S^T): row perm32(l%32) of each
+  // 32-key block, chunk 2*ks + half.  V (transposed reads, A operand of
+  // O^T += V^T P^T): lane s of 16-lane group g addresses row 8*(g/2) + s/4,
+  // columns 16*(g%2) + 4*(s%4) .. +3 of the 16-key step.
+  const int kread = perm32(lane & 31) * KST + half * 16;
+  const int gq = lane >> 4, sq = lane & 15;
+  const int vread = (8 * (gq >> 1) + (sq >> 2)) * VST + (16 * (gq & 1) + 4 * (sq & 3)) * 2;
 
   float m_run = -1e30f, l_run = 0.f;
   f32x16 oacc[D / 32];
@@ -190,17 +283,18 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   const int ntiles = (km.nkeys + BN - 1) / BN;
-  const int nfull = km.nkeys / BN;            // tiles without padding keys
-  const int prow0 = perm32(lane & 31);
+  const int nfull = km.nkeys / BN;
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  // One 64-key tile: scores, online softmax, P V.  MASKED (the partial last
-  // tile only) sets scores of keys past the end to -inf.
-  auto tile = [&](int it, auto masked) {
+  // One 64-key tile: scores, online softmax, P V.  BUFC: LDS buffer (0/1,
+  // compile time); MASKED: the partial last tile.
+  auto tile = [&](int it, auto bufc, auto masked) {
+    constexpr int bsel = decltype(bufc)::value;
     wait_vmem();
     __syncthreads();
-    if (it + 1 < ntiles) issue_load((it + 1) * BN, (it + 1) & 1);
-    const char VDN_LDS* kt = lds + (it & 1) * 2 * TILE;
-    const char VDN_LDS* vt = kt + TILE;
+    if (it + 1 < ntiles) issue_load((it + 1) * BN, lds + (1 - bsel) * BUFB);
+    const char VDN_LDS* kt = lds + bsel * BUFB + kread;
+    const char VDN_LDS* vt = lds + bsel * BUFB + KT + vread;
 
     f32x16 s[2];
 #pragma unroll
@@ -208,7 +302,7 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 a = lds_row8<D>(kt, kb * 32 + prow0, ks * 2 + half);
+        const bf16x8 a = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
         s[kb] = mfma32(a, qreg[ks], s[kb]);
       }
     }
@@ -218,7 +312,7 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          int key = base + kb * 32 + ((j >> 3) << 4) + half * 8 + (j & 7);
+          const int key = base + kb * 32 + ((j >> 3) << 4) + half * 8 + (j & 7);
           if (key >= km.nkeys) s[kb][j] = -INFINITY;
         }
     }
@@ -240,29 +334,47 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       m_run = m_new;
     }
     const float mc = m_run * c;
-    float rs = 0.f;
     bf16x8 pk[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p = fast_exp2(fmaf(s[kb][j], c, -mc));
-        rs += p;
-        pk[kb * 2 + (j >> 3)][j & 7] = (bf16)p;
-      }
-    l_run += rs;
+      for (int j = 0; j < 16; ++j)
+        pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(s[kb][j], c, -mc));
+    // row sum of the rounded weights (the ones P V uses): 16 bf16 dot2
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      const bf16x2* p2 = (const bf16x2*)&pk[sp];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l_run = __builtin_amdgcn_fdot2_f32_bf16(p2[e], ones2, l_run, false);
+    }
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        bf16x8 a = lds_col8<D>(vt, sp * 16, db * 32, lane);
+        const char VDN_LDS* pv = vt + sp * 16 * VST + db * 64;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)pv);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)(pv + 4 * VST));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = mfma32(a, pk[sp], oacc[db]);
       }
   };
 
-  issue_load(0, 0);
-  for (int it = 0; it < nfull; ++it) tile(it, std::false_type{});
-  if (nfull < ntiles) tile(nfull, std::true_type{});
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue_load(0, lds);
+  int it = 0;
+  for (; it + 2 <= nfull; it += 2) {
+    tile(it, B0{}, std::false_type{});
+    tile(it + 1, B1{}, std::false_type{});
+  }
+  if (it < nfull) {
+    tile(it, B0{}, std::false_type{});
+    ++it;
+  }
+  if (it < ntiles) {
+    if (it & 1) tile(it, B1{}, std::true_type{});
+    else tile(it, B0{}, std::true_type{});
+  }
 
   const float inv = 1.0f / xhalf_sum(l_run);
   if (qvalid) {
@@ -271,7 +383,7 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        int d = db * 32 + jj * 8 + half * 4;
+        const int d = db * 32 + jj * 8 + half * 4;
         bf16x4 val;
 #pragma unroll
         for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[db][jj * 4 + e] * inv);

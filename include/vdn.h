@@ -126,12 +126,19 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
 /* ---- Per-stage entry points: the same kernels the layer runs, one stage at
  * ---- a time (for checking and profiling each stage). ---- */
 
+/* Bytes of workspace vdn_softmax_fwd needs for `layout` (0 when the layout
+ * needs none or is invalid).  Host only. */
+size_t vdn_softmax_workspace_size(const vdn_layout_t* layout);
+
 /* Softmax branch alone: o_soft [B, T*P, H, d] (layout->dtype) gets, for every
  * video query, one softmax over the keys of its visible frames together with
- * all text keys, times the matching values.  [PaperDaily §二; arXiv abstract] */
+ * all text keys, times the matching values.  workspace: device memory of at
+ * least vdn_softmax_workspace_size(layout) bytes (may be NULL when that is 0),
+ * used for a transposed copy of V.  [PaperDaily §二; arXiv abstract] */
 vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v,
                              const void* text_k, const void* text_v,
                              const vdn_layout_t* layout, void* o_soft,
+                             void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
 /* Frame statistics: for every frame f < T and for the text block (slot T),

@@ -72,7 +72,9 @@ def test_workspace_size_and_chunks():
     assert V.num_chunks(lay) == 12
     ws = V.workspace_size(lay)
     d2 = 128 * 128 * 4
-    assert ws >= 24 * (2 * 61 + 3 * 13) * d2
+    assert ws >= 24 * (2 * 61 + 3 * 13) * d2 + 24 * 128 * (60 * 1008 + 512) * 2
+    assert V.softmax_workspace_size(lay) == 24 * 128 * (60 * 1008 + 512) * 2
+    assert V.softmax_workspace_size(_lay(tokens_per_frame=1001)) == 0   # P not a multiple of 8
     assert V.workspace_size(_lay(frames=120)) > ws
     assert V.workspace_size(_lay(frames=0)) == 0
     assert V.num_chunks(_lay(frames=61)) == 13
@@ -99,7 +101,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     lay_t = _lay(batch=1, heads=1, frames=2, tokens_per_frame=4, text_tokens=3, head_dim=16)
     a = list(args); a[8] = ctypes.byref(lay_t)
     assert lib.vdn_hybrid_attn_fwd(*a) == 1            # text tensors missing
-    assert lib.vdn_softmax_fwd(ok, ok, nul, nul, nul, ref, ok, nul) == 1
+    assert lib.vdn_softmax_fwd(ok, ok, nul, nul, nul, ref, ok, nul, 0, nul) == 1
+    lay_vt = _lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=0, head_dim=32)
+    assert V.softmax_workspace_size(lay_vt) > 0
+    assert lib.vdn_softmax_fwd(ok, ok, ok, nul, nul, ctypes.byref(lay_vt), ok, nul, 0, nul) == 1
+    assert lib.vdn_softmax_fwd(ok, ok, ok, nul, nul, ctypes.byref(lay_vt), ok, ok, 16, nul) == 5
     assert lib.vdn_vda_gram(ok, ok, nul, nul, odd, ref, ok, ok, nul) == 4
     assert lib.vdn_vda_factor_scan(ok, ok, ok, ref, ok, ok, 0, nul) == 5
     assert lib.vdn_merge(ok, ok, ok, ok, ref, nul, nul) == 1

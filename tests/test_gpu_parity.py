@@ -76,6 +76,14 @@ EDGE = [
          text_tokens=0, dtype="bf16"),
     dict(name="long_window_tail", batch=1, heads=1, head_dim=128, frames=23, tokens_per_frame=129,
          text_tokens=130, dtype="bf16", chunk_frames=4),
+    # P and L multiples of 8: the softmax reads V from its transposed copy;
+    # key tiles straddle the window / anchor / text segments
+    dict(name="vt_segments", batch=1, heads=2, head_dim=128, frames=13, tokens_per_frame=40,
+         text_tokens=8, dtype="bf16", chunk_frames=2),
+    dict(name="vt_d32", batch=2, heads=3, head_dim=32, frames=9, tokens_per_frame=24,
+         text_tokens=16, dtype="bf16", chunk_frames=3),
+    dict(name="vt_d64_one_frame", batch=1, heads=2, head_dim=64, frames=1, tokens_per_frame=96,
+         text_tokens=0, dtype="bf16"),
     dict(name="bf16_d16_valu", batch=1, heads=2, head_dim=16, frames=8, tokens_per_frame=24,
          text_tokens=4, dtype="bf16", chunk_frames=2),
     dict(name="f32_d64", batch=1, heads=2, head_dim=64, frames=11, tokens_per_frame=20,

@@ -94,17 +94,25 @@ size_t vdn_vda_factor_scan_workspace_size(const vdn_layout_t* layout) {
   return scan_ws_bytes(*layout);
 }
 
+size_t vdn_softmax_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return softmax_ws_bytes(*layout);
+}
+
 vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v, const void* text_k,
                              const void* text_v, const vdn_layout_t* layout, void* o_soft,
-                             hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   vdn_status_t st = check_layout(layout);
   if (st != VDN_OK) return st;
   if (!q || !k || !v || !o_soft || !text_ok(*layout, text_k, text_v)) return VDN_ERR_NULL_ARG;
+  const size_t need = softmax_ws_bytes(*layout);
+  if (need > 0 && !workspace) return VDN_ERR_NULL_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_soft) ||
-      !text_aligned(text_k, text_v))
+      !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
     return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(launch_softmax(q, k, v, text_k, text_v, *layout, eff_scale(*layout), o_soft,
-                                   stream));
+                                   workspace, stream));
 }
 
 vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
@@ -176,7 +184,8 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
   hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
   if (e == hipSuccess) e = launch_factor(A, l, false, stream);
   if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
-  if (e == hipSuccess) e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, stream);
+  if (e == hipSuccess)
+    e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
   if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
   return hip_status(e);
 }

@@ -168,24 +168,32 @@ __device__ __forceinline__ WorkItem decode_work_xcd(const Geo& g, int B, int H, 
   return w;
 }
 
-template <int D>
+template <int D, bool VTM>
 __global__ void __launch_bounds__(256, 2)
 softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, const bf16* __restrict__ tk,
-                    const bf16* __restrict__ tv, bf16* __restrict__ o, Geo g, int B, int H,
-                    int tpf, float c) {
+                    const bf16* __restrict__ tv, const bf16* __restrict__ vtg, int nl8,
+                    bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c) {
   constexpr int BM = 128, BN = 64;
   constexpr int KCH = D / 8;                         // 16-byte data chunks per row
   // LDS rows are padded (no XOR swizzle): with 64 banks, 16 consecutive K rows
-  // read at one 16-byte column and 4 consecutive V rows x 64 bytes read by
-  // ds_read_b64_tr_b16 both fall on distinct banks, and every read address is
-  // a per-lane base plus a compile-time offset.
+  // read at one 16-byte column by ds_read_b128 fall on distinct banks, and
+  // every read address is a per-lane base plus a compile-time offset.
+  // V, natural layout (VTM = false): rows of one key, read transposed with
+  // ds_read_b64_tr_b16 (4 rows x 64 bytes per half-wave hit distinct banks).
+  // V^T layout (VTM = true, from the transposed copy): rows of one d, 64 keys
+  // each, padded to 144 bytes, read with ds_read_b128 (about 3x the LDS
+  // throughput of the transposed read on gfx950).
   constexpr int KST = 2 * D + 16;                    // K row stride, bytes
-  constexpr int VST = D == 32 ? 64 : 2 * D + 64;     // V row stride, bytes
+  constexpr int VST = VTM ? 144 : (D == 32 ? 64 : 2 * D + 64);   // V row stride, bytes
+  constexpr int VROWS = VTM ? D : BN;
   constexpr int KSL = KST / 16, VSL = VST / 16;      // 16-byte slots per row
-  constexpr int KT = BN * KST, VT = BN * VST;
+  constexpr int KT = BN * KST;
+  constexpr int VSLOTS = VROWS * VSL;                // slots holding data or padding
+  constexpr int VBLK = (VSLOTS + 63) / 64;           // 1 KB DMA blocks per V tile
+  constexpr int VT = VBLK * 1024;
   constexpr int BUFB = KT + VT;                      // one K+V buffer
-  constexpr int NIK = (KSL + 3) / 4, NIV = (VSL + 3) / 4;   // DMA instructions per wave
+  constexpr int NIK = (KSL + 3) / 4, NIV = (VBLK + 3) / 4;  // DMA instructions per wave
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB];
   char VDN_LDS* lds = (char VDN_LDS*)smem;
 
@@ -226,9 +234,17 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
     const int j = (i * 4 + wv) * 64 + lane;
-    vrow[i] = j / VSL;
-    vch[i] = imin(j % VSL, KCH - 1) * 8;
+    if constexpr (VTM) {
+      // V^T slot: d row j / 9, 8-key chunk j % 9 (chunk 8 is padding)
+      const bool pad = j >= VSLOTS;
+      vrow[i] = pad ? 0 : j / VSL;
+      vch[i] = pad ? 0 : imin(j % VSL, BN / 8 - 1) * 8;
+    } else {
+      vrow[i] = j / VSL;
+      vch[i] = imin(j % VSL, KCH - 1) * 8;
+    }
   }
+  const bf16* vtbh = VTM ? vtg + ((size_t)w.b * H + w.h) * D * (size_t)nl8 : nullptr;
 
   auto seg_of = [=](int kv) {
     return (kv >= ka.e0) + (kv >= ka.e1) + (kv >= ka.e2) + (kv >= ka.nkeys);
@@ -242,13 +258,22 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int d = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
       const size_t tok0 = (size_t)(kb0 + d) * HD;
       const bf16* kb = (txt ? tkbh : kbh) + tok0;
-      const bf16* vb = (txt ? tvbh : vbh) + tok0;
 #pragma unroll
       for (int i = 0; i < NIK; ++i)
         if (i * 4 + wv < KSL) g2lds16(kb + (krow[i] * HD + kch[i]), kt + (i * 4 + wv) * 1024);
+      if constexpr (VTM) {
+        // V^T row d holds video tokens then text tokens: text token x sits
+        // at column N + x
+        const bf16* vb = vtbh + (kb0 + (txt ? N - ka.e2 : d));
 #pragma unroll
-      for (int i = 0; i < NIV; ++i)
-        if (i * 4 + wv < VSL) g2lds16(vb + (vrow[i] * HD + vch[i]), vt + (i * 4 + wv) * 1024);
+        for (int i = 0; i < NIV; ++i)
+          if (i * 4 + wv < VBLK) g2lds16(vb + (vrow[i] * nl8 + vch[i]), vt + (i * 4 + wv) * 1024);
+      } else {
+        const bf16* vb = (txt ? tvbh : vbh) + tok0;
+#pragma unroll
+        for (int i = 0; i < NIV; ++i)
+          if (i * 4 + wv < VBLK) g2lds16(vb + (vrow[i] * HD + vch[i]), vt + (i * 4 + wv) * 1024);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < NIK; ++i) {
@@ -260,11 +285,18 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
 #pragma unroll
       for (int i = 0; i < NIV; ++i) {
-        if (i * 4 + wv >= VSL) continue;
-        const int r = key_row(ka, kb0 + vrow[i]);
-        const bool txt = (r & 0x40000000) != 0;
-        const size_t off = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + vch[i];
-        g2lds16((txt ? tvbh : vbh) + off, vt + (i * 4 + wv) * 1024);
+        if (i * 4 + wv >= VBLK) continue;
+        if constexpr (VTM) {
+          // 8-key chunk: all 8 keys lie in one segment (P and L are multiples of 8)
+          const int r = key_row(ka, kb0 + vch[i]);
+          const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
+          g2lds16(vtbh + ((size_t)vrow[i] * nl8 + tok), vt + (i * 4 + wv) * 1024);
+        } else {
+          const int r = key_row(ka, kb0 + vrow[i]);
+          const bool txt = (r & 0x40000000) != 0;
+          const size_t off = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + vch[i];
+          g2lds16((txt ? tvbh : vbh) + off, vt + (i * 4 + wv) * 1024);
+        }
       }
     }
   };
@@ -275,7 +307,9 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // columns 16*(g%2) + 4*(s%4) .. +3 of the 16-key step.
   const int kread = perm32(lane & 31) * KST + half * 16;
   const int gq = lane >> 4, sq = lane & 15;
-  const int vread = (8 * (gq >> 1) + (sq >> 2)) * VST + (16 * (gq & 1) + 4 * (sq & 3)) * 2;
+  // V^T: lane reads row d = l%32 (+32 db), keys 16 sp + 8 half .. +7
+  const int vread = VTM ? (lane & 31) * VST + half * 16
+                        : (8 * (gq >> 1) + (sq >> 2)) * VST + (16 * (gq & 1) + 4 * (sq & 3)) * 2;
 
   float m_run = -1e30f, l_run = 0.f;
   f32x16 oacc[D / 32];
@@ -351,10 +385,15 @@ softmax_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int sp = 0; sp < 4; ++sp)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const char VDN_LDS* pv = vt + sp * 16 * VST + db * 64;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)pv);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)(pv + 4 * VST));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8 a;
+        if constexpr (VTM) {
+          a = *(const bf16x8 VDN_LDS*)(vt + db * 32 * VST + sp * 32);
+        } else {
+          const char VDN_LDS* pv = vt + sp * 16 * VST + db * 64;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)pv);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VDN_LDS*)(pv + 4 * VST));
+          a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         oacc[db] = mfma32(a, pk[sp], oacc[db]);
       }
   };
@@ -466,30 +505,288 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
   return hipGetLastError();
 }
 
+// Softmax kernel for the V^T path (P and L multiples of 8).
+//  * 8 waves x 32 queries = 256 query rows per workgroup, one workgroup per
+//    CU (two waves per SIMD): every K / V^T tile in LDS feeds 256 queries.
+//  * 64-key tiles in a 3-deep LDS ring; the DMA for tile i+2 is issued while
+//    tile i is processed (two tiles of lead time against L2/HBM latency).
+//    Every wave issues exactly NIW DMA instructions per tile (dummies
+//    included), so "tile i+1 landed" is s_waitcnt vmcnt(NIW).
+//  * All K fragments of a tile are read from LDS before its score MFMAs and
+//    all V^T fragments before the softmax VALU work, so LDS latency overlaps
+//    MFMA / VALU work instead of stalling each MFMA pair.
+//  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
+//    both read with ds_read_b128 at base + immediate, conflict-free.
+template <int D>
+__global__ void __launch_bounds__(512)
+softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                  const bf16* __restrict__ tk, const bf16* __restrict__ vtg, int nl8,
+                  bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c) {
+  constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 3;
+  constexpr int KCH = D / 8;
+  constexpr int KST = 2 * D + 16, KSL = KST / 16;    // K row stride (bytes), slots
+  constexpr int VST = 144, VSL = 9;                  // V^T row: 64 keys + pad
+  constexpr int KBLK = (BN * KSL + 63) / 64;         // 1 KB DMA blocks of the K tile
+  constexpr int VBLK = (D * VSL + 63) / 64;          // ... of the V^T tile
+  constexpr int NBLK = KBLK + VBLK;
+  constexpr int NIW = (NBLK + NW - 1) / NW;          // DMA instructions per wave per tile
+  constexpr int VOFF = KBLK * 1024;
+  constexpr int BUFB = (NBLK + 1) * 1024;            // + one dummy block
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB];
+  char VDN_LDS* lds = (char VDN_LDS*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int N = g.T * g.P;
+  const WorkItem w = decode_work_xcd(g, B, H, tpf);
+  const KeyMap km = key_map(g, w.t);
+  const KeyAddr ka = key_addr(km);
+
+  const int qlocal = w.tile * BM + wv * 32 + (lane & 31);
+  const bool qvalid = qlocal < g.P;
+  const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
+  const size_t qoff = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * D;
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+
+  const int HD = H * D;
+  const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
+  const bf16* tkbh = tk + ((size_t)w.b * g.L * H + w.h) * D;
+  const bf16* vtbh = vtg + ((size_t)w.b * H + w.h) * D * (size_t)nl8;
+
+  // DMA instruction i of this wave moves block blk = NW*i + wv (K, V^T or
+  // dummy; wave-uniform).  off[i]: element offset of this lane's chunk from
+  // the tile's first token (single-segment fast path).
+  int off[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int blk = i * NW + wv;
+    if (blk < KBLK) {
+      const int j = blk * 64 + lane;
+      off[i] = imin(j / KSL, BN - 1) * HD + imin(j % KSL, KCH - 1) * 8;
+    } else if (blk < NBLK) {
+      const int j = (blk - KBLK) * 64 + lane;
+      off[i] = imin(j / VSL, D - 1) * nl8 + imin(j % VSL, BN / 8 - 1) * 8;
+    } else {
+      off[i] = 0;
+    }
+  }
+  auto seg_of = [=](int kv) {
+    return (kv >= ka.e0) + (kv >= ka.e1) + (kv >= ka.e2) + (kv >= ka.nkeys);
+  };
+  const int ntiles = (km.nkeys + BN - 1) / BN;
+  auto issue = [=](int tile, int buf) {
+    char VDN_LDS* bb = lds + buf * BUFB;
+    const int kb0 = imin(tile, ntiles - 1) * BN;   // tiles past the end reload the last one
+    const int s0 = seg_of(kb0), s1 = seg_of(kb0 + BN - 1);
+    if (s0 == s1 && s0 < 4) {
+      const bool txt = s0 == 3;
+      const int dl = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
+      const bf16* kbase = (txt ? tkbh : kbh) + (size_t)(kb0 + dl) * HD;
+      const bf16* vbase = vtbh + (kb0 + (txt ? N - ka.e2 : dl));
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const int blk = i * NW + wv;
+        if (blk < KBLK) g2lds16(kbase + off[i], bb + blk * 1024);
+        else if (blk < NBLK) g2lds16(vbase + off[i], bb + blk * 1024);
+        else g2lds16(vtbh, bb + NBLK * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const int blk = i * NW + wv;
+        if (blk < KBLK) {
+          const int j = blk * 64 + lane;
+          const int r = key_row(ka, kb0 + imin(j / KSL, BN - 1));
+          const bool txt = (r & 0x40000000) != 0;
+          const size_t eo = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + imin(j % KSL, KCH - 1) * 8;
+          g2lds16((txt ? tkbh : kbh) + eo, bb + blk * 1024);
+        } else if (blk < NBLK) {
+          const int j = (blk - KBLK) * 64 + lane;
+          const int d = imin(j / VSL, D - 1);
+          const int r = key_row(ka, kb0 + imin(j % VSL, BN / 8 - 1) * 8);   // 8 keys, one segment
+          const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
+          g2lds16(vtbh + ((size_t)d * nl8 + tok), bb + blk * 1024);
+        } else {
+          g2lds16(vtbh, bb + NBLK * 1024);
+        }
+      }
+    }
+  };
+
+  const int kread = perm32(lane & 31) * KST + half * 16;
+  const int vread = VOFF + (lane & 31) * VST + half * 16;
+  const bool partial = (km.nkeys & (BN - 1)) != 0;
+
+  float m_run = -1e30f, l_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it % NBUF;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");   // tile it landed
+    __syncthreads();                                           // ... for all waves; tile it-1 done
+    issue(it + 2, (it + 2) % NBUF);
+
+    // scores S^T = K Q^T: all K fragments first, then the MFMAs
+    const char VDN_LDS* kt = lds + buf * BUFB + kread;
+    bf16x8 kf[2][D / 16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kf[kb][ks] = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ks], qreg[ks], s[kb]);
+    // V^T fragments for P V, read while the softmax runs on the VALU
+    const char VDN_LDS* vt = lds + buf * BUFB + vread;
+    bf16x8 vf[4][D / 32];
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) vf[sp][db] = *(const bf16x8 VDN_LDS*)(vt + db * 32 * VST + sp * 32);
+
+    if (partial && it == ntiles - 1) {
+      const int base = it * BN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (base + kb * 32 + ((j >> 3) << 4) + half * 8 + (j & 7) >= km.nkeys) s[kb][j] = -INFINITY;
+    }
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
+    mx = xhalf_max(mx);
+    // Lazy rescale: the exponent offset moves only when some query's max
+    // grows by more than 2^8 (exp2 units); until then p <= 256.
+    if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2((m_run - m_new) * c);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    bf16x8 pk[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(s[kb][j], c, -mc));
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      const bf16x2* p2 = (const bf16x2*)&pk[sp];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l_run = __builtin_amdgcn_fdot2_f32_bf16(p2[e], ones2, l_run, false);
+    }
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(vf[sp][db], pk[sp], oacc[db]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const float inv = 1.0f / xhalf_sum(l_run);
+  if (qvalid) {
+    bf16* orow = o + qoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = db * 32 + jj * 8 + half * 4;
+        bf16x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[db][jj * 4 + e] * inv);
+        *(bf16x4*)(orow + d) = val;
+      }
+  }
+}
+
+// V^T copy for the softmax: vt[b][h][d][x] = value d of token x, with the
+// T*P video tokens first, then the L text tokens, then zeros up to nl8 (a
+// multiple of 8).  One workgroup per (b, h, 64 tokens), staged through LDS.
+template <int D>
+__global__ void __launch_bounds__(256)
+vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
+                    bf16* __restrict__ vt, int N, int L, int H, int nl8, int ntile) {
+  constexpr int LDR = D + 2;                 // row stride (elements)
+  __shared__ bf16 sm[64 * LDR];
+  const int tile = blockIdx.x % ntile;
+  const int bh = blockIdx.x / ntile;
+  const int b = bh / H, h = bh % H;
+  const int x0 = tile * 64;
+  for (int i = threadIdx.x; i < 64 * (D / 8); i += 256) {
+    const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
+    const int x = x0 + r;
+    bf16x8 val = {};
+    if (x < N) val = *(const bf16x8*)(v + (((size_t)b * N + x) * H + h) * D + c8);
+    else if (x < N + L) val = *(const bf16x8*)(tv + (((size_t)b * L + (x - N)) * H + h) * D + c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm[r * LDR + c8 + e] = val[e];
+  }
+  __syncthreads();
+  bf16* dst = vt + (size_t)bh * D * nl8;
+  for (int i = threadIdx.x; i < D * 8; i += 256) {
+    const int d = i / 8, c = i % 8;
+    const int x = x0 + c * 8;
+    if (x >= nl8) continue;
+    bf16x8 val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] = sm[(c * 8 + e) * LDR + d];
+    *(bf16x8*)(dst + (size_t)d * nl8 + x) = val;
+  }
+}
+
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
-                       const void* tv, const vdn_layout_t& l, float scale, void* o,
+                       const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
                        hipStream_t s) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
-  softmax_mfma_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
-      (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
-      (bf16*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
+  if (softmax_uses_vt(l)) {
+    const int tpf2 = (g.P + 255) / 256;
+    const long grid2 = (long)l.batch * l.heads * g.T * tpf2;
+    const int N = g.T * g.P;
+    const int nl8 = (N + g.L + 7) / 8 * 8;
+    const int ntile = (nl8 + 63) / 64;
+    vt_transpose_kernel<D><<<dim3((unsigned)(l.batch * l.heads * ntile)), dim3(256), 0, s>>>(
+        (const bf16*)v, (const bf16*)tv, (bf16*)ws, N, g.L, l.heads, nl8, ntile);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    softmax_vt_kernel<D><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+        l.batch, l.heads, tpf2, scale * kLog2e);
+  } else {
+    softmax_mfma_kernel<D, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
+        nullptr, 0, (bf16*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_softmax(const void* q, const void* k, const void* v, const void* tk,
-                          const void* tv, const vdn_layout_t& l, float scale, void* o,
+                          const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
                           hipStream_t s) {
   const int d = l.head_dim_k;
   if (l.dtype == VDN_BF16) {
     switch (d) {
-      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, s);
-      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, s);
-      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, s);
+      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, s);
+      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, s);
+      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, s);
       case 16: return launch_valu<bf16, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
   } else {

@@ -127,10 +127,24 @@ __host__ __device__ inline int count_slots(const Geo& g, bool all_frames) {
 
 // Workspace plan (bytes, each region 256-byte aligned).
 struct Plan {
-  size_t a_off, b_off, sf_off, sb_off, r_off, total;
+  size_t a_off, b_off, sf_off, sb_off, r_off, vt_off, total;
 };
 
 __host__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The bf16 MFMA softmax reads V from a transposed copy (V^T, video then text
+// tokens per row) when every 8-key chunk of its key sequence lies inside one
+// segment, i.e. when P and L are multiples of 8.
+__host__ __device__ inline bool softmax_uses_vt(const vdn_layout_t& l) {
+  return l.dtype == VDN_BF16 && l.head_dim_k >= 32 && l.tokens_per_frame % 8 == 0 &&
+         l.text_tokens % 8 == 0;
+}
+
+__host__ inline size_t softmax_ws_bytes(const vdn_layout_t& l) {
+  if (!softmax_uses_vt(l)) return 0;
+  size_t nl8 = ((size_t)l.frames * l.tokens_per_frame + l.text_tokens + 7) / 8 * 8;
+  return align256((size_t)l.batch * l.heads * l.head_dim_k * nl8 * 2);
+}
 
 __host__ inline Plan make_plan(const vdn_layout_t& l) {
   Geo g = make_geo(l);
@@ -145,7 +159,8 @@ __host__ inline Plan make_plan(const vdn_layout_t& l) {
   p.sf_off = align256(p.b_off + stats);
   p.sb_off = align256(p.sf_off + snaps);
   p.r_off = align256(p.sb_off + snaps);
-  p.total = align256(p.r_off + snaps);
+  p.vt_off = align256(p.r_off + snaps);
+  p.total = align256(p.vt_off + softmax_ws_bytes(l));
   return p;
 }
 
@@ -161,7 +176,7 @@ __host__ inline size_t scan_ws_bytes(const vdn_layout_t& l) {
 // launch.  Pointers are device pointers; shapes were validated by the caller.
 // ---------------------------------------------------------------------------
 hipError_t launch_softmax(const void* q, const void* k, const void* v, const void* tk,
-                          const void* tv, const vdn_layout_t& l, float scale, void* o,
+                          const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
                           hipStream_t s);
 hipError_t launch_gram(const void* k, const void* v, const void* tk, const void* tv,
                        const float* beta, const vdn_layout_t& l, bool all_frames, float* A,

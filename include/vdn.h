@@ -141,6 +141,21 @@ vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Softmax branch and merge in one pass (the layer's last stage):
+ *   o = sigmoid(g0) * O_soft + sigmoid(g1) * RMSNorm(R[c] q)
+ * with O_soft as in vdn_softmax_fwd (kept in float32, not rounded, before
+ * the merge) and R from vdn_vda_factor_scan (slot nc for anchor frames).
+ * Covers bf16 layouts with d in {32, 64, 128} and P, L multiples of 8;
+ * returns VDN_ERR_UNSUPPORTED otherwise (vdn_softmax_fwd + vdn_merge cover
+ * every layout).  workspace: as for vdn_softmax_fwd.  o must not alias any
+ * input.  [PaperDaily §二, §三; arXiv abstract] */
+vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
+                                   const void* text_k, const void* text_v,
+                                   const float* R, const float* gate_logits,
+                                   const vdn_layout_t* layout, void* o,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Frame statistics: for every frame f < T and for the text block (slot T),
  * A[b,h,slot] = sum_i beta_i k_i k_i^T and B[b,h,slot] = sum_i beta_i v_i k_i^T
  * over the slot's tokens.  A_out, B_out: float32 [B, H, T+1, d, d] (row index

@@ -109,6 +109,16 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.vdn_vda_gram(ok, ok, nul, nul, odd, ref, ok, ok, nul) == 4
     assert lib.vdn_vda_factor_scan(ok, ok, ok, ref, ok, ok, 0, nul) == 5
     assert lib.vdn_merge(ok, ok, ok, ok, ref, nul, nul) == 1
+    # fused softmax + merge: only the bf16 V^T layouts; then argument checks
+    sm = [ok, ok, ok, nul, nul, ok, ok, ctypes.byref(lay_vt), ok, ok, 1 << 40, nul]
+    a = list(sm); a[7] = ref                             # f32 d=16: not covered
+    assert lib.vdn_softmax_merge_fwd(*a) == 3
+    a = list(sm); a[5] = nul
+    assert lib.vdn_softmax_merge_fwd(*a) == 1
+    a = list(sm); a[6] = odd
+    assert lib.vdn_softmax_merge_fwd(*a) == 4
+    a = list(sm); a[10] = 16
+    assert lib.vdn_softmax_merge_fwd(*a) == 5
 
 
 @pytest.fixture(scope="module")

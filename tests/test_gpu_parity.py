@@ -255,21 +255,11 @@ def test_stage_softmax(name):
     assert err <= (1e-5 if w.dtype == "f32" else 1e-2)
 
 
-@pytest.mark.parametrize("name", STAGE_CASES)
-def test_stage_merge(name):
-    """Merge given the oracle's states (as fp32) and softmax output (rounded
-    to the tensor dtype): isolates read + RMSNorm + gates."""
-    require_gpu()
-    w = workload(name)
-    _announce(f"merge {name}")
-    inp = synth.make_inputs(w)
-    lay = oracle_layout(w)
+def _oracle_states(inp, lay, w):
+    """R [B, H, nc+1, d, d] float32 from the oracle's per-frame states: slot c
+    holds what a non-anchor frame of chunk c reads, slot nc the text write."""
     nc = lay.num_chunks
     d = w.head_dim
-    o_soft = O.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
-    o_soft = o_soft.astype(np.float32)
-    if w.dtype == "bf16":
-        o_soft = synth.round_bf16(o_soft)
     R = np.zeros((w.batch, w.heads, nc + 1, d, d), np.float32)
     for b in range(w.batch):
         for h in range(w.heads):
@@ -278,7 +268,12 @@ def test_stage_merge(name):
             for c in range(nc):
                 R[b, h, c] = per_frame[min(c * lay.chunk_frames + 1, w.frames - 1)]
             R[b, h, nc] = per_frame[0]            # anchor frame 0 reads the text write
-    # reference: merge with exactly these R and o_soft
+    return R
+
+
+def _oracle_merge(inp, lay, w, o_soft, R):
+    """Merge with exactly these R and o_soft, in float64."""
+    nc = lay.num_chunks
     ref = np.zeros(inp["q"].shape)
     P = w.tokens_per_frame
     for t in range(w.frames):
@@ -290,6 +285,24 @@ def test_stage_merge(name):
                 n = O.rms_norm(o_lin, lay.rms_eps)
                 ref[b, rows, h] = O.merge(o_soft[b, rows, h].astype(np.float64), n,
                                           inp["gate_logits"][b, rows, h])
+    return ref
+
+
+@pytest.mark.parametrize("name", STAGE_CASES)
+def test_stage_merge(name):
+    """Merge given the oracle's states (as fp32) and softmax output (rounded
+    to the tensor dtype): isolates read + RMSNorm + gates."""
+    require_gpu()
+    w = workload(name)
+    _announce(f"merge {name}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    o_soft = O.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
+    o_soft = o_soft.astype(np.float32)
+    if w.dtype == "bf16":
+        o_soft = synth.round_bf16(o_soft)
+    R = _oracle_states(inp, lay, w)
+    ref = _oracle_merge(inp, lay, w, o_soft, R)
     dev = to_dev(inp, w.dtype)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     os_dev = torch.from_numpy(o_soft).to(tdt).cuda()
@@ -299,6 +312,44 @@ def test_stage_merge(name):
     err = rel_err(out.float().cpu().numpy(), ref)
     print(f"{name}: merge rel err {err:.3e}")
     assert err <= (1e-5 if w.dtype == "f32" else 1e-2)
+
+
+FUSED_CASES = [
+    dict(name="fused_d64", batch=1, heads=8, head_dim=64, frames=30, tokens_per_frame=112,
+         text_tokens=64, dtype="bf16", chunk_frames=5),
+    # several 256-query tiles per frame with a ragged last one, two chunks of 3
+    dict(name="fused_d128", batch=1, heads=2, head_dim=128, frames=7, tokens_per_frame=600,
+         text_tokens=24, dtype="bf16", chunk_frames=3),
+    dict(name="fused_d32_b2", batch=2, heads=3, head_dim=32, frames=6, tokens_per_frame=40,
+         text_tokens=0, dtype="bf16", chunk_frames=2),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c["name"] for c in FUSED_CASES])
+def test_stage_softmax_merge(case):
+    """Fused softmax + merge given the oracle's states: the softmax output
+    enters the merge unrounded, so the float64 reference merges the float64
+    softmax; bf16 P and output rounding bound the error (1e-2)."""
+    require_gpu()
+    w = custom(**case)
+    _announce(f"softmax+merge {case['name']}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    o_soft = O.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
+    R = _oracle_states(inp, lay, w)
+    ref = _oracle_merge(inp, lay, w, o_soft, R)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    out = V.softmax_merge_fwd(dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+                              dev["text_v"] if L else None, torch.from_numpy(R).cuda(),
+                              dev["gate_logits"], **geo_kw(w))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    err = rel_err(got, ref)
+    worst = max(rel_err(got[b, :, h], ref[b, :, h]) for b in range(w.batch) for h in range(w.heads))
+    print(f"{case['name']}: softmax+merge rel err {err:.3e}, worst head {worst:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= 1e-2
 
 
 # ---------------------------------------------------------------------------

@@ -16,7 +16,7 @@ __all__ = [
     "VdnError", "Layout", "lib", "library_path", "version", "validate_layout",
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
-    "softmax_fwd", "vda_gram", "vda_factor_scan", "merge", "make_layout",
+    "softmax_fwd", "softmax_merge_fwd", "vda_gram", "vda_factor_scan", "merge", "make_layout",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +29,8 @@ _STATUS = {
 EXPORTED_SYMBOLS = (
     "vdn_version", "vdn_status_str", "vdn_last_hip_error", "vdn_validate_layout",
     "vdn_num_chunks", "vdn_hybrid_attn_workspace_size", "vdn_hybrid_attn_fwd",
-    "vdn_softmax_workspace_size", "vdn_softmax_fwd", "vdn_vda_gram", "vdn_vda_factor_scan_workspace_size",
+    "vdn_softmax_workspace_size", "vdn_softmax_fwd", "vdn_softmax_merge_fwd", "vdn_vda_gram",
+    "vdn_vda_factor_scan_workspace_size",
     "vdn_vda_factor_scan", "vdn_merge",
 )
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_softmax_workspace_size.argtypes = [lp]
         L.vdn_softmax_fwd.restype = ctypes.c_int
         L.vdn_softmax_fwd.argtypes = [vp, vp, vp, vp, vp, lp, vp, vp, sz, vp]
+        L.vdn_softmax_merge_fwd.restype = ctypes.c_int
+        L.vdn_softmax_merge_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, vp, vp, sz, vp]
         L.vdn_vda_gram.restype = ctypes.c_int
         L.vdn_vda_gram.argtypes = [vp, vp, vp, vp, vp, lp, vp, vp, vp]
         L.vdn_vda_factor_scan.restype = ctypes.c_int
@@ -231,6 +234,33 @@ def softmax_fwd(q, k, v, text_k, text_v, *, frames, tokens_per_frame, chunk_fram
     _check(lib().vdn_softmax_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
                                  _ptr(text_v if L else None), ctypes.byref(lay), _ptr(out),
                                  _ptr(workspace), nbytes, _stream()), "vdn_softmax_fwd")
+    return out
+
+
+def softmax_merge_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tokens_per_frame,
+                      chunk_frames=5, window_chunks=1, anchor_first=True, anchor_last=True,
+                      softmax_scale=0.0, rms_eps=0.0, out=None, workspace=None) -> torch.Tensor:
+    """Softmax branch with the merge fused in (``vdn_softmax_merge_fwd``)."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    _expect(R, (B, H, num_chunks(lay) + 1, d, d), torch.float32, "R")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    L = lay.text_tokens
+    need = softmax_workspace_size(lay)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vdn_softmax_merge_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
+                                       _ptr(text_v if L else None), _ptr(R), _ptr(gate_logits),
+                                       ctypes.byref(lay), _ptr(out), _ptr(workspace), nbytes,
+                                       _stream()), "vdn_softmax_merge_fwd")
     return out
 
 

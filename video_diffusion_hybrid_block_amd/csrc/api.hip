@@ -115,6 +115,26 @@ vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v, const 
                                    workspace, stream));
 }
 
+vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
+                                   const void* text_k, const void* text_v, const float* R,
+                                   const float* gate_logits, const vdn_layout_t* layout, void* o,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!softmax_merge_fusable(*layout)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !R || !gate_logits || !o || !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  const size_t need = softmax_ws_bytes(*layout);
+  if (need > 0 && !workspace) return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(R) || !aligned16(gate_logits) ||
+      !aligned16(o) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
+                                         eff_scale(*layout), eff_eps(*layout), o, workspace,
+                                         stream));
+}
+
 vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
                           const float* beta, const vdn_layout_t* layout, float* A_out,
                           float* B_out, hipStream_t stream) {
@@ -184,8 +204,11 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
   hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
   if (e == hipSuccess) e = launch_factor(A, l, false, stream);
   if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
-  if (e == hipSuccess)
-    e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (softmax_merge_fusable(l))
+    return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                           eff_eps(l), o, ws + p.vt_off, stream));
+  e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
   if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
   return hip_status(e);
 }

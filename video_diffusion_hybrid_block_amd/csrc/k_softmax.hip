@@ -509,19 +509,19 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //  * 8 waves x 32 queries = 256 query rows per workgroup, one workgroup per
 //    CU (two waves per SIMD): every K / V^T tile in LDS feeds 256 queries.
 //  * 64-key tiles in a 3-deep LDS ring; the DMA for tile i+2 is issued while
-//    tile i is processed (two tiles of lead time against L2/HBM latency).
-//    Every wave issues exactly NIW DMA instructions per tile (dummies
-//    included), so "tile i+1 landed" is s_waitcnt vmcnt(NIW).
+//    tile i is processed.  Every wave issues exactly NIW DMA instructions per
+//    tile (dummies included), so "tile i+1 landed" is s_waitcnt vmcnt(NIW).
 //  * All K fragments of a tile are read from LDS before its score MFMAs and
 //    all V^T fragments before the softmax VALU work, so LDS latency overlaps
 //    MFMA / VALU work instead of stalling each MFMA pair.
 //  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
 //    both read with ds_read_b128 at base + immediate, conflict-free.
-template <int D>
+template <int D, bool FUSE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                   const bf16* __restrict__ tk, const bf16* __restrict__ vtg, int nl8,
-                  bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c) {
+                  bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c,
+                  const float* __restrict__ R, const float* __restrict__ gates, float eps) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 3;
   constexpr int KCH = D / 8;
   constexpr int KST = 2 * D + 16, KSL = KST / 16;    // K row stride (bytes), slots
@@ -529,7 +529,9 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int KBLK = (BN * KSL + 63) / 64;         // 1 KB DMA blocks of the K tile
   constexpr int VBLK = (D * VSL + 63) / 64;          // ... of the V^T tile
   constexpr int NBLK = KBLK + VBLK;
-  constexpr int NIW = (NBLK + NW - 1) / NW;          // DMA instructions per wave per tile
+  constexpr int NWH = NW / 2;                        // waves per half (K half, V^T half)
+  constexpr int NIK = (KBLK + NWH - 1) / NWH, NIV = (VBLK + NWH - 1) / NWH;
+  constexpr int NIW = NIK > NIV ? NIK : NIV;         // DMA instructions per wave per tile
   constexpr int VOFF = KBLK * 1024;
   constexpr int BUFB = (NBLK + 1) * 1024;            // + one dummy block
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB];
@@ -539,9 +541,15 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
   const int N = g.T * g.P;
-  const WorkItem w = decode_work_xcd(g, B, H, tpf);
+  WorkItem w = decode_work_xcd(g, B, H, tpf);
+  w.b = sgpr(w.b); w.h = sgpr(w.h); w.t = sgpr(w.t); w.tile = sgpr(w.tile);
   const KeyMap km = key_map(g, w.t);
-  const KeyAddr ka = key_addr(km);
+  // Segment bounds are workgroup-uniform: keep them in SGPRs so the per-tile
+  // address logic runs on the scalar unit.
+  KeyAddr ka = key_addr(km);
+  ka.e0 = sgpr(ka.e0); ka.e1 = sgpr(ka.e1); ka.e2 = sgpr(ka.e2); ka.nkeys = sgpr(ka.nkeys);
+  ka.d0 = sgpr(ka.d0); ka.d1 = sgpr(ka.d1); ka.d2 = sgpr(ka.d2); ka.clamp_tok = sgpr(ka.clamp_tok);
+  const int nkeys = ka.nkeys;
 
   const int qlocal = w.tile * BM + wv * 32 + (lane & 31);
   const bool qvalid = qlocal < g.P;
@@ -556,27 +564,36 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bf16* tkbh = tk + ((size_t)w.b * g.L * H + w.h) * D;
   const bf16* vtbh = vtg + ((size_t)w.b * H + w.h) * D * (size_t)nl8;
 
-  // DMA instruction i of this wave moves block blk = NW*i + wv (K, V^T or
-  // dummy; wave-uniform).  off[i]: element offset of this lane's chunk from
-  // the tile's first token (single-segment fast path).
-  int off[NIW];
+  // Waves 0..NWH-1 move the K tile and waves NWH.. the V^T tile, so each
+  // wave's DMA base is uniform.  DMA i of a wave fills block NWH*i + (wv %
+  // NWH) of its half; slots past the half's last block reload block 0's chunk
+  // into the spare block.  offb[i]: byte offset of the lane's 16-byte chunk
+  // from the tile's first token (one-segment tiles), 32-bit so the load takes
+  // a scalar base plus a vector offset; ldsb[i]: LDS block (uniform).
+  const bool vwave = wv >= NWH;
+  uint32_t offb[NIW];
+  int ldsb[NIW];
 #pragma unroll
   for (int i = 0; i < NIW; ++i) {
-    const int blk = i * NW + wv;
-    if (blk < KBLK) {
-      const int j = blk * 64 + lane;
-      off[i] = imin(j / KSL, BN - 1) * HD + imin(j % KSL, KCH - 1) * 8;
-    } else if (blk < NBLK) {
-      const int j = (blk - KBLK) * 64 + lane;
-      off[i] = imin(j / VSL, D - 1) * nl8 + imin(j % VSL, BN / 8 - 1) * 8;
+    const int blk = i * NWH + (wv & (NWH - 1));
+    if (!vwave) {
+      const bool ok = blk < KBLK;
+      const int jj = (ok ? blk : 0) * 64 + lane;
+      offb[i] = (uint32_t)(imin(jj / KSL, BN - 1) * HD + imin(jj % KSL, KCH - 1) * 8) * 2u;
+      ldsb[i] = sgpr(ok ? blk * 1024 : NBLK * 1024);
     } else {
-      off[i] = 0;
+      const bool ok = blk < VBLK;
+      const int jj = (ok ? blk : 0) * 64 + lane;
+      offb[i] = (uint32_t)(imin(jj / VSL, D - 1) * nl8 + imin(jj % VSL, BN / 8 - 1) * 8) * 2u;
+      ldsb[i] = sgpr(ok ? VOFF + blk * 1024 : NBLK * 1024);
     }
   }
+  // segment of key kv: number of segment ends <= kv (all values >= 0)
   auto seg_of = [=](int kv) {
-    return (kv >= ka.e0) + (kv >= ka.e1) + (kv >= ka.e2) + (kv >= ka.nkeys);
+    return (int)(((uint32_t)(ka.e0 - 1 - kv) >> 31) + ((uint32_t)(ka.e1 - 1 - kv) >> 31) +
+                 ((uint32_t)(ka.e2 - 1 - kv) >> 31) + ((uint32_t)(ka.nkeys - 1 - kv) >> 31));
   };
-  const int ntiles = (km.nkeys + BN - 1) / BN;
+  const int ntiles = sgpr((nkeys + BN - 1) / BN);
   auto issue = [=](int tile, int buf) {
     char VDN_LDS* bb = lds + buf * BUFB;
     const int kb0 = imin(tile, ntiles - 1) * BN;   // tiles past the end reload the last one
@@ -584,33 +601,26 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (s0 == s1 && s0 < 4) {
       const bool txt = s0 == 3;
       const int dl = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
-      const bf16* kbase = (txt ? tkbh : kbh) + (size_t)(kb0 + dl) * HD;
-      const bf16* vbase = vtbh + (kb0 + (txt ? N - ka.e2 : dl));
+      const char* base = sgpr_ptr(vwave ? (const void*)(vtbh + (kb0 + (txt ? N - ka.e2 : dl)))
+                                        : (const void*)((txt ? tkbh : kbh) + (size_t)(kb0 + dl) * HD));
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) {
-        const int blk = i * NW + wv;
-        if (blk < KBLK) g2lds16(kbase + off[i], bb + blk * 1024);
-        else if (blk < NBLK) g2lds16(vbase + off[i], bb + blk * 1024);
-        else g2lds16(vtbh, bb + NBLK * 1024);
-      }
+      for (int i = 0; i < NIW; ++i) g2lds16(base + offb[i], bb + ldsb[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
-        const int blk = i * NW + wv;
-        if (blk < KBLK) {
-          const int j = blk * 64 + lane;
-          const int r = key_row(ka, kb0 + imin(j / KSL, BN - 1));
+        const int blk = i * NWH + (wv & (NWH - 1));
+        if (!vwave) {
+          const int jj = (blk < KBLK ? blk : 0) * 64 + lane;
+          const int r = key_row(ka, kb0 + imin(jj / KSL, BN - 1));
           const bool txt = (r & 0x40000000) != 0;
-          const size_t eo = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + imin(j % KSL, KCH - 1) * 8;
-          g2lds16((txt ? tkbh : kbh) + eo, bb + blk * 1024);
-        } else if (blk < NBLK) {
-          const int j = (blk - KBLK) * 64 + lane;
-          const int d = imin(j / VSL, D - 1);
-          const int r = key_row(ka, kb0 + imin(j % VSL, BN / 8 - 1) * 8);   // 8 keys, one segment
-          const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
-          g2lds16(vtbh + ((size_t)d * nl8 + tok), bb + blk * 1024);
+          const size_t eo = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + imin(jj % KSL, KCH - 1) * 8;
+          g2lds16((txt ? tkbh : kbh) + eo, bb + ldsb[i]);
         } else {
-          g2lds16(vtbh, bb + NBLK * 1024);
+          const int jj = (blk < VBLK ? blk : 0) * 64 + lane;
+          const int d = imin(jj / VSL, D - 1);
+          const int r = key_row(ka, kb0 + imin(jj % VSL, BN / 8 - 1) * 8);   // 8 keys, one segment
+          const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
+          g2lds16(vtbh + ((size_t)d * nl8 + tok), bb + ldsb[i]);
         }
       }
     }
@@ -618,65 +628,67 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int kread = perm32(lane & 31) * KST + half * 16;
   const int vread = VOFF + (lane & 31) * VST + half * 16;
-  const bool partial = (km.nkeys & (BN - 1)) != 0;
+  const bool partial = (nkeys & (BN - 1)) != 0;
+  const float thr = 8.0f / c;   // lazy-rescale margin in score units
 
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run = -1e30f, m_thr = -1e30f, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  issue(0, 0);
-  issue(1, 1);
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it % NBUF;
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");   // tile it landed
-    __syncthreads();                                           // ... for all waves; tile it-1 done
-    issue(it + 2, (it + 2) % NBUF);
-
-    // scores S^T = K Q^T: all K fragments first, then the MFMAs
+  // S^T = K Q^T for the tile in buffer buf: all K fragments, then the MFMAs.
+  auto scores = [&](int buf, f32x16 (&s)[2]) {
     const char VDN_LDS* kt = lds + buf * BUFB + kread;
     bf16x8 kf[2][D / 16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) kf[kb][ks] = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
-    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ks], qreg[ks], s[kb]);
-    // V^T fragments for P V, read while the softmax runs on the VALU
+  };
+  // Online softmax of tile `it` (scores s, buffer buf) and O^T += V^T P^T.
+  auto soft_pv = [&](int it, int buf, f32x16 (&s)[2]) {
+    // V^T fragments, read while the softmax runs on the VALU
     const char VDN_LDS* vt = lds + buf * BUFB + vread;
     bf16x8 vf[4][D / 32];
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) vf[sp][db] = *(const bf16x8 VDN_LDS*)(vt + db * 32 * VST + sp * 32);
-
     if (partial && it == ntiles - 1) {
-      const int base = it * BN;
+      // keys past the end score -inf (computed here, not hoisted as masks)
+      const int lim = sgpr(nkeys - it * BN) - half * 8;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (base + kb * 32 + ((j >> 3) << 4) + half * 8 + (j & 7) >= km.nkeys) s[kb][j] = -INFINITY;
+          if (kb * 32 + ((j >> 3) << 4) + (j & 7) >= lim) s[kb][j] = -INFINITY;
     }
-    float mx = fmaxf(s[0][0], s[1][0]);
+    // row max: two max3 chains over the 32 scores, then the partner half
+    float ma = max3_raw(s[0][0], s[0][1], s[0][2]), mb = max3_raw(s[1][0], s[1][1], s[1][2]);
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
-    mx = xhalf_max(mx);
+    for (int j = 3; j < 15; j += 2) {
+      ma = max3_raw(ma, s[0][j], s[0][j + 1]);
+      mb = max3_raw(mb, s[1][j], s[1][j + 1]);
+    }
+    float mx = max3_raw(max3_raw(ma, mb, s[0][15]), s[1][15], s[1][15]);
+    mx = xhalf_max_raw(mx);
     // Lazy rescale: the exponent offset moves only when some query's max
     // grows by more than 2^8 (exp2 units); until then p <= 256.
-    if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.0f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float corr = fast_exp2((m_run - m_new) * c);
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
       m_run = m_new;
+      m_thr = m_new + thr;
     }
     const float mc = m_run * c;
     bf16x8 pk[4];
@@ -694,22 +706,113 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int sp = 0; sp < 4; ++sp)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32(vf[sp][db], pk[sp], oacc[db]);
+  };
+
+  // Tile t sits in buffer t % NBUF.  At the top of iteration t, tile t has
+  // landed (own DMAs: vmcnt; everyone's: the barrier) and every wave is done
+  // with tile t-1, whose buffer then receives tile t+2.
+  issue(0, 0);
+  issue(1, 1);
+  f32x16 s[2];
+  for (int it = 0; it < ntiles; ++it) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+    __syncthreads();
+    issue(it + 2, (it + 2) % NBUF);
+    scores(it % NBUF, s);
+    soft_pv(it, it % NBUF, s);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float inv = 1.0f / xhalf_sum(l_run);
-  if (qvalid) {
-    bf16* orow = o + qoff;
+  if constexpr (!FUSE) {
+    if (qvalid) {
+      bf16* orow = o + qoff;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = db * 32 + jj * 8 + half * 4;
-        bf16x4 val;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + jj * 8 + half * 4;
+          bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[db][jj * 4 + e] * inv);
-        *(bf16x4*)(orow + d) = val;
+          for (int e = 0; e < 4; ++e) val[e] = (bf16)(oacc[db][jj * 4 + e] * inv);
+          *(bf16x4*)(orow + d) = val;
+        }
+    }
+  } else {
+    // Merge in registers: o = sigmoid(g0) o_soft + sigmoid(g1) RMSNorm(R q),
+    // R = the summed VDA state this frame reads (slot nc for anchors).
+    // R is staged once per workgroup as bf16 hi + lo rows in the (now idle)
+    // ring memory; o_lin^T = R q^T takes q^T from the score B operand, so it
+    // lands in the same registers layout as O^T.
+    const float* Rs = R + ((size_t)(w.b * H + w.h) * (g.nc + 1) + (is_anchor(g, w.t) ? g.nc : w.t / g.C)) * D * D;
+    char VDN_LDS* rh = lds;
+    char VDN_LDS* rl = lds + D * KST;
+    // all global loads of the epilogue first: gate logits and this thread's
+    // share of R (NR chunks of 8 floats)
+    const float2 gl = *(const float2*)(gates + ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2);
+    constexpr int NR = (D * D / 8 + NW * 64 - 1) / (NW * 64);
+    float4 xr[NR][2];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int i = imin(u * NW * 64 + (int)threadIdx.x, D * D / 8 - 1);
+      xr[u][0] = *(const float4*)(Rs + i * 8);
+      xr[u][1] = *(const float4*)(Rs + i * 8 + 4);
+    }
+    __syncthreads();                       // every wave is done with the ring
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      const int i = u * NW * 64 + threadIdx.x;
+      if (i >= D * D / 8) break;
+      const int r = (i * 8) / D, cc = (i * 8) % D;
+      const float xv[8] = {xr[u][0].x, xr[u][0].y, xr[u][0].z, xr[u][0].w,
+                           xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w};
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hi, lo;
+        split_bf16(xv[e], hi, lo);
+        hv[e] = hi;
+        lv[e] = lo;
       }
+      *(bf16x8 VDN_LDS*)(rh + r * KST + cc * 2) = hv;
+      *(bf16x8 VDN_LDS*)(rl + r * KST + cc * 2) = lv;
+    }
+    __syncthreads();
+    f32x16 lin[D / 32];
+#pragma unroll
+    for (int rb = 0; rb < D / 32; ++rb) {
+      lin[rb] = f32x16{};
+      const int ro = (rb * 32 + (lane & 31)) * KST + half * 16;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 ah = *(const bf16x8 VDN_LDS*)(rh + ro + ks * 32);
+        const bf16x8 al = *(const bf16x8 VDN_LDS*)(rl + ro + ks * 32);
+        lin[rb] = mfma32(ah, qreg[ks], lin[rb]);
+        lin[rb] = mfma32(al, qreg[ks], lin[rb]);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < D / 32; ++rb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss = fmaf(lin[rb][j], lin[rb][j], ss);
+    ss = xhalf_sum(ss);
+    const float rinv = rsqrtf(ss * (1.0f / D) + eps);
+    const float g0 = sigmoidf(gl.x) * inv, g1 = sigmoidf(gl.y) * rinv;
+    if (qvalid) {
+      bf16* orow = o + qoff;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = db * 32 + jj * 8 + half * 4;
+          bf16x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            val[e] = (bf16)fmaf(g0, oacc[db][jj * 4 + e], g1 * lin[db][jj * 4 + e]);
+          *(bf16x4*)(orow + d) = val;
+        }
+    }
   }
 }
 
@@ -751,7 +854,7 @@ vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
-                       hipStream_t s) {
+                       const float* R, const float* gates, float eps, hipStream_t s) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
@@ -765,10 +868,16 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
         (const bf16*)v, (const bf16*)tv, (bf16*)ws, N, g.L, l.heads, nl8, ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    softmax_vt_kernel<D><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-        l.batch, l.heads, tpf2, scale * kLog2e);
+    if (R)
+      softmax_vt_kernel<D, true><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps);
+    else
+      softmax_vt_kernel<D, false><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f);
   } else {
+    if (R) return hipErrorNotSupported;
     softmax_mfma_kernel<D, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
         nullptr, 0, (bf16*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
@@ -784,9 +893,9 @@ hipError_t launch_softmax(const void* q, const void* k, const void* v, const voi
   const int d = l.head_dim_k;
   if (l.dtype == VDN_BF16) {
     switch (d) {
-      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, s);
-      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, s);
-      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, s);
+      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
+      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
+      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
       case 16: return launch_valu<bf16, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
   } else {
@@ -796,6 +905,23 @@ hipError_t launch_softmax(const void* q, const void* k, const void* v, const voi
       case 32: return launch_valu<float, 32>(q, k, v, tk, tv, l, scale, o, s);
       case 16: return launch_valu<float, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+bool softmax_merge_fusable(const vdn_layout_t& l) {
+  return softmax_uses_vt(l) && l.head_dim_k >= 32;
+}
+
+hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
+                                const void* tv, const float* R, const float* gates,
+                                const vdn_layout_t& l, float scale, float eps, void* o, void* ws,
+                                hipStream_t s) {
+  if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
+  switch (l.head_dim_k) {
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
   }
   return hipErrorInvalidValue;
 }

@@ -51,6 +51,32 @@ __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
 }
 
 // Exchange with lane l^32: returns max / sum of the value and its partner's.
+// v_max3_f32 / v_max_f32 without the NaN-quieting copies the compiler adds
+// to fmaxf on MFMA results (scores are finite or -inf).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float xhalf_max_raw(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int sgpr(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// A wave-uniform pointer, pinned to SGPRs (lets loads use scalar base +
+// 32-bit vector offset addressing).
+__device__ __forceinline__ const char* sgpr_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float xhalf_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -139,7 +139,6 @@ __host__ __device__ inline bool softmax_uses_vt(const vdn_layout_t& l) {
   return l.dtype == VDN_BF16 && l.head_dim_k >= 32 && l.tokens_per_frame % 8 == 0 &&
          l.text_tokens % 8 == 0;
 }
-
 __host__ inline size_t softmax_ws_bytes(const vdn_layout_t& l) {
   if (!softmax_uses_vt(l)) return 0;
   size_t nl8 = ((size_t)l.frames * l.tokens_per_frame + l.text_tokens + 7) / 8 * 8;
@@ -186,5 +185,12 @@ hipError_t launch_scan(const float* G, const float* B, const float* alpha, const
                        float* Sf, float* Sb, float* R, hipStream_t s);
 hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
                         const vdn_layout_t& l, float eps, void* o, hipStream_t s);
+// Softmax branch with the merge fused into its epilogue (bf16, V^T path only):
+// o = sigmoid(g0) softmax + sigmoid(g1) RMSNorm(R q).
+bool softmax_merge_fusable(const vdn_layout_t& l);
+hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
+                                const void* tv, const float* R, const float* gates,
+                                const vdn_layout_t& l, float scale, float eps, void* o, void* ws,
+                                hipStream_t s);
 
 }  // namespace vdn

@@ -50,8 +50,9 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
   constexpr int NT = 64 * NRB;
   constexpr int LDF = D + 4;            // fp32 state row stride (floats)
-  constexpr int NBV = 32 * D / NT;      // B values per thread per step
-  __shared__ float S[32 * LDF];
+  constexpr int NCH = 32 * D / 8 / NT;  // 8-value chunks of X per thread per step
+  static_assert(NCH >= 1 && NCH * 8 * NT == 32 * D, "X build split");
+  __shared__ __attribute__((aligned(16))) float S[32 * LDF];
   __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
   char VDN_LDS* Xh = (char VDN_LDS*)xh;
@@ -59,8 +60,13 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
-  const int rb = blockIdx.x % NRB;
-  const int chain = blockIdx.x / NRB;
+  // Workgroup i runs on XCD i % 8.  When the grid splits evenly, each XCD
+  // gets whole chains, so the NRB row blocks of a chain (which all read the
+  // same G_f and B_f every step) share one L2.
+  int wid = blockIdx.x;
+  if (gridDim.x % (8 * NRB) == 0) wid = (wid & 7) * (gridDim.x >> 3) + (wid >> 3);
+  const int rb = wid % NRB;
+  const int chain = wid / NRB;
   const int dir = chain & 1;
   const int bh = chain >> 1;
   const int b = bh / H, h = bh % H;
@@ -75,9 +81,10 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
 
   // Per-step operands, prefetched one step ahead: this lane's G row (B
   // operand, G symmetric) and its share of the B rows.
+  // Thread t builds X chunks q = t + i*NT: row q / (D/8), columns 8*(q % (D/8)).
   float4 gcur[D / 8], gnxt[D / 8];
-  float bcur[NBV], bnxt[NBV];
-  auto load = [&](int slot, float4* gr, float* br) {
+  float4 bcur[2 * NCH], bnxt[2 * NCH];
+  auto load = [&](int slot, float4* gr, float4* br) {
     const float4* gp = (const float4*)(Gbh + (size_t)slot * mat + (size_t)(wv * 32 + (lane & 31)) * D);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -86,23 +93,39 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
     }
     const float* Bs = Bbh + (size_t)slot * mat + (size_t)row0 * D;
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) br[i] = Bs[tid + i * NT];
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + i * NT;
+      const float4* bp = (const float4*)(Bs + (q / (D / 8)) * D + (q % (D / 8)) * 8);
+      br[2 * i] = bp[0];
+      br[2 * i + 1] = bp[1];
+    }
   };
   // S <- (a S + B) G, times `post`.
   auto step = [&](float a, float post) {
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) {
-      const int e = tid + i * NT;
-      const int r = e / D, c = e % D;
-      const float x = fmaf(a, S[r * LDF + c], bcur[i]);
-      bf16 hi, lo;
-      split_bf16(x, hi, lo);
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + i * NT;
+      const int r = q / (D / 8), c = (q % (D / 8)) * 8;
+      const f32x4 s0 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c);
+      const f32x4 s1 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c + 4);
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float4 b0 = bcur[2 * i], b1 = bcur[2 * i + 1];
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hi, lo;
+        split_bf16(fmaf(a, sv[e], bv[e]), hi, lo);
+        hv[e] = hi;
+        lv[e] = lo;
+      }
       const int off = swz_off<D>(r, c);
-      *(bf16 VDN_LDS*)(Xh + off) = hi;
-      *(bf16 VDN_LDS*)(Xl + off) = lo;
+      *(bf16x8 VDN_LDS*)(Xh + off) = hv;
+      *(bf16x8 VDN_LDS*)(Xl + off) = lv;
     }
     __syncthreads();
-    f32x16 acc = f32x16{};
+    // three independent accumulation chains: X_hi G_hi, X_hi G_lo, X_lo G_hi
+    f32x16 acc = f32x16{}, acc1 = f32x16{}, acc2 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const float4 g0 = gcur[2 * ks], g1 = gcur[2 * ks + 1];
@@ -118,13 +141,13 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
       const bf16x8 ah = lds_row8<D>(Xh, lane & 31, ks * 2 + half);
       const bf16x8 alo = lds_row8<D>(Xl, lane & 31, ks * 2 + half);
       acc = mfma32(ah, gh, acc);
-      acc = mfma32(ah, gl, acc);
-      acc = mfma32(alo, gh, acc);
+      acc1 = mfma32(ah, gl, acc1);
+      acc2 = mfma32(alo, gh, acc2);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = (j >> 2) * 8 + half * 4 + (j & 3);
-      S[r * LDF + wv * 32 + (lane & 31)] = acc[j] * post;
+      S[r * LDF + wv * 32 + (lane & 31)] = (acc[j] + (acc1[j] + acc2[j])) * post;
     }
     __syncthreads();
   };
@@ -142,7 +165,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) bcur[i] = bnxt[i];
+    for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
   } else {
     if (f >= 0) load(f, gcur, bcur);
     __syncthreads();
@@ -163,7 +186,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
 #pragma unroll
-    for (int i = 0; i < NBV; ++i) bcur[i] = bnxt[i];
+    for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
     f = fn;
   }
   if (dir == 0) {

@@ -70,6 +70,9 @@ EDGE = [
     # window wider than the video: dense softmax, linear read = text write
     dict(name="dense_window", batch=1, heads=2, head_dim=128, frames=9, tokens_per_frame=40,
          text_tokens=9, dtype="bf16", chunk_frames=3, window_chunks=5),
+    # dense window on the V^T / fused path (P, L multiples of 8)
+    dict(name="dense_window_vt", batch=1, heads=2, head_dim=128, frames=9, tokens_per_frame=48,
+         text_tokens=16, dtype="bf16", chunk_frames=2, window_chunks=5),
     dict(name="one_token_frames", batch=1, heads=2, head_dim=128, frames=13, tokens_per_frame=1,
          text_tokens=1, dtype="bf16", chunk_frames=2),
     dict(name="no_text", batch=1, heads=2, head_dim=128, frames=15, tokens_per_frame=64,

@@ -509,8 +509,9 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //  * 8 waves x 32 queries = 256 query rows per workgroup, one workgroup per
 //    CU (two waves per SIMD): every K / V^T tile in LDS feeds 256 queries.
 //  * 64-key tiles in a 3-deep LDS ring; the DMA for tile i+2 is issued while
-//    tile i is processed.  Every wave issues exactly NIW DMA instructions per
-//    tile (dummies included), so "tile i+1 landed" is s_waitcnt vmcnt(NIW).
+//    tile i is processed.  A wave issues the same number of DMA instructions
+//    (NIW or NIW - 1) every tile, so "tile i+1 landed" is one s_waitcnt
+//    vmcnt on that count.
 //  * All K fragments of a tile are read from LDS before its score MFMAs and
 //    all V^T fragments before the softmax VALU work, so LDS latency overlaps
 //    MFMA / VALU work instead of stalling each MFMA pair.
@@ -571,6 +572,9 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // from the tile's first token (one-segment tiles), 32-bit so the load takes
   // a scalar base plus a vector offset; ldsb[i]: LDS block (uniform).
   const bool vwave = wv >= NWH;
+  // real DMA instructions of this wave per tile: NIW or NIW - 1 (no dummies)
+  const int ndma = ((vwave ? VBLK : KBLK) - (wv & (NWH - 1)) + NWH - 1) / NWH;
+  const bool full = ndma == NIW;
   uint32_t offb[NIW];
   int ldsb[NIW];
 #pragma unroll
@@ -604,10 +608,12 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const char* base = sgpr_ptr(vwave ? (const void*)(vtbh + (kb0 + (txt ? N - ka.e2 : dl)))
                                         : (const void*)((txt ? tkbh : kbh) + (size_t)(kb0 + dl) * HD));
 #pragma unroll
-      for (int i = 0; i < NIW; ++i) g2lds16(base + offb[i], bb + ldsb[i]);
+      for (int i = 0; i < NIW; ++i)
+        if (i < NIW - 1 || full) g2lds16(base + offb[i], bb + ldsb[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
+        if (i == NIW - 1 && !full) break;
         const int blk = i * NWH + (wv & (NWH - 1));
         if (!vwave) {
           const int jj = (blk < KBLK ? blk : 0) * 64 + lane;
@@ -715,7 +721,8 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   issue(1, 1);
   f32x16 s[2];
   for (int it = 0; it < ntiles; ++it) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+    if (full) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW - 1) : "memory");
     __syncthreads();
     issue(it + 2, (it + 2) % NBUF);
     scores(it % NBUF, s);

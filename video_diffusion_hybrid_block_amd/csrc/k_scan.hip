@@ -16,9 +16,10 @@
 // wave w computes the 32 x 32 block of columns 32w..32w+31 of the new state
 // with v_mfma_f32_32x32x16_bf16 on a three-pass bf16 split of both operands
 // (X_hi G_hi + X_hi G_lo + X_lo G_hi, relative error ~2^-16).  G is symmetric,
-// so its B-operand columns are read as contiguous rows from global memory.
-// The state lives in LDS between steps (the MFMA result is column-owned, the
-// next A operand row-owned).
+// so its B-operand columns are contiguous rows; G_f is copied to LDS with
+// coalesced direct-to-LDS loads one step ahead.  The state lives in LDS
+// between steps (the MFMA result is column-owned, the next A operand
+// row-owned).
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
@@ -49,14 +50,25 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
                  Geo g, int H) {
   constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
   constexpr int NT = 64 * NRB;
-  constexpr int LDF = D + 4;            // fp32 state row stride (floats)
+  constexpr int LDF = D;                // fp32 state row stride (floats)
   constexpr int NCH = 32 * D / 8 / NT;  // 8-value chunks of X per thread per step
+  constexpr int CPR = D / 4;            // 16-byte chunks per G row
+  constexpr int GBYTES = D * D * 4;
+  constexpr int NGI = GBYTES / 1024 / NRB;   // DMA instructions per wave per G
   static_assert(NCH >= 1 && NCH * 8 * NT == 32 * D, "X build split");
+  static_assert(NGI * 1024 * NRB == GBYTES, "G copy split");
+  // G_f is staged through LDS (two buffers, the next step's copy in flight
+  // during this one) with 16-byte direct-to-LDS loads, one 1 KB block per
+  // instruction; chunk c of row n sits at c ^ gsw(n) so the B-operand reads
+  // (sixteen consecutive rows, one chunk) are conflict-free.
+  __shared__ __attribute__((aligned(1024))) char gbuf[2 * GBYTES];
   __shared__ __attribute__((aligned(16))) float S[32 * LDF];
   __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
   __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
+  char VDN_LDS* Gl = (char VDN_LDS*)gbuf;
   char VDN_LDS* Xh = (char VDN_LDS*)xh;
   char VDN_LDS* Xl = (char VDN_LDS*)xl;
+  auto gsw = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
@@ -77,20 +89,23 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   float* snap = (dir == 0 ? Sf : Sb) + (size_t)bh * (g.nc + 1) * mat;
   const float* al = alpha + (size_t)b * g.T * H + h;
 
-  for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
-
-  // Per-step operands, prefetched one step ahead: this lane's G row (B
-  // operand, G symmetric) and its share of the B rows.
-  // Thread t builds X chunks q = t + i*NT: row q / (D/8), columns 8*(q % (D/8)).
-  float4 gcur[D / 8], gnxt[D / 8];
-  float4 bcur[2 * NCH], bnxt[2 * NCH];
-  auto load = [&](int slot, float4* gr, float4* br) {
-    const float4* gp = (const float4*)(Gbh + (size_t)slot * mat + (size_t)(wv * 32 + (lane & 31)) * D);
+  // G of `slot` into LDS buffer bi: block blk = wv*NGI + i covers slots
+  // 64*blk .. +63 (row slot / CPR, physical chunk slot % CPR).
+  auto copy_g = [&](int slot, int bi) {
+    const float* Gs = Gbh + (size_t)slot * mat;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      gr[2 * ks] = gp[(ks * 16 + half * 8) / 4];
-      gr[2 * ks + 1] = gp[(ks * 16 + half * 8) / 4 + 1];
+    for (int i = 0; i < NGI; ++i) {
+      const int blk = wv * NGI + i;
+      const int sl = blk * 64 + lane;
+      const int row = sl / CPR;
+      const int ch = (sl % CPR) ^ gsw(row);
+      g2lds16(Gs + (size_t)row * D + ch * 4, Gl + bi * GBYTES + blk * 1024);
     }
+  };
+  // This thread's share of the B rows: X chunks q = tid + i*NT, row q / (D/8),
+  // columns 8*(q % (D/8)).
+  float4 bcur[2 * NCH], bnxt[2 * NCH];
+  auto load_b = [&](int slot, float4* br) {
     const float* Bs = Bbh + (size_t)slot * mat + (size_t)row0 * D;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -100,8 +115,9 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
       br[2 * i + 1] = bp[1];
     }
   };
-  // S <- (a S + B) G, times `post`.
-  auto step = [&](float a, float post) {
+  // S <- (a S + B) G, times `post`; G from LDS buffer bi (G symmetric: its
+  // B-operand columns are rows).
+  auto step = [&](float a, float post, int bi) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = tid + i * NT;
@@ -124,12 +140,17 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
       *(bf16x8 VDN_LDS*)(Xl + off) = lv;
     }
     __syncthreads();
+    const int n = wv * 32 + (lane & 31);
+    const int x = gsw(n);
+    const char VDN_LDS* grow = Gl + bi * GBYTES + n * (4 * D);
     // three independent accumulation chains: X_hi G_hi, X_hi G_lo, X_lo G_hi
     f32x16 acc = f32x16{}, acc1 = f32x16{}, acc2 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const float4 g0 = gcur[2 * ks], g1 = gcur[2 * ks + 1];
-      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const int c0 = 4 * ks + 2 * half;
+      const f32x4 g0 = *(const f32x4 VDN_LDS*)(grow + ((c0 ^ x) << 4));
+      const f32x4 g1 = *(const f32x4 VDN_LDS*)(grow + (((c0 + 1) ^ x) << 4));
+      const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
       bf16x8 gh, gl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -156,38 +177,44 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
     for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
   };
 
-  int f = next_frame(g, dir, -1);
-  if (g.L > 0) {
-    load(g.T, gcur, bcur);
-    if (f >= 0) load(f, gnxt, bnxt);
-    __syncthreads();
-    step(0.0f, 0.5f);                    // S0 = S_x / 2
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
-#pragma unroll
-    for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
-  } else {
-    if (f >= 0) load(f, gcur, bcur);
-    __syncthreads();
+  // Step sequence: the text write (slot T, a = 0, times 1/2) when there is
+  // text, then the frames the chain folds.  Step k uses LDS buffer k & 1; the
+  // copy for step k+1 is issued once every wave is done with step k-1.
+  bool text = g.L > 0;
+  int slot = text ? g.T : next_frame(g, dir, -1);
+  if (slot >= 0) {
+    copy_g(slot, 0);
+    load_b(slot, bcur);
   }
-  snapshot(g.nc);
+  for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
+  __syncthreads();
+  if (!text) snapshot(g.nc);
   int c = dir == 0 ? 0 : g.nc - 1;
-  while (f >= 0) {
-    const int fn = next_frame(g, dir, f);
-    if (fn >= 0) load(fn, gnxt, bnxt);
-    // chunks whose state is the one before frame f (anchors in between do
-    // not change the state)
-    if (dir == 0) {
-      while (c < g.nc && win_lo(g, c) <= f) snapshot(c++);
-    } else {
-      while (c >= 0 && win_hi(g, c) >= f) snapshot(c--);
+  int bi = 0;
+  while (slot >= 0) {
+    const int nslot = text ? next_frame(g, dir, -1) : next_frame(g, dir, slot);
+    if (!text) {
+      // chunks whose state is the one before frame `slot` (anchors in
+      // between do not change the state)
+      if (dir == 0) {
+        while (c < g.nc && win_lo(g, c) <= slot) snapshot(c++);
+      } else {
+        while (c >= 0 && win_hi(g, c) >= slot) snapshot(c--);
+      }
     }
-    step(al[(size_t)f * H], 1.0f);
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) gcur[i] = gnxt[i];
+    wait_vmem();                          // own copies of this step's G and B
+    __syncthreads();                      // everyone's; step k-1 done with buffer bi ^ 1
+    if (nslot >= 0) {
+      copy_g(nslot, bi ^ 1);
+      load_b(nslot, bnxt);
+    }
+    step(text ? 0.0f : al[(size_t)slot * H], text ? 0.5f : 1.0f, bi);
+    if (text) snapshot(g.nc);
 #pragma unroll
     for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
-    f = fn;
+    bi ^= 1;
+    text = false;
+    slot = nslot;
   }
   if (dir == 0) {
     while (c < g.nc) snapshot(c++);

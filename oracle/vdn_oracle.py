@@ -415,3 +415,37 @@ def hybrid_attn(inputs: dict, lay: Layout, readings: Readings = PRIMARY) -> np.n
         for h in range(lay.heads):
             out[b, :, h] = hybrid_attn_rows(inputs, lay, b, h, tokens, readings)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Output projections (the step right after the layer)  [PD §三, figure 3]
+# ---------------------------------------------------------------------------
+
+def gated_branches(inputs: dict, lay: Layout, readings: Readings = PRIMARY) -> np.ndarray:
+    """The two gated branch outputs side by side, before their projections:
+    X2[b, i, 0] = sigmoid(l0) O_soft and X2[b, i, 1] = sigmoid(l1) RMSNorm(o_lin),
+    each [H, d], so a token's row is 2*H*d long, softmax branch first.  Their
+    per-head sum is the layer output O [PD §三: each branch has its own gate
+    and its own output projection, then both return to the residual]."""
+    B, N, H, d = inputs["q"].shape
+    x2 = np.zeros((B, N, 2, H, d), dtype=np.float64)
+    tokens = np.arange(lay.video_tokens)
+    gates = np.asarray(inputs["gate_logits"], np.float64)
+    for b in range(lay.batch):
+        for h in range(lay.heads):
+            _, o_soft, _, n_lin = hybrid_attn_rows(inputs, lay, b, h, tokens, readings, parts=True)
+            g = gates[b, tokens, h]
+            x2[b, :, 0, h] = _sigmoid(g[:, 0:1]) * o_soft
+            x2[b, :, 1, h] = _sigmoid(g[:, 1:2]) * n_lin
+    return x2
+
+
+def output_projection(x2, w_o) -> np.ndarray:
+    """y = W_s (gated softmax branch) + W_l (gated linear branch), one product
+    with the two weights side by side: w_o [d_model, 2*H*d] in (out, in)
+    order, the first H*d input columns for the softmax branch, the rest for
+    the linear branch.  x2 [B, N, 2, H, d] -> y [B, N, d_model]
+    [PD §三; deepmagic blog 實測數據 (linear layers after the attention)]."""
+    x2 = np.asarray(x2, np.float64)
+    B, N = x2.shape[:2]
+    return x2.reshape(B, N, -1) @ np.asarray(w_o, np.float64).T

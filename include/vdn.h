@@ -156,6 +156,53 @@ vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
                                    void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* The two gated branches side by side, the input of the per-branch output
+ * projections: x2 [B, T*P, 2, H, d] (layout->dtype) with
+ *   x2[b][n][0][h] = sigmoid(g0) * O_soft,  x2[b][n][1][h] = sigmoid(g1) * RMSNorm(R[c] q)
+ * (O_soft and R q kept in float32 until this final rounding).  Covers the
+ * layouts vdn_softmax_merge_fwd covers, else VDN_ERR_UNSUPPORTED.
+ * workspace: as for vdn_softmax_fwd.  x2 must not alias any input.
+ * [PaperDaily §三, figure 3 (each branch has its own gate and output
+ *  projection); arXiv abstract (separate output projections)] */
+vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* v,
+                                      const void* text_k, const void* text_v,
+                                      const float* R, const float* gate_logits,
+                                      const vdn_layout_t* layout, void* x2,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Output projections of the two branches as one product:
+ *   y[m][n] = sum_k x[m][k] * w[n][k]     (fp32 accumulation)
+ * x: bf16 [M, K] row-major (M tokens; per token the K = 2*H*d values of x2),
+ * w: bf16 [N, K] row-major = [W_softmax | W_linear] in (out, in) order, softmax
+ * branch columns first, y: bf16 [M, N].  So y = W_s x_s + W_l x_l per token,
+ * each branch through its own matrix.  Needs K a positive multiple of 64 and
+ * N a multiple of 8 (else VDN_ERR_UNSUPPORTED); y must not alias x or w.
+ * [PaperDaily §三, figure 3; arXiv abstract] */
+vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, int32_t N,
+                          void* y, hipStream_t stream);
+
+/* Bytes of workspace vdn_hybrid_attn_proj_fwd needs (0 if the layout is
+ * invalid): the vdn_hybrid_attn_fwd workspace plus x2.  Host only. */
+size_t vdn_hybrid_attn_proj_workspace_size(const vdn_layout_t* layout);
+
+/* The layer with its separate output projections:
+ *   y = [sigmoid(g0) O_soft ; sigmoid(g1) RMSNorm(R q)] . w_o^T
+ * per video token, i.e. vdn_hybrid_attn_fwd's stages with the branches kept
+ * apart (vdn_softmax_branches_fwd) followed by vdn_out_proj.  w_o: bf16
+ * [d_model, 2*H*d] (softmax-branch columns first); y: bf16 [B, T*P, d_model].
+ * Covers bf16 layouts with d in {32, 64, 128}, P and L multiples of 8, and
+ * d_model a multiple of 8; else VDN_ERR_UNSUPPORTED.  workspace: at least
+ * vdn_hybrid_attn_proj_workspace_size(layout) bytes, 256-byte aligned.
+ * [PaperDaily §三, figure 3; arXiv abstract] */
+vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* v,
+                                      const void* text_k, const void* text_v,
+                                      const float* beta, const float* alpha,
+                                      const float* gate_logits, const void* w_o,
+                                      int32_t d_model, const vdn_layout_t* layout, void* y,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* Frame statistics: for every frame f < T and for the text block (slot T),
  * A[b,h,slot] = sum_i beta_i k_i k_i^T and B[b,h,slot] = sum_i beta_i v_i k_i^T
  * over the slot's tokens.  A_out, B_out: float32 [B, H, T+1, d, d] (row index
@@ -170,8 +217,8 @@ vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k,
 size_t vdn_vda_factor_scan_workspace_size(const vdn_layout_t* layout);
 
 /* Factor and scan: A_io holds the frame Grams from vdn_vda_gram and is
- * overwritten with (I + A)^-1 for the frames the scan uses (Cholesky
- * I + A = L L^T, then L^-T L^-1) and for the text slot.  B is read only.
+ * overwritten with (I + A)^-1 for the frames the scan uses (a symmetric
+ * sweep: in-place Gauss-Jordan on the SPD matrix) and for the text slot.  B is read only.
  * R_out: float32 [B, H, nc+1, d, d] with nc = vdn_num_chunks(layout);
  * R_out[c] = S_fwd(c) + S_bwd(c), the summed states a non-anchor query frame of
  * chunk c reads, and R_out[nc] = S_x, the full text write (what anchor frames

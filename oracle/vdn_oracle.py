@@ -421,6 +421,23 @@ def hybrid_attn(inputs: dict, lay: Layout, readings: Readings = PRIMARY) -> np.n
 # Output projections (the step right after the layer)  [PD §三, figure 3]
 # ---------------------------------------------------------------------------
 
+def gated_branches_rows(inputs: dict, lay: Layout, b: int, tokens,
+                        readings: Readings = PRIMARY) -> np.ndarray:
+    """Gated branch outputs of the given video tokens of batch b, every head:
+    [len(tokens), 2, H, d] with [:, 0, h] = sigmoid(l0) O_soft and
+    [:, 1, h] = sigmoid(l1) RMSNorm(o_lin) [PD §三, figure 3]."""
+    tokens = np.asarray(tokens)
+    H, d = inputs["q"].shape[2], inputs["q"].shape[3]
+    out = np.zeros((len(tokens), 2, H, d), dtype=np.float64)
+    gates = np.asarray(inputs["gate_logits"], np.float64)
+    for h in range(lay.heads):
+        _, o_soft, _, n_lin = hybrid_attn_rows(inputs, lay, b, h, tokens, readings, parts=True)
+        g = gates[b, tokens, h]
+        out[:, 0, h] = _sigmoid(g[:, 0:1]) * o_soft
+        out[:, 1, h] = _sigmoid(g[:, 1:2]) * n_lin
+    return out
+
+
 def gated_branches(inputs: dict, lay: Layout, readings: Readings = PRIMARY) -> np.ndarray:
     """The two gated branch outputs side by side, before their projections:
     X2[b, i, 0] = sigmoid(l0) O_soft and X2[b, i, 1] = sigmoid(l1) RMSNorm(o_lin),
@@ -430,13 +447,8 @@ def gated_branches(inputs: dict, lay: Layout, readings: Readings = PRIMARY) -> n
     B, N, H, d = inputs["q"].shape
     x2 = np.zeros((B, N, 2, H, d), dtype=np.float64)
     tokens = np.arange(lay.video_tokens)
-    gates = np.asarray(inputs["gate_logits"], np.float64)
     for b in range(lay.batch):
-        for h in range(lay.heads):
-            _, o_soft, _, n_lin = hybrid_attn_rows(inputs, lay, b, h, tokens, readings, parts=True)
-            g = gates[b, tokens, h]
-            x2[b, :, 0, h] = _sigmoid(g[:, 0:1]) * o_soft
-            x2[b, :, 1, h] = _sigmoid(g[:, 1:2]) * n_lin
+        x2[b] = gated_branches_rows(inputs, lay, b, tokens, readings)
     return x2
 
 

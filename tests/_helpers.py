@@ -65,3 +65,26 @@ def sample_tokens(w: synth.Workload, rng) -> np.ndarray:
     local |= set(rng.integers(0, P, size=4).tolist())
     local = sorted(x for x in local if 0 <= x < P)
     return np.array([f * P + x for f in frames for x in local], dtype=np.int64)
+
+
+def oracle_chunk_reads(inp: dict, lay, w: synth.Workload) -> np.ndarray:
+    """R [B, H, nc+1, d, d] float32 from the oracle's per-frame states: slot c
+    holds what the non-anchor frames of chunk c read (taken from the chunk's
+    first non-anchor frame; zero when the chunk holds anchors only), slot nc
+    the text write (what an anchor frame reads)."""
+    nc = lay.num_chunks
+    d = w.head_dim
+    anchors = set(O.anchor_frames(lay))
+    R = np.zeros((w.batch, w.heads, nc + 1, d, d), np.float32)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            per_frame = O.chunk_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], inp["beta"],
+                                       inp["alpha"], lay, b, h)
+            for c in range(nc):
+                frames = [t for t in range(c * lay.chunk_frames,
+                                           min((c + 1) * lay.chunk_frames, w.frames))
+                          if t not in anchors]
+                if frames:
+                    R[b, h, c] = per_frame[frames[0]]
+            R[b, h, nc] = per_frame[min(anchors)] if anchors else 0.0
+    return R

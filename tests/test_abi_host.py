@@ -171,3 +171,45 @@ def test_kernel_geometry_matches_oracle(geometry_probe, C, w):
         needed = sorted(set().union(*[set(O.far_forward(lay, t)) | set(O.far_backward(lay, t))
                                       for t in range(T)]))
         assert slots == needed + [T], (T, C, w, af, al)
+
+
+def test_projection_entry_points_reject_bad_arguments_before_launch():
+    lib = V.lib()
+    ok = ctypes.c_void_p(0x10000)         # aligned fake pointers: never dereferenced
+    odd = ctypes.c_void_p(0x10004)
+    nul = None
+    lay_vt = _lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=0, head_dim=32)
+    lay_16 = _lay(batch=1, heads=1, frames=2, tokens_per_frame=4, text_tokens=0, head_dim=16)
+    # gated branches side by side: same coverage and checks as the fused merge
+    br = [ok, ok, ok, nul, nul, ok, ok, ctypes.byref(lay_vt), ok, ok, 1 << 40, nul]
+    a = list(br); a[7] = ctypes.byref(lay_16)
+    assert lib.vdn_softmax_branches_fwd(*a) == 3
+    a = list(br); a[8] = nul
+    assert lib.vdn_softmax_branches_fwd(*a) == 1
+    a = list(br); a[8] = odd
+    assert lib.vdn_softmax_branches_fwd(*a) == 4
+    a = list(br); a[10] = 16
+    assert lib.vdn_softmax_branches_fwd(*a) == 5
+    # the product: K a multiple of 64, N a multiple of 8, sizes >= 1
+    assert lib.vdn_out_proj(nul, ok, 10, 128, 64, ok, nul) == 1
+    assert lib.vdn_out_proj(ok, ok, 0, 128, 64, ok, nul) == 2
+    assert lib.vdn_out_proj(ok, ok, 10, 96, 64, ok, nul) == 3
+    assert lib.vdn_out_proj(ok, ok, 10, 128, 60, ok, nul) == 3
+    assert lib.vdn_out_proj(ok, odd, 10, 128, 64, ok, nul) == 4
+    # the layer with projections
+    ws = V.proj_workspace_size(lay_vt)
+    assert ws > V.workspace_size(lay_vt)
+    assert ws - V.workspace_size(lay_vt) >= 2 * 16 * 1 * 32 * 2      # x2: N*2*H*d bf16
+    args = [ok, ok, ok, nul, nul, ok, ok, ok, ok, 64, ctypes.byref(lay_vt), ok, ok, 1 << 40, nul]
+    a = list(args); a[8] = nul
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 1
+    a = list(args); a[9] = 0
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 2
+    a = list(args); a[9] = 12
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 3
+    a = list(args); a[10] = ctypes.byref(lay_16)
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 3
+    a = list(args); a[11] = odd
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 4
+    a = list(args); a[13] = ws - 256
+    assert lib.vdn_hybrid_attn_proj_fwd(*a) == 5

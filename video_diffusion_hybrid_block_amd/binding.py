@@ -16,7 +16,8 @@ __all__ = [
     "VdnError", "Layout", "lib", "library_path", "version", "validate_layout",
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
-    "softmax_fwd", "softmax_merge_fwd", "vda_gram", "vda_factor_scan", "merge", "make_layout",
+    "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "vda_gram", "vda_factor_scan",
+    "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "make_layout",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -31,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "vdn_num_chunks", "vdn_hybrid_attn_workspace_size", "vdn_hybrid_attn_fwd",
     "vdn_softmax_workspace_size", "vdn_softmax_fwd", "vdn_softmax_merge_fwd", "vdn_vda_gram",
     "vdn_vda_factor_scan_workspace_size",
-    "vdn_vda_factor_scan", "vdn_merge",
+    "vdn_vda_factor_scan", "vdn_merge", "vdn_softmax_branches_fwd", "vdn_out_proj",
+    "vdn_hybrid_attn_proj_workspace_size", "vdn_hybrid_attn_proj_fwd",
 )
 
 
@@ -97,6 +99,15 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_factor_scan.argtypes = [vp, vp, vp, lp, vp, vp, sz, vp]
         L.vdn_merge.restype = ctypes.c_int
         L.vdn_merge.argtypes = [vp, vp, vp, vp, lp, vp, vp]
+        L.vdn_softmax_branches_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, vp, vp, sz, vp]
+        L.vdn_softmax_branches_fwd.restype = ctypes.c_int
+        L.vdn_out_proj.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        L.vdn_out_proj.restype = ctypes.c_int
+        L.vdn_hybrid_attn_proj_workspace_size.argtypes = [lp]
+        L.vdn_hybrid_attn_proj_workspace_size.restype = sz
+        L.vdn_hybrid_attn_proj_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                               lp, vp, vp, sz, vp]
+        L.vdn_hybrid_attn_proj_fwd.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -261,6 +272,93 @@ def softmax_merge_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tokens
                                        _ptr(text_v if L else None), _ptr(R), _ptr(gate_logits),
                                        ctypes.byref(lay), _ptr(out), _ptr(workspace), nbytes,
                                        _stream()), "vdn_softmax_merge_fwd")
+    return out
+
+
+def softmax_branches_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tokens_per_frame,
+                         chunk_frames=5, window_chunks=1, anchor_first=True, anchor_last=True,
+                         softmax_scale=0.0, rms_eps=0.0, out=None, workspace=None) -> torch.Tensor:
+    """The two gated branches side by side (``vdn_softmax_branches_fwd``):
+    returns x2 [B, N, 2, H, d] in q's dtype, softmax branch at index 0."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    _expect(R, (B, H, num_chunks(lay) + 1, d, d), torch.float32, "R")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty((B, N, 2, H, d), dtype=q.dtype, device=q.device)
+    _expect(out, (B, N, 2, H, d), q.dtype, "out")
+    L = lay.text_tokens
+    need = softmax_workspace_size(lay)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vdn_softmax_branches_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
+                                          _ptr(text_v if L else None), _ptr(R),
+                                          _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
+                                          _ptr(workspace), nbytes, _stream()),
+           "vdn_softmax_branches_fwd")
+    return out
+
+
+def out_proj(x, w, out=None) -> torch.Tensor:
+    """Output projections as one product (``vdn_out_proj``): x bf16 [..., K],
+    w bf16 [N, K]; returns y bf16 [..., N] = x . w^T."""
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("out_proj takes bf16 x and w")
+    K = x.shape[-1]
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w: expected [N, {K}], got {tuple(w.shape)}")
+    N = w.shape[0]
+    M = x.numel() // K if K else 0
+    _expect(x, x.shape, torch.bfloat16, "x")
+    _expect(w, w.shape, torch.bfloat16, "w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
+    _expect(out, tuple(x.shape[:-1]) + (N,), torch.bfloat16, "out")
+    _check(lib().vdn_out_proj(_ptr(x), _ptr(w), M, K, N, _ptr(out), _stream()), "vdn_out_proj")
+    return out
+
+
+def proj_workspace_size(layout: Layout) -> int:
+    return lib().vdn_hybrid_attn_proj_workspace_size(ctypes.byref(layout))
+
+
+def hybrid_attn_proj(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_o, *, frames,
+                     tokens_per_frame, chunk_frames=5, window_chunks=1, anchor_first=True,
+                     anchor_last=True, softmax_scale=0.0, rms_eps=0.0, out=None,
+                     workspace=None) -> torch.Tensor:
+    """The layer with its separate output projections
+    (``vdn_hybrid_attn_proj_fwd``): w_o bf16 [d_model, 2*H*d]; returns y bf16
+    [B, N, d_model]."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if w_o is None or w_o.dim() != 2 or w_o.shape[1] != 2 * H * d:
+        raise ValueError(f"w_o: expected [d_model, {2 * H * d}]")
+    _expect(w_o, w_o.shape, q.dtype, "w_o")
+    dm = w_o.shape[0]
+    if out is None:
+        out = torch.empty((B, N, dm), dtype=q.dtype, device=q.device)
+    _expect(out, (B, N, dm), q.dtype, "out")
+    need = proj_workspace_size(lay)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().vdn_hybrid_attn_proj_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(w_o), dm, ctypes.byref(lay), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_proj_fwd")
     return out
 
 

@@ -131,8 +131,39 @@ vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
     return VDN_ERR_MISALIGNED;
   if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
-                                         eff_scale(*layout), eff_eps(*layout), o, workspace,
+                                         eff_scale(*layout), eff_eps(*layout), false, o, workspace,
                                          stream));
+}
+
+vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* v,
+                                      const void* text_k, const void* text_v, const float* R,
+                                      const float* gate_logits, const vdn_layout_t* layout,
+                                      void* x2, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!softmax_merge_fusable(*layout)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !R || !gate_logits || !x2 || !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  const size_t need = softmax_ws_bytes(*layout);
+  if (need > 0 && !workspace) return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(R) || !aligned16(gate_logits) ||
+      !aligned16(x2) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
+                                         eff_scale(*layout), eff_eps(*layout), true, x2, workspace,
+                                         stream));
+}
+
+vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, int32_t N, void* y,
+                          hipStream_t stream) {
+  if (!x || !w || !y) return VDN_ERR_NULL_ARG;
+  if (M < 1 || K < 1 || N < 1) return VDN_ERR_BAD_SHAPE;
+  if (!proj_shape_ok(M, K, N)) return VDN_ERR_UNSUPPORTED;
+  if ((M + 255) / 256 * ((N + 255) / 256) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return VDN_ERR_MISALIGNED;
+  return hip_status(launch_proj(x, w, M, K, N, y, stream));
 }
 
 vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
@@ -207,9 +238,73 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
   if (e != hipSuccess) return hip_status(e);
   if (softmax_merge_fusable(l))
     return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                           eff_eps(l), o, ws + p.vt_off, stream));
+                                           eff_eps(l), false, o, ws + p.vt_off, stream));
   e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
   if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// x2 (the gated branches, bf16 [B, T*P, 2, H, d]) follows the layer's plan.
+size_t proj_x2_off(const vdn_layout_t& l) { return make_plan(l).total; }
+size_t proj_ws_total(const vdn_layout_t& l) {
+  return align256(proj_x2_off(l) + (size_t)l.batch * l.frames * l.tokens_per_frame * 2 * l.heads *
+                                       l.head_dim_k * 2);
+}
+bool proj_layer_ok(const vdn_layout_t& l, int32_t d_model) {
+  return softmax_merge_fusable(l) &&
+         proj_shape_ok((long)l.batch * l.frames * l.tokens_per_frame, 2 * l.heads * l.head_dim_k,
+                       d_model);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vdn_hybrid_attn_proj_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return proj_ws_total(*layout);
+}
+
+vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* v,
+                                      const void* text_k, const void* text_v, const float* beta,
+                                      const float* alpha, const float* gate_logits,
+                                      const void* w_o, int32_t d_model,
+                                      const vdn_layout_t* layout, void* y, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (d_model < 1) return VDN_ERR_BAD_SHAPE;
+  const vdn_layout_t& l = *layout;
+  if (!proj_layer_ok(l, d_model)) return VDN_ERR_UNSUPPORTED;
+  const long M = (long)l.batch * l.frames * l.tokens_per_frame;
+  if ((M + 255) / 256 * ((d_model + 255) / 256) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !w_o || !y || !workspace ||
+      !text_ok(l, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(w_o) || !aligned16(y) || !aligned16(workspace) ||
+      !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < proj_ws_total(l)) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  const Plan p = make_plan(l);
+  char* ws = (char*)workspace;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* Sf = (float*)(ws + p.sf_off);
+  float* Sb = (float*)(ws + p.sb_off);
+  float* R = (float*)(ws + p.r_off);
+  void* x2 = ws + proj_x2_off(l);
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  if (e == hipSuccess)
+    e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
+                             true, x2, ws + p.vt_off, stream);
+  if (e == hipSuccess) e = launch_proj(x2, w_o, M, 2 * l.heads * l.head_dim_k, d_model, y, stream);
   return hip_status(e);
 }
 

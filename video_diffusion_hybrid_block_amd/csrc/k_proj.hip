@@ -1,0 +1,146 @@
+// Output projections of the two branches as one product:
+//   y[m][n] = sum_k x[m][k] w[n][k],
+// x = [sigmoid(l0) O_soft ; sigmoid(l1) RMSNorm(R q)] per token (2*H*d
+// values, softmax branch first), w = [W_s W_l] in (out, in) order.  Each
+// branch keeps its own projection; one product applies both and adds them.
+// [PaperDaily "伯克利与Impossible视频生成:14.3秒视频6.70秒去噪" §三, figure 3
+//  (each branch: own gate, own output projection, then added back to the
+//  residual stream); arXiv listing "Video DeltaNet: A Video-Native Hybrid
+//  Attention for Livestream Video Generation", abstract (separate output
+//  projections and learnable gates calibrate the two branches)]
+//
+// gfx950 design: bf16 operands, fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16, bf16 output.  A workgroup of 8 waves computes a
+// 256 (n) x 256 (m) block of y^T: wave (wn, wm) owns 128 n x 64 m, i.e.
+// 4 x 2 MFMA blocks.  Computing y^T (A = w rows, B = x rows, both
+// k-contiguous) lets each lane own one token and store four consecutive
+// outputs at a time.  64-deep k steps stream through a two-stage LDS ring
+// with 16-byte direct-to-LDS loads (waves 0-3 move the w tile, 4-7 the x
+// tile); rows are 128 bytes with the 16-byte chunk c of row r stored at
+// c ^ ((r / 2) % 8), so sixteen lanes reading sixteen rows at one chunk hit
+// distinct bank groups.  XCD-aware tile order keeps the output tiles of one
+// token block on one XCD, whose L2 then serves that block's x to all of them.
+#include "vdn_device.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+namespace {
+
+constexpr int PBM = 256, PBN = 256, PBK = 64;
+
+__global__ void __launch_bounds__(512)
+proj_gemm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* __restrict__ y,
+                 long M, int K, int N) {
+  constexpr int ROWB = PBK * 2;                   // 128-byte rows
+  constexpr int TILEB = PBM * ROWB;               // 32 KB per operand tile
+  constexpr int STAGE = 2 * TILEB;                // w tile then x tile
+  constexpr int NIW = TILEB / 1024 / 4;           // DMA instructions per wave per tile (8)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  char VDN_LDS* lds = (char VDN_LDS*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int mt_n = (int)((M + PBM - 1) / PBM), nt_n = (N + PBN - 1) / PBN;
+  const int ntile = mt_n * nt_n;
+  int tid_ = blockIdx.x;
+  if ((ntile & 7) == 0) tid_ = (tid_ & 7) * (ntile >> 3) + (tid_ >> 3);
+  const int mt = sgpr(tid_ / nt_n), nt = sgpr(tid_ % nt_n);
+  const long m0 = (long)mt * PBM;
+  const int n0 = nt * PBN;
+
+  // DMA: waves 0-3 fill the w tile (rows n0 ..), waves 4-7 the x tile (rows
+  // m0 ..); instruction i of a wave fills 1 KB block 4*i + (wv % 4), lane l
+  // writing slot 64*blk + l: row slot / 8, physical chunk slot % 8, which holds
+  // logical chunk (slot % 8) ^ ((row / 2) % 8).  Rows past M (N) re-read the
+  // last row; their results are never stored.
+  const bool xw = wv >= 4;
+  const bf16* src[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int sl = (i * 4 + (wv & 3)) * 64 + lane;
+    const int r = sl / 8;
+    const int ch = (sl % 8) ^ ((r / 2) % 8);
+    const long grow = xw ? (m0 + r < M ? m0 + r : M - 1) : (long)(n0 + r < N ? n0 + r : N - 1);
+    src[i] = (xw ? x : w) + grow * K + ch * 8;
+  }
+  auto issue = [&](int kt, int stg) {
+    char VDN_LDS* tb = lds + stg * STAGE + (xw ? TILEB : 0);
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) g2lds16(src[i] + kt * PBK, tb + (i * 4 + (wv & 3)) * 1024);
+  };
+
+  // Read bases: row r, logical chunk 2j + half sits at physical
+  // (2j + half) ^ ((r / 2) % 8) = 2j ^ yv, yv = half ^ ((r / 2) % 8); the 32-row
+  // blocks of a wave add multiples of 4 KB (immediate offsets).
+  const int wn = wv & 1, wm = wv >> 1;             // 2 (n) x 4 (m) waves
+  const int rl = lane & 31;
+  const int rbase = rl * ROWB + 16 * (half ^ ((rl / 2) % 8));
+  const int aoff = wn * 128 * ROWB;                // w rows of this wave
+  const int boff = TILEB + wm * 64 * ROWB;         // x rows of this wave
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int nk = K / PBK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // own copies of step kt
+    __syncthreads();                                     // everyone's; step kt-1 done
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    const char VDN_LDS* st = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < PBK / 16; ++ks) {
+      const int ro = rbase ^ (32 * ks);
+      bf16x8 af[4], bfv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8 VDN_LDS*)(st + aoff + i * 32 * ROWB + ro);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfv[j] = *(const bf16x8 VDN_LDS*)(st + boff + j * 32 * ROWB + ro);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
+    }
+  }
+
+  // acc[i][j][e]: y^T[n][m] with n = n0 + wn*128 + 32 i + 8 (e / 4) + 4 half +
+  // e % 4 and m = m0 + wm*64 + 32 j + lane % 32: four consecutive n per group.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const long m = m0 + wm * 64 + 32 * j + rl;
+    if (m >= M) continue;
+    bf16* yr = y + m * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * half;
+        if (n >= N) continue;
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][g * 4 + e];
+        *(bf16x4*)(yr + n) = v;
+      }
+  }
+}
+
+}  // namespace
+
+bool proj_shape_ok(long M, int K, int N) {
+  return M >= 1 && K >= PBK && K % PBK == 0 && N >= 8 && N % 8 == 0;
+}
+
+hipError_t launch_proj(const void* x, const void* w, long M, int K, int N, void* y, hipStream_t s) {
+  if (!proj_shape_ok(M, K, N)) return hipErrorInvalidValue;
+  const long ntile = ((M + PBM - 1) / PBM) * (long)((N + PBN - 1) / PBN);
+  proj_gemm_kernel<<<dim3((unsigned)ntile), dim3(512), 0, s>>>((const bf16*)x, (const bf16*)w,
+                                                                (bf16*)y, M, K, N);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

@@ -517,7 +517,12 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //    MFMA / VALU work instead of stalling each MFMA pair.
 //  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
 //    both read with ds_read_b128 at base + immediate, conflict-free.
-template <int D, bool FUSE>
+// MODE 0 writes the softmax branch O_soft; MODE 1 the merged output
+// sigmoid(l0) O_soft + sigmoid(l1) RMSNorm(R q); MODE 2 the two gated branches
+// side by side, o[b][n][0][h][:] = sigmoid(l0) O_soft and
+// o[b][n][1][h][:] = sigmoid(l1) RMSNorm(R q), the input of the per-branch
+// output projections.
+template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                   const bf16* __restrict__ tk, const bf16* __restrict__ vtg, int nl8,
@@ -731,7 +736,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float inv = 1.0f / xhalf_sum(l_run);
-  if constexpr (!FUSE) {
+  if constexpr (MODE == 0) {
     if (qvalid) {
       bf16* orow = o + qoff;
 #pragma unroll
@@ -807,18 +812,37 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const float rinv = rsqrtf(ss * (1.0f / D) + eps);
     const float g0 = sigmoidf(gl.x) * inv, g1 = sigmoidf(gl.y) * rinv;
     if (qvalid) {
-      bf16* orow = o + qoff;
+      if constexpr (MODE == 1) {
+        bf16* orow = o + qoff;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = db * 32 + jj * 8 + half * 4;
-          bf16x4 val;
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + jj * 8 + half * 4;
+            bf16x4 val;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            val[e] = (bf16)fmaf(g0, oacc[db][jj * 4 + e], g1 * lin[db][jj * 4 + e]);
-          *(bf16x4*)(orow + d) = val;
-        }
+            for (int e = 0; e < 4; ++e)
+              val[e] = (bf16)fmaf(g0, oacc[db][jj * 4 + e], g1 * lin[db][jj * 4 + e]);
+            *(bf16x4*)(orow + d) = val;
+          }
+      } else {
+        bf16* orow = o + ((size_t)(w.b * (size_t)N + qrow) * 2 * H + w.h) * D;
+        bf16* lrow = orow + (size_t)H * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + jj * 8 + half * 4;
+            bf16x4 vs, vl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              vs[e] = (bf16)(g0 * oacc[db][jj * 4 + e]);
+              vl[e] = (bf16)(g1 * lin[db][jj * 4 + e]);
+            }
+            *(bf16x4*)(orow + d) = vs;
+            *(bf16x4*)(lrow + d) = vl;
+          }
+      }
     }
   }
 }
@@ -861,7 +885,7 @@ vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
-                       const float* R, const float* gates, float eps, hipStream_t s) {
+                       const float* R, const float* gates, float eps, int mode, hipStream_t s) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
@@ -875,16 +899,20 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
         (const bf16*)v, (const bf16*)tv, (bf16*)ws, N, g.L, l.heads, nl8, ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (R)
-      softmax_vt_kernel<D, true><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+    if (mode == 1)
+      softmax_vt_kernel<D, 1><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps);
+    else if (mode == 2)
+      softmax_vt_kernel<D, 2><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
           l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps);
     else
-      softmax_vt_kernel<D, false><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+      softmax_vt_kernel<D, 0><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
           l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f);
   } else {
-    if (R) return hipErrorNotSupported;
+    if (mode != 0) return hipErrorNotSupported;
     softmax_mfma_kernel<D, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
         nullptr, 0, (bf16*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
@@ -900,9 +928,9 @@ hipError_t launch_softmax(const void* q, const void* k, const void* v, const voi
   const int d = l.head_dim_k;
   if (l.dtype == VDN_BF16) {
     switch (d) {
-      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
-      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
-      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, s);
+      case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, 0, s);
+      case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, 0, s);
+      case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, nullptr, nullptr, 0.f, 0, s);
       case 16: return launch_valu<bf16, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
   } else {
@@ -922,13 +950,14 @@ bool softmax_merge_fusable(const vdn_layout_t& l) {
 
 hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
                                 const void* tv, const float* R, const float* gates,
-                                const vdn_layout_t& l, float scale, float eps, void* o, void* ws,
-                                hipStream_t s) {
+                                const vdn_layout_t& l, float scale, float eps, bool split, void* o,
+                                void* ws, hipStream_t s) {
   if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
+  const int mode = split ? 2 : 1;
   switch (l.head_dim_k) {
-    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
-    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
-    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, s);
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
   }
   return hipErrorInvalidValue;
 }

@@ -186,11 +186,16 @@ hipError_t launch_scan(const float* G, const float* B, const float* alpha, const
 hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
                         const vdn_layout_t& l, float eps, void* o, hipStream_t s);
 // Softmax branch with the merge fused into its epilogue (bf16, V^T path only):
-// o = sigmoid(g0) softmax + sigmoid(g1) RMSNorm(R q).
+// o = sigmoid(g0) softmax + sigmoid(g1) RMSNorm(R q), or with `split` the two
+// gated branches side by side, o [B][N][2][H][d] (softmax branch first).
 bool softmax_merge_fusable(const vdn_layout_t& l);
 hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
                                 const void* tv, const float* R, const float* gates,
-                                const vdn_layout_t& l, float scale, float eps, void* o, void* ws,
-                                hipStream_t s);
+                                const vdn_layout_t& l, float scale, float eps, bool split, void* o,
+                                void* ws, hipStream_t s);
+// Output projections: y[m][n] = sum_k x[m][k] w[n][k] (bf16 in and out, fp32
+// accumulation); needs K a positive multiple of 64 and N a multiple of 8.
+bool proj_shape_ok(long M, int K, int N);
+hipError_t launch_proj(const void* x, const void* w, long M, int K, int N, void* y, hipStream_t s);
 
 }  // namespace vdn

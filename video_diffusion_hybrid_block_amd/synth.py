@@ -19,7 +19,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_bf16", "layout_kwargs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_proj_weight", "make_gemm_operands",
+           "round_bf16", "layout_kwargs"]
 
 
 @dataclass(frozen=True)
@@ -140,3 +141,23 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> dict:
     return dict(q=q, k=k, v=v, text_k=text_k, text_v=text_v,
                 beta=beta.astype(np.float32), alpha=alpha.astype(np.float32),
                 gate_logits=gates.astype(np.float32))
+
+
+def make_proj_weight(d_model: int, heads: int, head_dim: int, seed: int,
+                     dtype: str = "bf16") -> np.ndarray:
+    """Output-projection weights w_o [d_model, 2*H*d] in (out, in) order,
+    softmax-branch input columns first: N(0, 1 / (2*H*d)) draws (a random
+    initialisation of a trained projection's scale), rounded to dtype;
+    float32 array."""
+    rng = np.random.default_rng(seed)
+    K = 2 * heads * head_dim
+    return _cast(rng.standard_normal((d_model, K)) / np.sqrt(K), dtype)
+
+
+def make_gemm_operands(M: int, K: int, N: int, seed: int) -> tuple:
+    """x [M, K] ~ N(0, 1) and w [N, K] ~ N(0, 1/K), both rounded to bf16
+    (float32 arrays), for the projection product on its own."""
+    rng = np.random.default_rng(seed)
+    x = _cast(rng.standard_normal((M, K)), "bf16")
+    w = _cast(rng.standard_normal((N, K)) / np.sqrt(K), "bf16")
+    return x, w

@@ -16,10 +16,15 @@
 // k-contiguous) lets each lane own one token and store four consecutive
 // outputs at a time.  64-deep k steps stream through a two-stage LDS ring
 // with 16-byte direct-to-LDS loads (waves 0-3 move the w tile, 4-7 the x
-// tile); rows are 128 bytes with the 16-byte chunk c of row r stored at
-// c ^ ((r / 2) % 8), so sixteen lanes reading sixteen rows at one chunk hit
-// distinct bank groups.  XCD-aware tile order keeps the output tiles of one
-// token block on one XCD, whose L2 then serves that block's x to all of them.
+// tile); each wave's eight copies for the next step are spread between the
+// MFMAs of the first half of the current step (issued in one burst they hold
+// up the MFMA stream of every wave at once).  Rows are 128 bytes with the
+// 16-byte chunk c of row r stored at c ^ ((r / 2) % 8), so sixteen lanes
+// reading sixteen rows at one chunk hit distinct bank groups.  XCD-aware tile
+// order (consecutive tiles on one XCD) keeps the output tiles of one token
+// block on one XCD, whose L2 then serves that block's x to all of them.
+#include <type_traits>
+
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
@@ -44,9 +49,13 @@ proj_gemm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* _
   const int half = lane >> 5;
   const int mt_n = (int)((M + PBM - 1) / PBM), nt_n = (N + PBN - 1) / PBN;
   const int ntile = mt_n * nt_n;
-  int tid_ = blockIdx.x;
-  if ((ntile & 7) == 0) tid_ = (tid_ & 7) * (ntile >> 3) + (tid_ >> 3);
-  const int mt = sgpr(tid_ / nt_n), nt = sgpr(tid_ % nt_n);
+  // workgroup b runs on XCD b % 8: give XCD x a contiguous range of tiles
+  int t = blockIdx.x;
+  {
+    const int q = ntile >> 3, r = ntile & 7, xc = t & 7, k = t >> 3;
+    t = xc * q + (xc < r ? xc : r) + k;
+  }
+  const int mt = sgpr(t / nt_n), nt = sgpr(t % nt_n);
   const long m0 = (long)mt * PBM;
   const int n0 = nt * PBN;
 
@@ -65,12 +74,6 @@ proj_gemm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* _
     const long grow = xw ? (m0 + r < M ? m0 + r : M - 1) : (long)(n0 + r < N ? n0 + r : N - 1);
     src[i] = (xw ? x : w) + grow * K + ch * 8;
   }
-  auto issue = [&](int kt, int stg) {
-    char VDN_LDS* tb = lds + stg * STAGE + (xw ? TILEB : 0);
-#pragma unroll
-    for (int i = 0; i < NIW; ++i) g2lds16(src[i] + kt * PBK, tb + (i * 4 + (wv & 3)) * 1024);
-  };
-
   // Read bases: row r, logical chunk 2j + half sits at physical
   // (2j + half) ^ ((r / 2) % 8) = 2j ^ yv, yv = half ^ ((r / 2) % 8); the 32-row
   // blocks of a wave add multiples of 4 KB (immediate offsets).
@@ -87,12 +90,20 @@ proj_gemm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* _
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int nk = K / PBK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // own copies of step kt
-    __syncthreads();                                     // everyone's; step kt-1 done
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+  {
+    char VDN_LDS* tb = lds + (xw ? TILEB : 0);
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) g2lds16(src[i], tb + (i * 4 + (wv & 3)) * 1024);
+  }
+  // One k step: wait for this wave's copies, barrier (everyone's copies are in
+  // and everyone is done with the other stage), then 4 x 8 MFMAs, with the
+  // copies of the next step (when there is one) after every second MFMA of the
+  // first two 16-deep slices.
+  auto step = [&](int kt, auto more) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const char VDN_LDS* st = lds + (kt & 1) * STAGE;
+    char VDN_LDS* tbw = lds + ((kt + 1) & 1) * STAGE + (xw ? TILEB : 0);
 #pragma unroll
     for (int ks = 0; ks < PBK / 16; ++ks) {
       const int ro = rbase ^ (32 * ks);
@@ -102,11 +113,19 @@ proj_gemm_kernel(const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* _
 #pragma unroll
       for (int j = 0; j < 2; ++j) bfv[j] = *(const bf16x8 VDN_LDS*)(st + boff + j * 32 * ROWB + ro);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
+      for (int mi = 0; mi < 8; ++mi) {
+        acc[mi >> 1][mi & 1] = mfma32(af[mi >> 1], bfv[mi & 1], acc[mi >> 1][mi & 1]);
+        if constexpr (decltype(more)::value) {
+          if (ks < 2 && (mi & 1)) {
+            const int i = ks * 4 + (mi >> 1);
+            g2lds16(src[i] + (kt + 1) * PBK, tbw + (i * 4 + (wv & 3)) * 1024);
+          }
+        }
+      }
     }
-  }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::true_type{});
+  step(nk - 1, std::false_type{});
 
   // acc[i][j][e]: y^T[n][m] with n = n0 + wn*128 + 32 i + 8 (e / 4) + 4 half +
   // e % 4 and m = m0 + wm*64 + 32 j + lane % 32: four consecutive n per group.

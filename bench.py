@@ -8,7 +8,10 @@ factor, scan, then the block-sparse softmax with the merge fused into its
 epilogue) on synthetic inputs already resident in HBM.  Prints one JSON line:
 layer throughput in video tokens/s, the roofline of the dominant kernel (the
 fused softmax + merge stage, timed alone with HIP events on its stream), and
-the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload.  It also times
+the layer followed by the two branches' separate output projections
+(d_model = H*d), the projection product alone, and the library matmul on the
+same operands for comparison.
 """
 from __future__ import annotations
 
@@ -122,6 +125,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="768p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-proj", action="store_true",
+                    help="skip the layer-with-output-projections timing")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -198,6 +203,56 @@ def main():
     torch.cuda.synchronize()
     k1_ms = e0.elapsed_time(e1) / args.steps
 
+    # the step after the layer: both gated branches through their own output
+    # projections (d_model = H*d), as one product (bf16 layouts only)
+    proj = None
+    if w.dtype == "bf16" and not args.no_proj:
+        H, d = w.heads, w.head_dim
+        dm = H * d
+        w_o = torch.from_numpy(synth.make_proj_weight(dm, H, d, seed=w.seed + 1)).to(tdt).cuda()
+        pws = torch.empty(V.proj_workspace_size(lay), dtype=torch.uint8, device="cuda")
+        y = torch.empty((w.batch, w.video_tokens, dm), dtype=tdt, device="cuda")
+        x2 = V.softmax_branches_fwd(dev["q"], dev["k"], dev["v"], tk, tv, R, dev["gate_logits"],
+                                    **geo, workspace=sws).view(w.batch * w.video_tokens, 2 * H * d)
+        y2 = torch.empty((w.batch * w.video_tokens, dm), dtype=tdt, device="cuda")
+
+        def layer_proj():
+            V.hybrid_attn_proj(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"],
+                               dev["gate_logits"], w_o, **geo, out=y, workspace=pws)
+
+        def product():
+            V.out_proj(x2, w_o, out=y2)
+
+        wt = w_o.t().contiguous()
+
+        def library_product():
+            torch.matmul(x2, wt, out=y2)
+
+        def timed(fn, n):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        print("[bench] layer with output projections", file=sys.stderr, flush=True)
+        lp_ms = timed(layer_proj, args.steps)
+        pr_ms = timed(product, args.steps)
+        lib_ms = timed(library_product, args.steps)
+        pflops = 2.0 * w.batch * w.video_tokens * (2 * H * d) * dm
+        proj = {"d_model": dm, "layer_with_proj_ms": round(lp_ms, 4),
+                "video_tokens_per_s": round(w.batch * w.video_tokens / (lp_ms / 1e3), 1),
+                "proj_kernel": "proj_gemm_kernel (bf16, 256x256 tiles)",
+                "proj_ms": round(pr_ms, 4),
+                "proj_tflops": round(pflops / (pr_ms / 1e3) / 1e12, 1),
+                "proj_frac": round(pflops / (pr_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "library_matmul_ms": round(lib_ms, 4)}
+        del pws, y, y2, x2, w_o, wt
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -228,12 +283,13 @@ def main():
                                f"T={w.frames} P={w.tokens_per_frame} L={w.text_tokens} "
                                f"chunk={w.chunk_frames} window=+-{w.window_chunks}",
                    "video_tokens": video_tokens, "parallelism": "single GPU"},
-        "roofline": {"kernel": "softmax_vt_kernel<128, fused merge> (+ vt_transpose pre-pass)",
+        "roofline": {"kernel": "softmax_vt_kernel<128, 1> (merge fused; + vt_transpose pre-pass)",
                      "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": k1_flops, "ms_per_launch": round(k1_ms, 4)},
         "wall_s_timed_region": round(wall, 3),
+        "output_projections": proj,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -203,6 +203,40 @@ vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* ---- Backward pass ---- */
+
+/* Bytes of workspace vdn_hybrid_attn_bwd needs (0 if the layout is invalid).
+ * Host only. */
+size_t vdn_hybrid_attn_bwd_workspace_size(const vdn_layout_t* layout);
+
+/* Gradients of the layer (the vector-Jacobian product with dO, the gradient
+ * of the loss with respect to O): with the same inputs as
+ * vdn_hybrid_attn_fwd and dO [B, T*P, H, d] (layout->dtype), writes
+ *   dq, dk, dv        [B, T*P, H, d]   float32
+ *   dtext_k, dtext_v  [B, L, H, d]     float32 (may be NULL when L == 0)
+ *   dbeta             [B, T*P + L, H]  float32 (zero for tokens of frames no
+ *                                      state folds)
+ *   dalpha            [B, T, H]        float32 (zero for frames no state folds)
+ *   dgate_logits      [B, T*P, H, 2]   float32
+ * The forward is recomputed inside (the VDA statistics, factor and scan,
+ * keeping every scan state, and the softmax with the merge backward in its
+ * epilogue); nothing from a previous forward call is needed.  Covers bf16
+ * layouts with d in {32, 64, 128} and P, L multiples of 8; else
+ * VDN_ERR_UNSUPPORTED.  workspace: at least
+ * vdn_hybrid_attn_bwd_workspace_size(layout) bytes, 256-byte aligned.
+ * Outputs must not alias inputs or each other.  The gradient of the softmax
+ * branch is the standard attention backward over each query's visible keys;
+ * that of the linear branch runs the scan in reverse (PaperDaily §三/§四 and
+ * the deepmagic closed form define the forward it differentiates). */
+vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v,
+                                 const void* text_k, const void* text_v,
+                                 const float* beta, const float* alpha,
+                                 const float* gate_logits, const void* dO,
+                                 const vdn_layout_t* layout, float* dq, float* dk,
+                                 float* dv, float* dtext_k, float* dtext_v, float* dbeta,
+                                 float* dalpha, float* dgate_logits, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* Frame statistics: for every frame f < T and for the text block (slot T),
  * A[b,h,slot] = sum_i beta_i k_i k_i^T and B[b,h,slot] = sum_i beta_i v_i k_i^T
  * over the slot's tokens.  A_out, B_out: float32 [B, H, T+1, d, d] (row index

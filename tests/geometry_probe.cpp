@@ -22,6 +22,13 @@ int main(int argc, char** argv) {
     printf("\n");
   }
   for (int c = 0; c < g.nc; ++c) printf("win %d %d %d\n", c, vdn::win_lo(g, c), vdn::win_hi(g, c));
+  for (int dir = 0; dir < 2; ++dir) {
+    printf("fold %d", dir);
+    for (int f = 0; f < g.T; ++f) printf(" %d", vdn::fold_index(g, dir, f));
+    printf("\nsnap %d", dir);
+    for (int c = 0; c < g.nc; ++c) printf(" %d", vdn::snap_index(g, dir, c));
+    printf("\n");
+  }
   int ns = vdn::count_slots(g, false);
   printf("slots");
   for (int i = 0; i < ns; ++i) printf(" %d", vdn::slot_of(g, i, false));

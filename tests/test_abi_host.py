@@ -156,6 +156,7 @@ def test_kernel_geometry_matches_oracle(geometry_probe, C, w):
                        chunk_frames=C, window_chunks=w, anchor_first=bool(af), anchor_last=bool(al))
         segs = {}
         slots = None
+        fold = {}
         for ln in lines:
             f = ln.split()
             if not f:
@@ -165,12 +166,29 @@ def test_kernel_geometry_matches_oracle(geometry_probe, C, w):
                 segs[int(f[1])] = [tuple(vals[i:i + 2]) for i in range(0, len(vals), 2)]
             elif f[0] == "slots":
                 slots = list(map(int, f[1:]))
+            elif f[0] in ("fold", "snap"):
+                fold.setdefault(f[0], {})[int(f[1])] = list(map(int, f[2:]))
         for t in range(T):
             assert segs[t] == _segments_from_oracle(lay, t), (T, C, w, af, al, t)
         # frames whose statistics the scans need = union of the far sets
         needed = sorted(set().union(*[set(O.far_forward(lay, t)) | set(O.far_backward(lay, t))
                                       for t in range(T)]))
         assert slots == needed + [T], (T, C, w, af, al)
+        # backward pass: each chain's fold order, and the state each chunk's
+        # snapshot holds = the chunk's far frames, a prefix of that order
+        for dr in (0, 1):
+            idx = fold["fold"][dr]
+            order = sorted((j, f) for f, j in enumerate(idx) if j > 0)
+            order = [f for _, f in order]
+            assert [j for j, _ in sorted((j, f) for f, j in enumerate(idx) if j > 0)] == \
+                list(range(1, len(order) + 1))
+            assert order == (sorted(order) if dr == 0 else sorted(order, reverse=True))
+            for c in range(lay.num_chunks):
+                qf = [t for t in range(c * C, min((c + 1) * C, T)) if t not in O.anchor_frames(lay)]
+                if not qf:
+                    continue
+                far = O.far_forward(lay, qf[0]) if dr == 0 else O.far_backward(lay, qf[0])
+                assert order[:fold["snap"][dr][c]] == far, (T, C, w, af, al, dr, c)
 
 
 def test_projection_entry_points_reject_bad_arguments_before_launch():

@@ -1,0 +1,96 @@
+"""GPU parity of the backward pass (vdn_hybrid_attn_bwd, through the C ABI)
+against the backward oracle (oracle.vdn_oracle_grad) on the same seeded
+inputs and upstream gradient.
+
+Metric: relative Frobenius error per gradient tensor.  Bound 2e-2 (the bf16
+layer tolerance): the gradients run through the same bf16 roundings as the
+forward (P, the scan's three-pass products) plus bf16 dO_s and dS operands.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import vdn_oracle_grad as G
+from video_diffusion_hybrid_block_amd import binding as V
+from video_diffusion_hybrid_block_amd import synth
+
+from _helpers import custom, oracle_layout, rel_err, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+CASES = [
+    # far frames on both sides, anchors, text; two 256-query tiles per frame
+    dict(name="bwd_d64", batch=1, heads=2, head_dim=64, frames=12, tokens_per_frame=104,
+         text_tokens=16, dtype="bf16", chunk_frames=3),
+    # d = 128, batch 2, 128-key tiles with a ragged tail, text
+    dict(name="bwd_d128_b2", batch=2, heads=2, head_dim=128, frames=7, tokens_per_frame=136,
+         text_tokens=24, dtype="bf16", chunk_frames=2),
+    # d = 32, no text (states start at zero), partial last chunk
+    dict(name="bwd_d32_notext", batch=1, heads=3, head_dim=32, frames=10, tokens_per_frame=40,
+         text_tokens=0, dtype="bf16", chunk_frames=3),
+    # the linear branch gated off (sigmoid(-30)): dq, dk, dv are the softmax
+    # backward alone
+    dict(name="bwd_softmax_only", batch=1, heads=2, head_dim=128, frames=9, tokens_per_frame=72,
+         text_tokens=16, dtype="bf16", chunk_frames=2, gates=(4.0, -30.0)),
+    # the softmax branch gated off: the linear branch's gradients alone
+    dict(name="bwd_linear_only", batch=1, heads=2, head_dim=64, frames=13, tokens_per_frame=48,
+         text_tokens=8, dtype="bf16", chunk_frames=2, gates=(-30.0, 4.0)),
+    # one frame: every query is an anchor query, no far frames, no text
+    dict(name="bwd_one_frame", batch=1, heads=2, head_dim=64, frames=1, tokens_per_frame=200,
+         text_tokens=0, dtype="bf16"),
+    # window wider than the video: dense softmax, linear read = text write
+    dict(name="bwd_dense_window", batch=1, heads=1, head_dim=128, frames=9, tokens_per_frame=48,
+         text_tokens=16, dtype="bf16", chunk_frames=2, window_chunks=5),
+    dict(name="bwd_no_anchors", batch=1, heads=2, head_dim=64, frames=12, tokens_per_frame=40,
+         text_tokens=8, dtype="bf16", chunk_frames=3, anchor_first=False, anchor_last=False),
+    dict(name="bwd_last_anchor_only", batch=1, heads=1, head_dim=32, frames=14, tokens_per_frame=24,
+         text_tokens=8, dtype="bf16", chunk_frames=2, anchor_first=False),
+]
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_backward_matches_oracle(case):
+    require_gpu()
+    case = dict(case)
+    af = case.pop("anchor_first", True)
+    al = case.pop("anchor_last", True)
+    gates = case.pop("gates", None)
+    w = custom(**case)
+    _announce(f"backward {case['name']}")
+    inp = synth.make_inputs(w)
+    if gates is not None:
+        inp["gate_logits"][..., 0] += gates[0]
+        inp["gate_logits"][..., 1] += gates[1]
+    lay = oracle_layout(w, anchor_first=af, anchor_last=al)
+    dO = synth.round_bf16(np.random.default_rng(w.seed + 7).standard_normal(inp["q"].shape))
+    ref = G.hybrid_attn_grad({k_: np.asarray(a, np.float64) for k_, a in inp.items()}, lay, dO)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    got = V.hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+                            dev["text_v"] if L else None, dev["beta"], dev["alpha"],
+                            dev["gate_logits"], torch.from_numpy(dO).to(torch.bfloat16).cuda(),
+                            frames=w.frames, tokens_per_frame=w.tokens_per_frame,
+                            chunk_frames=w.chunk_frames, window_chunks=w.window_chunks,
+                            anchor_first=af, anchor_last=al)
+    torch.cuda.synchronize()
+    errs = {}
+    for key in G.GRAD_KEYS:
+        if got.get(key) is None:
+            continue
+        g = got[key].cpu().numpy()
+        assert np.isfinite(g).all(), key
+        if np.linalg.norm(ref[key]) < 1e-30:
+            # no gradient at all (e.g. alpha and beta with no folded frame)
+            errs[key] = float(np.abs(g).max())
+            continue
+        errs[key] = rel_err(g, ref[key])
+    print(case["name"], " ".join(f"{k_} {e:.2e}" for k_, e in errs.items()), flush=True)
+    bad = {k_: e for k_, e in errs.items() if not e <= TOL}
+    assert not bad, bad

@@ -17,7 +17,8 @@ __all__ = [
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
     "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "vda_gram", "vda_factor_scan",
-    "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "make_layout",
+    "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
+    "bwd_workspace_size", "make_layout",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -34,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "vdn_vda_factor_scan_workspace_size",
     "vdn_vda_factor_scan", "vdn_merge", "vdn_softmax_branches_fwd", "vdn_out_proj",
     "vdn_hybrid_attn_proj_workspace_size", "vdn_hybrid_attn_proj_fwd",
+    "vdn_hybrid_attn_bwd_workspace_size", "vdn_hybrid_attn_bwd",
 )
 
 
@@ -108,6 +110,10 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_proj_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                                lp, vp, vp, sz, vp]
         L.vdn_hybrid_attn_proj_fwd.restype = ctypes.c_int
+        L.vdn_hybrid_attn_bwd_workspace_size.argtypes = [lp]
+        L.vdn_hybrid_attn_bwd_workspace_size.restype = sz
+        L.vdn_hybrid_attn_bwd.argtypes = [vp] * 9 + [lp] + [vp] * 9 + [sz, vp]
+        L.vdn_hybrid_attn_bwd.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -360,6 +366,48 @@ def hybrid_attn_proj(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_o, *, 
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vdn_hybrid_attn_proj_fwd")
     return out
+
+
+def bwd_workspace_size(layout: Layout) -> int:
+    return lib().vdn_hybrid_attn_bwd_workspace_size(ctypes.byref(layout))
+
+
+def hybrid_attn_bwd(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, *, frames,
+                    tokens_per_frame, chunk_frames=5, window_chunks=1, anchor_first=True,
+                    anchor_last=True, softmax_scale=0.0, rms_eps=0.0, workspace=None) -> dict:
+    """Gradients of the layer (``vdn_hybrid_attn_bwd``) given dO, the
+    gradient of the loss with respect to O (dtype and shape of q).  Returns a
+    dict of float32 tensors shaped like the inputs: q, k, v, text_k, text_v
+    (None without text), beta, alpha, gate_logits."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    _expect(dO, q.shape, q.dtype, "dO")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"q": torch.empty(q.shape, **f32), "k": torch.empty(q.shape, **f32),
+         "v": torch.empty(q.shape, **f32),
+         "text_k": torch.empty((B, L, H, d), **f32) if L else None,
+         "text_v": torch.empty((B, L, H, d), **f32) if L else None,
+         "beta": torch.empty((B, N + L, H), **f32), "alpha": torch.empty((B, frames, H), **f32),
+         "gate_logits": torch.empty((B, N, H, 2), **f32)}
+    need = bwd_workspace_size(lay)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().vdn_hybrid_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(dO), ctypes.byref(lay), _ptr(g["q"]),
+        _ptr(g["k"]), _ptr(g["v"]), _ptr(g["text_k"]), _ptr(g["text_v"]), _ptr(g["beta"]),
+        _ptr(g["alpha"]), _ptr(g["gate_logits"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_bwd")
+    return g
 
 
 def vda_gram(k, v, text_k, text_v, beta, *, frames, tokens_per_frame, chunk_frames=5,

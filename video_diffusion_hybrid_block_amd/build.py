@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libvdn.so")
 ARCH = os.environ.get("VDN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "k_softmax.hip", "k_gram.hip", "k_factor.hip", "k_scan.hip", "k_merge.hip",
-           "k_proj.hip"]
+           "k_proj.hip", "k_attn_bwd.hip", "k_vda_bwd.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",

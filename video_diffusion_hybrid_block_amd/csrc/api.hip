@@ -248,6 +248,35 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
 
 namespace {
 
+// Backward-pass workspace: the forward plan, then the per-step states and
+// their gradients, the read-slot gradients, transposed copies and the merge
+// backward's outputs.
+struct BwdPlan {
+  size_t states, dspost, dR, kt, qt, dost, dos, dlin, lse, dvec, total;
+};
+
+BwdPlan make_bwd_plan(const vdn_layout_t& l) {
+  const Plan p = make_plan(l);
+  const Geo g = make_geo(l);
+  const size_t d = (size_t)l.head_dim_k, bh = (size_t)l.batch * l.heads;
+  const size_t N = (size_t)g.T * g.P;
+  const size_t mat = d * d * sizeof(float);
+  const size_t nl8 = (N + g.L + 7) / 8 * 8, nq8 = (N + 7) / 8 * 8;
+  BwdPlan b;
+  b.states = p.total;
+  b.dspost = align256(b.states + bh * 2 * (g.T + 1) * mat);
+  b.dR = align256(b.dspost + bh * 2 * (g.T + 1) * mat);
+  b.kt = align256(b.dR + bh * (g.nc + 1) * mat);
+  b.qt = align256(b.kt + bh * d * nl8 * 2);
+  b.dost = align256(b.qt + bh * d * nq8 * 2);
+  b.dos = align256(b.dost + bh * d * nq8 * 2);
+  b.dlin = align256(b.dos + (size_t)l.batch * N * l.heads * d * 2);
+  b.lse = align256(b.dlin + (size_t)l.batch * N * l.heads * d * 4);
+  b.dvec = align256(b.lse + bh * N * 4);
+  b.total = align256(b.dvec + bh * N * 4);
+  return b;
+}
+
 // x2 (the gated branches, bf16 [B, T*P, 2, H, d]) follows the layer's plan.
 size_t proj_x2_off(const vdn_layout_t& l) { return make_plan(l).total; }
 size_t proj_ws_total(const vdn_layout_t& l) {
@@ -263,6 +292,82 @@ bool proj_layer_ok(const vdn_layout_t& l, int32_t d_model) {
 }  // namespace
 
 extern "C" {
+
+size_t vdn_hybrid_attn_bwd_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return make_bwd_plan(*layout).total;
+}
+
+vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, const void* text_k,
+                                 const void* text_v, const float* beta, const float* alpha,
+                                 const float* gate_logits, const void* dO,
+                                 const vdn_layout_t* layout, float* dq, float* dk, float* dv,
+                                 float* dtext_k, float* dtext_v, float* dbeta, float* dalpha,
+                                 float* dgate_logits, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  const vdn_layout_t& l = *layout;
+  if (!softmax_merge_fusable(l)) return VDN_ERR_UNSUPPORTED;
+  const bool txt = l.text_tokens > 0;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !dO || !dq || !dk || !dv || !dbeta ||
+      !dalpha || !dgate_logits || !workspace || !text_ok(l, text_k, text_v) ||
+      (txt && (!dtext_k || !dtext_v)))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(dbeta) || !aligned16(dalpha) || !aligned16(dgate_logits) ||
+      !aligned16(workspace) || !text_aligned(text_k, text_v) ||
+      (dtext_k && !aligned16(dtext_k)) || (dtext_v && !aligned16(dtext_v)))
+    return VDN_ERR_MISALIGNED;
+  const BwdPlan bp = make_bwd_plan(l);
+  if (workspace_bytes < bp.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  const Plan p = make_plan(l);
+  char* ws = (char*)workspace;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* Sf = (float*)(ws + p.sf_off);
+  float* Sb = (float*)(ws + p.sb_off);
+  float* R = (float*)(ws + p.r_off);
+  float* states = (float*)(ws + bp.states);
+  float* dspost = (float*)(ws + bp.dspost);
+  float* dR = (float*)(ws + bp.dR);
+  __bf16* dos = (__bf16*)(ws + bp.dos);
+  float* dlin = (float*)(ws + bp.dlin);
+  float* lse = (float*)(ws + bp.lse);
+  float* dvec = (float*)(ws + bp.dvec);
+  const Geo g = make_geo(l);
+  const int N = g.T * g.P;
+  // forward recomputation: statistics, factor, scan (keeping every state)
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream, states);
+  // softmax forward with the merge backward in its epilogue
+  const MergeBwdIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, lse};
+  if (e == hipSuccess)
+    e = launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                 eff_eps(l), io, ws + p.vt_off, stream);
+  // transposed copies for the softmax backward
+  if (e == hipSuccess)
+    e = launch_transpose(k, text_k, l.batch, l.heads, l.head_dim_k, N, g.L, ws + bp.kt, stream);
+  if (e == hipSuccess)
+    e = launch_transpose(q, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.qt, stream);
+  if (e == hipSuccess)
+    e = launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream);
+  // linear branch: dq (its part), dA over G, dB over B, dalpha
+  if (e == hipSuccess)
+    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states, dR, dspost,
+                       dq, dk, dv, dtext_k, dtext_v, dbeta, dalpha, l, stream);
+  // softmax branch: dq (added), dk, dv, dtext_k, dtext_v (written)
+  if (e == hipSuccess)
+    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
+                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
+  // statistics: dk, dv, dtext_k, dtext_v (added), dbeta (written)
+  if (e == hipSuccess)
+    e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
+                        stream);
+  return hip_status(e);
+}
 
 size_t vdn_hybrid_attn_proj_workspace_size(const vdn_layout_t* layout) {
   if (check_layout(layout) != VDN_OK) return 0;

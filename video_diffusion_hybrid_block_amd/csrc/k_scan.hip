@@ -47,7 +47,7 @@ template <int D>
 __global__ void __launch_bounds__(2 * D)
 scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
                  const float* __restrict__ alpha, float* __restrict__ Sf, float* __restrict__ Sb,
-                 Geo g, int H) {
+                 Geo g, int H, float* __restrict__ states) {
   constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
   constexpr int NT = 64 * NRB;
   constexpr int LDF = D;                // fp32 state row stride (floats)
@@ -176,6 +176,16 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
     float* dst = snap + (size_t)c * mat + (size_t)row0 * D;
     for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
   };
+  // Backward pass only: the state after every step j of the chain (j = 0: the
+  // start, half the text write), [B*H][2][T+1][d][d].
+  float* st_base = states ? states + ((size_t)bh * 2 + dir) * (g.T + 1) * mat + (size_t)row0 * D
+                          : nullptr;
+  int nstep = 0;
+  auto keep = [&]() {
+    if (!st_base) return;
+    float* dst = st_base + (size_t)nstep * mat;
+    for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
+  };
 
   // Step sequence: the text write (slot T, a = 0, times 1/2) when there is
   // text, then the frames the chain folds.  Step k uses LDS buffer k & 1; the
@@ -188,7 +198,10 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   }
   for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
   __syncthreads();
-  if (!text) snapshot(g.nc);
+  if (!text) {
+    snapshot(g.nc);
+    keep();
+  }
   int c = dir == 0 ? 0 : g.nc - 1;
   int bi = 0;
   while (slot >= 0) {
@@ -210,6 +223,8 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
     }
     step(text ? 0.0f : al[(size_t)slot * H], text ? 0.5f : 1.0f, bi);
     if (text) snapshot(g.nc);
+    else ++nstep;
+    keep();
 #pragma unroll
     for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
     bi ^= 1;
@@ -221,6 +236,173 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   } else {
     while (c >= 0) snapshot(c--);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass of the scan.  A chain folds frames f_1, f_2, ..., f_n (fold
+// order) from S_0: S_j = (alpha_j S_{j-1} + B_j) G_j.  With dS_j the gradient
+// of the loss with respect to S_j (from the snapshots that read S_j and from
+// step j + 1):
+//   dS_{j-1} = alpha_j (dS_j G_j) + (gradients of the snapshots of S_{j-1}),
+// and dS_0 also takes the anchors' read of the start state (slot nc).  Every
+// dS_j is kept (dspost, [B*H][2][T+1][d][d]); the per-frame gradients of
+// B_j, G_j and alpha_j follow from dS_j, G_j and S_{j-1} frame by frame.
+// Same layout as the forward scan: d/32 workgroups of 32 rows per chain,
+// dS_j G_j on MFMA with the three-pass bf16 split, G_j staged through LDS.
+// ---------------------------------------------------------------------------
+
+// Frame folded just before f in the chain's fold order (-1 if none); f = -1
+// asks for the last frame the chain folds.
+__device__ __forceinline__ int prev_frame(const Geo& g, int dir, int f) {
+  if (dir == 0) {
+    int n = f < 0 ? fwd_scan_end(g) - 1 : f - 1;
+    while (n >= 0 && is_anchor(g, n)) --n;
+    return n;
+  }
+  const int fbeg = bwd_scan_begin(g);
+  int n = f < 0 ? fbeg + 1 : f + 1;
+  while (n < g.T && is_anchor(g, n)) ++n;
+  return n < g.T ? n : -1;
+}
+
+template <int D>
+__global__ void __launch_bounds__(2 * D)
+scan_bwd_kernel(const float* __restrict__ G, const float* __restrict__ dR,
+                const float* __restrict__ alpha, float* __restrict__ dspost, Geo g, int H) {
+  constexpr int NRB = D / 32;
+  constexpr int NT = 64 * NRB;
+  constexpr int LDF = D;
+  constexpr int NCH = 32 * D / 8 / NT;
+  constexpr int CPR = D / 4;
+  constexpr int GBYTES = D * D * 4;
+  constexpr int NGI = GBYTES / 1024 / NRB;
+  __shared__ __attribute__((aligned(1024))) char gbuf[2 * GBYTES];
+  __shared__ __attribute__((aligned(16))) float S[32 * LDF];
+  __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
+  __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
+  char VDN_LDS* Gl = (char VDN_LDS*)gbuf;
+  char VDN_LDS* Xh = (char VDN_LDS*)xh;
+  char VDN_LDS* Xl = (char VDN_LDS*)xl;
+  auto gsw = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  int wid = blockIdx.x;
+  if (gridDim.x % (8 * NRB) == 0) wid = (wid & 7) * (gridDim.x >> 3) + (wid >> 3);
+  const int rb = wid % NRB;
+  const int chain = wid / NRB;
+  const int dir = chain & 1;
+  const int bh = chain >> 1;
+  const int b = bh / H, h = bh % H;
+  const int row0 = rb * 32;
+  const size_t mat = (size_t)D * D;
+  const float* Gbh = G + (size_t)bh * (g.T + 1) * mat;
+  const float* dRbh = dR + (size_t)bh * (g.nc + 1) * mat + (size_t)row0 * D;
+  float* post = dspost + ((size_t)bh * 2 + dir) * (g.T + 1) * mat + (size_t)row0 * D;
+  const float* al = alpha + (size_t)b * g.T * H + h;
+
+  auto copy_g = [&](int slot, int bi) {
+    const float* Gs = Gbh + (size_t)slot * mat;
+#pragma unroll
+    for (int i = 0; i < NGI; ++i) {
+      const int blk = wv * NGI + i;
+      const int sl = blk * 64 + lane;
+      const int row = sl / CPR;
+      const int ch = (sl % CPR) ^ gsw(row);
+      g2lds16(Gs + (size_t)row * D + ch * 4, Gl + bi * GBYTES + blk * 1024);
+    }
+  };
+  // dS rows += the gradient of chunk snapshot slot c.
+  auto add_slot = [&](int c) {
+    const float* src = dRbh + (size_t)c * mat;
+    for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] += src[i];
+  };
+  // ... for every chunk whose snapshot holds state j
+  auto inject = [&](int j) {
+    for (int c = 0; c < g.nc; ++c)
+      if (snap_index(g, dir, c) == j) add_slot(c);
+  };
+  auto keep = [&](int j) {
+    float* dst = post + (size_t)j * mat;
+    for (int i = tid; i < 32 * D; i += NT) dst[i] = S[(i / D) * LDF + i % D];
+  };
+  // dS <- a * (dS G), G from LDS buffer bi.
+  auto step = [&](float a, int bi) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + i * NT;
+      const int r = q / (D / 8), c = (q % (D / 8)) * 8;
+      const f32x4 s0 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c);
+      const f32x4 s1 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c + 4);
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hi, lo;
+        split_bf16(sv[e], hi, lo);
+        hv[e] = hi;
+        lv[e] = lo;
+      }
+      const int off = swz_off<D>(r, c);
+      *(bf16x8 VDN_LDS*)(Xh + off) = hv;
+      *(bf16x8 VDN_LDS*)(Xl + off) = lv;
+    }
+    __syncthreads();
+    const int n = wv * 32 + (lane & 31);
+    const int x = gsw(n);
+    const char VDN_LDS* grow = Gl + bi * GBYTES + n * (4 * D);
+    f32x16 acc = f32x16{}, acc1 = f32x16{}, acc2 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int c0 = 4 * ks + 2 * half;
+      const f32x4 g0 = *(const f32x4 VDN_LDS*)(grow + ((c0 ^ x) << 4));
+      const f32x4 g1 = *(const f32x4 VDN_LDS*)(grow + (((c0 + 1) ^ x) << 4));
+      const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      bf16x8 gh, gl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 a_, c_;
+        split_bf16(gv[e], a_, c_);
+        gh[e] = a_;
+        gl[e] = c_;
+      }
+      const bf16x8 ah = lds_row8<D>(Xh, lane & 31, ks * 2 + half);
+      const bf16x8 alo = lds_row8<D>(Xl, lane & 31, ks * 2 + half);
+      acc = mfma32(ah, gh, acc);
+      acc1 = mfma32(ah, gl, acc1);
+      acc2 = mfma32(alo, gh, acc2);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = (j >> 2) * 8 + half * 4 + (j & 3);
+      S[r * LDF + wv * 32 + (lane & 31)] = (acc[j] + (acc1[j] + acc2[j])) * a;
+    }
+    __syncthreads();
+  };
+
+  int f = prev_frame(g, dir, -1);
+  int j = f >= 0 ? fold_index(g, dir, f) : 0;   // number of steps
+  for (int i = tid; i < 32 * D; i += NT) S[(i / D) * LDF + i % D] = 0.f;
+  __syncthreads();
+  inject(j);
+  if (f >= 0) copy_g(f, 0);
+  __syncthreads();
+  int bi = 0;
+  while (f >= 0) {
+    keep(j);
+    const int pf = prev_frame(g, dir, f);
+    wait_vmem();
+    __syncthreads();                     // G_f landed everywhere; buffer bi^1 free
+    if (pf >= 0) copy_g(pf, bi ^ 1);
+    step(al[(size_t)f * H], bi);
+    --j;
+    inject(j);
+    __syncthreads();
+    bi ^= 1;
+    f = pf;
+  }
+  add_slot(g.nc);                        // j == 0 here: the anchors' read of S_0
+  keep(0);
 }
 
 // Plain fp32 path: one workgroup per (batch, head, direction), whole state.
@@ -295,15 +477,16 @@ combine_kernel(const float4* __restrict__ Sf, const float4* __restrict__ Sb, flo
 
 template <int D>
 hipError_t launch_d(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
-                    float* Sf, float* Sb, float* R, hipStream_t s) {
+                    float* Sf, float* Sb, float* R, float* states, hipStream_t s) {
   Geo g = make_geo(l);
   long chains = (long)l.batch * l.heads * 2;
   if (l.dtype == VDN_BF16 && D >= 32) {
     if constexpr (D >= 32) {
       scan_mfma_kernel<D><<<dim3((unsigned)(chains * (D / 32))), dim3(2 * D), 0, s>>>(
-          G, B, alpha, Sf, Sb, g, l.heads);
+          G, B, alpha, Sf, Sb, g, l.heads, states);
     }
   } else {
+    if (states) return hipErrorNotSupported;
     scan_valu_kernel<D><<<dim3((unsigned)chains), dim3(256), 0, s>>>(G, B, alpha, Sf, Sb, g,
                                                                       l.heads);
   }
@@ -316,17 +499,41 @@ hipError_t launch_d(const float* G, const float* B, const float* alpha, const vd
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_bwd_d(const float* G, const float* dR, const float* alpha,
+                        const vdn_layout_t& l, float* dspost, hipStream_t s) {
+  if constexpr (D < 32) {
+    return hipErrorNotSupported;
+  } else {
+    Geo g = make_geo(l);
+    long chains = (long)l.batch * l.heads * 2;
+    scan_bwd_kernel<D><<<dim3((unsigned)(chains * (D / 32))), dim3(2 * D), 0, s>>>(
+        G, dR, alpha, dspost, g, l.heads);
+    return hipGetLastError();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
-                       float* Sf, float* Sb, float* R, hipStream_t s) {
+                       float* Sf, float* Sb, float* R, hipStream_t s, float* states) {
   switch (l.head_dim_k) {
-    case 128: return launch_d<128>(G, B, alpha, l, Sf, Sb, R, s);
-    case 64: return launch_d<64>(G, B, alpha, l, Sf, Sb, R, s);
-    case 32: return launch_d<32>(G, B, alpha, l, Sf, Sb, R, s);
-    case 16: return launch_d<16>(G, B, alpha, l, Sf, Sb, R, s);
+    case 128: return launch_d<128>(G, B, alpha, l, Sf, Sb, R, states, s);
+    case 64: return launch_d<64>(G, B, alpha, l, Sf, Sb, R, states, s);
+    case 32: return launch_d<32>(G, B, alpha, l, Sf, Sb, R, states, s);
+    case 16: return launch_d<16>(G, B, alpha, l, Sf, Sb, R, states, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan_bwd(const float* G, const float* dR, const float* alpha,
+                           const vdn_layout_t& l, float* dspost, hipStream_t s) {
+  switch (l.head_dim_k) {
+    case 128: return launch_bwd_d<128>(G, dR, alpha, l, dspost, s);
+    case 64: return launch_bwd_d<64>(G, dR, alpha, l, dspost, s);
+    case 32: return launch_bwd_d<32>(G, dR, alpha, l, dspost, s);
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace vdn

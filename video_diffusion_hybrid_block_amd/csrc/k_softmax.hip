@@ -25,148 +25,13 @@
 //    of 8 each XCD gets a fixed set of heads so K/V tiles are shared in its L2.
 #include <type_traits>
 
+#include "softmax_common.h"
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
 namespace vdn {
 
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ int frame_in_order(const Geo& g, int vfr) {
-  int first = g.af ? 0 : -1;
-  int last = (g.al && !(g.af && g.T == 1)) ? g.T - 1 : -1;
-  int na = (first >= 0) + (last >= 0);
-  if (vfr < na) return (vfr == 0 && first >= 0) ? first : last;
-  return vfr - na + (g.af ? 1 : 0);
-}
-
-struct WorkItem {
-  int b, h, t, tile;
-};
-
-__device__ __forceinline__ WorkItem decode_work(const Geo& g, int B, int H, int tpf) {
-  int i = blockIdx.x;
-  int G = B * H;
-  int gi, rest;
-  if ((G & 7) == 0) {
-    int xcd = i & 7, j = i >> 3, gper = G >> 3;
-    gi = xcd * gper + j % gper;
-    rest = j / gper;
-  } else {
-    gi = i % G;
-    rest = i / G;
-  }
-  WorkItem w;
-  w.b = gi / H;
-  w.h = gi % H;
-  w.t = frame_in_order(g, rest / tpf);
-  w.tile = rest % tpf;
-  return w;
-}
-
-// Row permutation inside a 32-key block: MFMA row m holds key pi(m), so the
-// score registers of lane half h hold keys 8h..8h+7 and 16+8h..16+8h+7.
-__device__ __forceinline__ int perm32(int m) {
-  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
-struct KeyMap {
-  int s0, n0, s1, n1, s2, n2, nvid, nkeys;
-};
-
-__device__ __forceinline__ KeyMap key_map(const Geo& g, int t) {
-  int ss[3] = {0, 0, 0}, sl[3] = {0, 0, 0};
-  key_segments(g, t, ss, sl);
-  KeyMap m;
-  m.s0 = ss[0]; m.n0 = sl[0];
-  m.s1 = ss[1]; m.n1 = sl[1];
-  m.s2 = ss[2]; m.n2 = sl[2];
-  m.nvid = m.n0 + m.n1 + m.n2;
-  m.nkeys = m.nvid + g.L;
-  return m;
-}
-
-// Element offset of virtual key kv of (b, h) in the video or text tensor;
-// keys past the end are clamped to the first visible key (their scores are
-// masked).  Returns true when the key is a text key.
-__device__ __forceinline__ bool key_src(const KeyMap& m, int kv, int b, int h, int H, int N,
-                                        int L, int D, size_t& off) {
-  if (kv < m.nvid) {
-    int tok = kv < m.n0 ? m.s0 + kv : (kv < m.n0 + m.n1 ? m.s1 + kv - m.n0 : m.s2 + kv - m.n0 - m.n1);
-    off = ((size_t)(b * (size_t)N + tok) * H + h) * D;
-    return false;
-  }
-  if (kv < m.nkeys) {
-    off = ((size_t)(b * (size_t)L + (kv - m.nvid)) * H + h) * D;
-    return true;
-  }
-  off = ((size_t)(b * (size_t)N + m.s0) * H + h) * D;
-  return false;
-}
-
-// Branch-free form for the MFMA kernel: element offset (relative to the
-// head's base pointer, in units of H*D elements per token) and text flag.
-struct KeyAddr {
-  int e0, e1, e2, nkeys;   // ends of the three video segments and of the text
-  int d0, d1, d2;          // token = kv + d_seg inside video segment seg
-  int clamp_tok;
-};
-
-__device__ __forceinline__ KeyAddr key_addr(const KeyMap& m) {
-  KeyAddr a;
-  a.e0 = m.n0; a.e1 = m.n0 + m.n1; a.e2 = m.nvid; a.nkeys = m.nkeys;
-  a.d0 = m.s0; a.d1 = m.s1 - m.n0; a.d2 = m.s2 - m.n0 - m.n1;
-  a.clamp_tok = m.s0;
-  return a;
-}
-
-// Token row of virtual key kv; `text` tells which tensor it indexes.
-// Returns the row, plus 0x40000000 when the key is a text key.
-__device__ __forceinline__ int key_row(KeyAddr a, int kv) {
-  int d = kv < a.e0 ? a.d0 : (kv < a.e1 ? a.d1 : a.d2);
-  bool text = (kv >= a.e2) & (kv < a.nkeys);
-  int vtok = kv < a.e2 ? kv + d : a.clamp_tok;
-  return text ? ((kv - a.e2) | 0x40000000) : vtok;
-}
-
-// Work order of the MFMA kernel.  Anchor-frame tiles (every key of the head)
-// come first.  When B*H is a multiple of 8, XCD x (blocks x, x+8, ...) owns
-// heads x*G/8 .. and walks them head by head, so the ~64 workgroups resident
-// on one XCD belong to a few neighbouring chunks of one head and stream the
-// same keys through that XCD's L2 at about the same time.
-__device__ __forceinline__ WorkItem decode_work_xcd(const Geo& g, int B, int H, int tpf) {
-  const int G = B * H;
-  if ((G & 7) != 0) return decode_work(g, B, H, tpf);
-  const int i = blockIdx.x;
-  const int xcd = i & 7, j = i >> 3, gper = G >> 3;
-  const int first = g.af ? 0 : -1;
-  const int last = (g.al && !(g.af && g.T == 1)) ? g.T - 1 : -1;
-  const int na = (first >= 0) + (last >= 0);
-  const int nanchor_items = na * tpf * gper;
-  int gl, t, tile;
-  if (j < nanchor_items) {
-    gl = j % gper;
-    const int r = j / gper;
-    t = (r / tpf == 0 && first >= 0) ? first : last;
-    tile = r % tpf;
-  } else {
-    const int jj = j - nanchor_items;
-    const int per_head = (g.T - na) * tpf;
-    gl = jj / per_head;
-    const int r = jj % per_head;
-    t = r / tpf + (g.af ? 1 : 0);
-    tile = r % tpf;
-  }
-  const int gi = xcd * gper + gl;
-  WorkItem w;
-  w.b = gi / H;
-  w.h = gi % H;
-  w.t = t;
-  w.tile = tile;
-  return w;
-}
 
 template <int D, bool VTM>
 __global__ void __launch_bounds__(256, 2)
@@ -521,13 +386,18 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // sigmoid(l0) O_soft + sigmoid(l1) RMSNorm(R q); MODE 2 the two gated branches
 // side by side, o[b][n][0][h][:] = sigmoid(l0) O_soft and
 // o[b][n][1][h][:] = sigmoid(l1) RMSNorm(R q), the input of the per-branch
-// output projections.
+// output projections.  MODE 3 (backward pass) takes the upstream gradient dO
+// of the merged output instead and writes what the backward needs: the gate
+// logits' gradients, dO_soft = sigmoid(l0) dO (bf16), the row statistics of
+// the softmax (its log-sum-exp in exp2 units and D = dO_soft . O_soft) and
+// the gradient of the linear read before RMSNorm.
 template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                   const bf16* __restrict__ tk, const bf16* __restrict__ vtg, int nl8,
                   bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c,
-                  const float* __restrict__ R, const float* __restrict__ gates, float eps) {
+                  const float* __restrict__ R, const float* __restrict__ gates, float eps,
+                  MergeBwdIO bio) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 3;
   constexpr int KCH = D / 8;
   constexpr int KST = 2 * D + 16, KSL = KST / 16;    // K row stride (bytes), slots
@@ -810,6 +680,65 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int j = 0; j < 16; ++j) ss = fmaf(lin[rb][j], lin[rb][j], ss);
     ss = xhalf_sum(ss);
     const float rinv = rsqrtf(ss * (1.0f / D) + eps);
+    if constexpr (MODE == 3) {
+      // Merge backward.  With s0, s1 the gate sigmoids, O_s = oacc * inv and
+      // n = lin * rinv: dl0 = (dO . O_s) s0 (1 - s0), dl1 = (dO . n) s1 (1 - s1),
+      // dO_s = s0 dO, and through RMSNorm (n = o / r, r = sqrt(mean(o^2) + eps))
+      // do = (s1 dO - n (s1 dO . n) / d) / r.
+      const float s0 = sigmoidf(gl.x), s1 = sigmoidf(gl.y);
+      const bf16* dorow = bio.dO + qoff;
+      bf16x4 dov[D / 32][4];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dov[db][jj] = *(const bf16x4*)(dorow + db * 32 + jj * 8 + half * 4);
+      float dot0 = 0.f, dot1 = 0.f, dsum = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dv = (float)dov[db][jj][e];
+            const float os = oacc[db][jj * 4 + e] * inv;
+            dot0 = fmaf(dv, os, dot0);
+            dot1 = fmaf(dv, lin[db][jj * 4 + e] * rinv, dot1);
+            dsum = fmaf((float)(bf16)(s0 * dv), os, dsum);
+          }
+      dot0 = xhalf_sum(dot0);
+      dot1 = xhalf_sum(dot1);
+      dsum = xhalf_sum(dsum);
+      const float lse2 = fmaf(m_run, c, __log2f(1.0f / inv));
+      if (qvalid) {
+        bf16* dosrow = bio.dos + qoff;
+        float* dlrow = bio.dlin + qoff;
+        const float kn = s1 * dot1 * (1.0f / D);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + jj * 8 + half * 4;
+            bf16x4 vs;
+            f32x4 vl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float dv = (float)dov[db][jj][e];
+              vs[e] = (bf16)(s0 * dv);
+              vl[e] = rinv * fmaf(-lin[db][jj * 4 + e] * rinv, kn, s1 * dv);
+            }
+            *(bf16x4*)(dosrow + d) = vs;
+            *(f32x4*)(dlrow + d) = vl;
+          }
+        if (half == 0) {
+          const size_t gi = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2;
+          *(float2*)(bio.dgates + gi) = make_float2(dot0 * s0 * (1.0f - s0), dot1 * s1 * (1.0f - s1));
+          const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
+          bio.dvec[ri] = dsum;
+          bio.lse[ri] = lse2;
+        }
+      }
+      return;
+    }
     const float g0 = sigmoidf(gl.x) * inv, g1 = sigmoidf(gl.y) * rinv;
     if (qvalid) {
       if constexpr (MODE == 1) {
@@ -885,7 +814,8 @@ vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
-                       const float* R, const float* gates, float eps, int mode, hipStream_t s) {
+                       const float* R, const float* gates, float eps, int mode, hipStream_t s,
+                       const MergeBwdIO& bio = MergeBwdIO{}) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
@@ -902,15 +832,19 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
     if (mode == 1)
       softmax_vt_kernel<D, 1><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps);
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, MergeBwdIO{});
     else if (mode == 2)
       softmax_vt_kernel<D, 2><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps);
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, MergeBwdIO{});
+    else if (mode == 3)
+      softmax_vt_kernel<D, 3><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, nullptr, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, bio);
     else
       softmax_vt_kernel<D, 0><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f);
+          l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f, MergeBwdIO{});
   } else {
     if (mode != 0) return hipErrorNotSupported;
     softmax_mfma_kernel<D, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
@@ -940,6 +874,40 @@ hipError_t launch_softmax(const void* q, const void* k, const void* v, const voi
       case 32: return launch_valu<float, 32>(q, k, v, tk, tv, l, scale, o, s);
       case 16: return launch_valu<float, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, int N, int L,
+                            void* xt, hipStream_t s) {
+  const int nl8 = (N + L + 7) / 8 * 8;
+  const int ntile = (nl8 + 63) / 64;
+  const dim3 grid((unsigned)(B * H * ntile));
+  switch (D) {
+    case 128:
+      vt_transpose_kernel<128><<<grid, dim3(256), 0, s>>>((const bf16*)x, (const bf16*)tx, (bf16*)xt, N, L, H, nl8, ntile);
+      break;
+    case 64:
+      vt_transpose_kernel<64><<<grid, dim3(256), 0, s>>>((const bf16*)x, (const bf16*)tx, (bf16*)xt, N, L, H, nl8, ntile);
+      break;
+    case 32:
+      vt_transpose_kernel<32><<<grid, dim3(256), 0, s>>>((const bf16*)x, (const bf16*)tx, (bf16*)xt, N, L, H, nl8, ntile);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_merge_bwd(const void* q, const void* k, const void* v, const void* tk,
+                                    const void* tv, const float* R, const float* gates,
+                                    const vdn_layout_t& l, float scale, float eps,
+                                    const MergeBwdIO& bio, void* ws, hipStream_t s) {
+  if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
+  switch (l.head_dim_k) {
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
   }
   return hipErrorInvalidValue;
 }

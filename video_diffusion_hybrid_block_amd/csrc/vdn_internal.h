@@ -99,6 +99,37 @@ __host__ __device__ inline bool frame_needs_stats(const Geo& g, int f) {
   return f < fwd_scan_end(g) || f > bwd_scan_begin(g);
 }
 
+// Anchor frames below m / above m (the anchor set {0, T-1} without repeats).
+__host__ __device__ inline int anchors_below(const Geo& g, int m) {
+  int n = (g.af && 0 < m) ? 1 : 0;
+  if (g.al && g.T - 1 < m && !(g.af && g.T == 1)) ++n;
+  return n;
+}
+__host__ __device__ inline int anchors_above(const Geo& g, int m) {
+  int n = (g.al && g.T - 1 > m) ? 1 : 0;
+  if (g.af && 0 > m && !(g.al && g.T == 1)) ++n;
+  return n;
+}
+// Position j (1-based) of frame f in the fold order of direction dir (0:
+// forward, ascending; 1: backward, descending), 0 when that state does not
+// fold f.
+__host__ __device__ inline int fold_index(const Geo& g, int dir, int f) {
+  if (is_anchor(g, f)) return 0;
+  if (dir == 0) return f < fwd_scan_end(g) ? f + 1 - anchors_below(g, f + 1) : 0;
+  return f > bwd_scan_begin(g) ? g.T - f - anchors_above(g, f - 1) : 0;
+}
+// Index j of the state chunk c's snapshot holds in direction dir: the number
+// of steps before it (non-anchor frames below min(win_lo, fend), resp. above
+// max(win_hi, fbeg)).
+__host__ __device__ inline int snap_index(const Geo& g, int dir, int c) {
+  if (dir == 0) {
+    const int m = imin(win_lo(g, c), fwd_scan_end(g));
+    return m - anchors_below(g, m);
+  }
+  const int m = imax(win_hi(g, c), bwd_scan_begin(g));
+  return (g.T - 1 - m) - anchors_above(g, m);
+}
+
 // Statistics slots of one (batch, head): frames the scans fold (or every
 // frame when `all_frames`), then the text block as slot T.  slot_of maps the
 // dense index 0..count_slots-1 to the slot.
@@ -181,8 +212,15 @@ hipError_t launch_gram(const void* k, const void* v, const void* tk, const void*
                        const float* beta, const vdn_layout_t& l, bool all_frames, float* A,
                        float* B, hipStream_t s);
 hipError_t launch_factor(float* A, const vdn_layout_t& l, bool all_frames, hipStream_t s);
+// states (backward pass, bf16 MFMA path only; may be null): every chain's
+// state after each of its steps, [B*H][2][T+1][d][d] fp32, step 0 = start.
 hipError_t launch_scan(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
-                       float* Sf, float* Sb, float* R, hipStream_t s);
+                       float* Sf, float* Sb, float* R, hipStream_t s, float* states = nullptr);
+// Backward pass of the scan: dspost [B*H][2][T+1][d][d] gets, per chain, the
+// gradient of its state after every step j (j = 0: the start), from dR
+// [B*H][nc+1][d][d] (the gradients of the read slots).  bf16, d >= 32.
+hipError_t launch_scan_bwd(const float* G, const float* dR, const float* alpha,
+                           const vdn_layout_t& l, float* dspost, hipStream_t s);
 hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
                         const vdn_layout_t& l, float eps, void* o, hipStream_t s);
 // Softmax branch with the merge fused into its epilogue (bf16, V^T path only):
@@ -193,6 +231,49 @@ hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, con
                                 const void* tv, const float* R, const float* gates,
                                 const vdn_layout_t& l, float scale, float eps, bool split, void* o,
                                 void* ws, hipStream_t s);
+// Outputs of the merge backward written by the softmax kernel's epilogue
+// (backward pass): for every video token-head, dgates [B,N,H,2] fp32,
+// dos = sigmoid(l0) dO [B,N,H,d] bf16, dlin = gradient of the linear read
+// before RMSNorm [B,N,H,d] fp32, and per (b, h, token) the softmax's
+// log-sum-exp in exp2 units (lse) and D = dos . O_soft (dvec), [B,H,N] fp32.
+struct MergeBwdIO {
+  const __bf16* dO;
+  float* dgates;
+  __bf16* dos;
+  float* dlin;
+  float* dvec;
+  float* lse;
+};
+hipError_t launch_softmax_merge_bwd(const void* q, const void* k, const void* v, const void* tk,
+                                    const void* tv, const float* R, const float* gates,
+                                    const vdn_layout_t& l, float scale, float eps,
+                                    const MergeBwdIO& bio, void* ws, hipStream_t s);
+// Transposed copy xt[b][h][d][n] of x [B,N,H,D] followed by tx [B,L,H,D]
+// (tokens along the row, zero-padded to a multiple of 8), bf16.
+hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, int N, int L,
+                            void* xt, hipStream_t s);
+// Softmax backward (bf16, d in {32, 64, 128}, P and L multiples of 8):
+// dq += scale * sum_j dS_ij k_j (dq fp32, already holding the linear read's
+// part), dk/dv (fp32, written) and dtk/dtv (text keys, written), from dos,
+// the row statistics lse/dvec, and transposed copies kt (keys + text), qt and
+// dost (video tokens).
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* tk,
+                           const void* tv, const void* dos, const float* lse, const float* dvec,
+                           const void* kt, const void* qt, const void* dost,
+                           const vdn_layout_t& l, float scale, float* dq, float* dk, float* dv,
+                           float* dtk, float* dtv, hipStream_t s);
+// VDA backward: dR / dq (written), reverse scan, per-frame dA (over G), dB
+// (over B), dalpha; then gram_bwd adds dk, dv, dtk, dtv and writes dbeta.
+hipError_t launch_vda_bwd(const void* q, const void* k, const void* v, const void* tk,
+                          const void* tv, const float* beta, const float* alpha,
+                          const float* dlin, const float* R, float* GA, float* BB,
+                          const float* states, float* dR, float* dspost, float* dq, float* dk,
+                          float* dv, float* dtk, float* dtv, float* dbeta, float* dalpha,
+                          const vdn_layout_t& l, hipStream_t s);
+hipError_t launch_gram_bwd(const void* k, const void* v, const void* tk, const void* tv,
+                           const float* beta, const float* dA, const float* dB, float* dk,
+                           float* dv, float* dtk, float* dtv, float* dbeta, const vdn_layout_t& l,
+                           hipStream_t s);
 // Output projections: y[m][n] = sum_k x[m][k] w[n][k] (bf16 in and out, fp32
 // accumulation); needs K a positive multiple of 64 and N a multiple of 8.
 bool proj_shape_ok(long M, int K, int N);

@@ -252,7 +252,7 @@ namespace {
 // their gradients, the read-slot gradients, transposed copies and the merge
 // backward's outputs.
 struct BwdPlan {
-  size_t states, dspost, dR, kt, qt, dost, dos, dlin, lse, dvec, total;
+  size_t states, dspost, dR, dRp, kt, qt, dost, dos, dlin, lse, dvec, total;
 };
 
 BwdPlan make_bwd_plan(const vdn_layout_t& l) {
@@ -266,7 +266,8 @@ BwdPlan make_bwd_plan(const vdn_layout_t& l) {
   b.states = p.total;
   b.dspost = align256(b.states + bh * 2 * (g.T + 1) * mat);
   b.dR = align256(b.dspost + bh * 2 * (g.T + 1) * mat);
-  b.kt = align256(b.dR + bh * (g.nc + 1) * mat);
+  b.dRp = align256(b.dR + bh * (g.nc + 1) * mat);
+  b.kt = align256(b.dRp + vda_bwd_partial_bytes(l));
   b.qt = align256(b.kt + bh * d * nl8 * 2);
   b.dost = align256(b.qt + bh * d * nq8 * 2);
   b.dos = align256(b.dost + bh * d * nq8 * 2);
@@ -356,8 +357,8 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
     e = launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream);
   // linear branch: dq (its part), dA over G, dB over B, dalpha
   if (e == hipSuccess)
-    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states, dR, dspost,
-                       dq, dk, dv, dtext_k, dtext_v, dbeta, dalpha, l, stream);
+    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
+                       (float*)(ws + bp.dRp), dR, dspost, dq, dalpha, l, stream);
   // softmax branch: dq (added), dk, dv, dtext_k, dtext_v (written)
   if (e == hipSuccess)
     e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,

@@ -19,9 +19,12 @@
 //  (S = (S̄ + B)(I + A)^-1); PaperDaily "伯克利与Impossible视频生成" §三 (two
 //  states from half the text write, summed read), §四 (frame statistics)]
 //
-// These are fp32 VALU kernels: their work (a few d x d x d products per
-// frame, three d x d matrix-vector products per token) is a few percent of
-// the softmax backward.
+// gfx950 design: the per-token products (steps 1 and 4) run on
+// v_mfma_f32_32x32x16_bf16 with fp32 operands split into bf16 hi + lo (bf16
+// inputs are exact), tiles staged in swizzled LDS and read row-wise
+// (ds_read_b128) or column-wise (ds_read_b64_tr_b16) as each product needs;
+// the per-frame d x d x d products (step 3, ~1 % of the backward) are fp32
+// VALU.
 #include "vdn_device.h"
 #include "vdn_internal.h"
 
@@ -30,35 +33,15 @@ namespace vdn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. dR and the linear part of dq.  One workgroup per (batch, head, slot).
+// 1. dR and the linear part of dq.  Workgroup = (batch, head, slot, chunk of
+// DR_CH of the slot's tokens); partial dR per chunk, summed by dr_sum_kernel.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256)
-dr_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin, const float* __restrict__ R,
-          float* __restrict__ dR, float* __restrict__ dq, Geo g, int H) {
-  constexpr int TT = 32;                 // tokens per tile
-  constexpr int RB = D / 16;             // dR block per thread: RB x RB
-  constexpr int QC = D / 8;              // dq columns per thread
-  constexpr int LD = D + 4;
-  __shared__ __attribute__((aligned(16))) float Rs[D * D];
-  __shared__ __attribute__((aligned(16))) float dl[TT * LD];
-  __shared__ __attribute__((aligned(16))) float qs[TT * LD];
-  const int tid = threadIdx.x;
-  const int slot = blockIdx.x % (g.nc + 1);
-  const int bh = blockIdx.x / (g.nc + 1);
-  const int b = bh / H, h = bh % H;
-  const size_t mat = (size_t)D * D;
-  const float* Rc = R + ((size_t)bh * (g.nc + 1) + slot) * mat;
-  for (int i = tid; i < D * D; i += 256) Rs[i] = Rc[i];
-  const int N = g.T * g.P;
-  const int ti = tid >> 4, tj = tid & 15;
-  float acc[RB][RB];
-#pragma unroll
-  for (int a = 0; a < RB; ++a)
-#pragma unroll
-    for (int c = 0; c < RB; ++c) acc[a][c] = 0.f;
-  // frames of the slot: the chunk's non-anchor frames, or the anchors
-  int f0, f1;
+constexpr int DR_CH = 256;               // tokens per workgroup
+constexpr int DR_TT = 64;                // tokens per LDS tile
+
+// Frames of read slot `slot` (a chunk's non-anchor frames; slot nc: the
+// anchors) and its token count.
+__device__ __forceinline__ int slot_frame_range(const Geo& g, int slot, int& f0, int& f1) {
   if (slot < g.nc) {
     f0 = slot * g.C;
     f1 = imin(g.T, f0 + g.C);
@@ -66,57 +49,172 @@ dr_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin, const floa
     f0 = 0;
     f1 = g.T;
   }
-  for (int f = f0; f < f1; ++f) {
-    if ((slot < g.nc) == is_anchor(g, f)) continue;
-    for (int t0 = 0; t0 < g.P; t0 += TT) {
-      const int nt = imin(TT, g.P - t0);
-      __syncthreads();                   // previous tile consumed (and Rs loaded)
-      for (int i = tid; i < TT * D; i += 256) {
-        const int r = i / D, c = i % D;
-        float dv = 0.f, qv = 0.f;
-        if (r < nt) {
-          const size_t off = (((size_t)b * N + (size_t)f * g.P + t0 + r) * H + h) * D + c;
-          dv = dlin[off];
-          qv = (float)q[off];
+  int n = 0;
+  for (int f = f0; f < f1; ++f) n += ((slot < g.nc) != is_anchor(g, f)) ? 1 : 0;
+  return n * g.P;
+}
+// Video token of the slot's i-th token.
+__device__ __forceinline__ int slot_token(const Geo& g, int slot, int f0, int i) {
+  int want = i / g.P;
+  for (int f = f0;; ++f) {
+    if ((slot < g.nc) != is_anchor(g, f)) {
+      if (want == 0) return f * g.P + i % g.P;
+      --want;
+    }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
+               const float* __restrict__ R, float* __restrict__ dRp, float* __restrict__ dq,
+               Geo g, int H, int nch) {
+  constexpr int MAT = D * D * 2;         // bf16 d x d tile, bytes
+  constexpr int TB = DR_TT * D * 2;      // bf16 token tile, bytes
+  constexpr int NBK = D / 32;
+  __shared__ __attribute__((aligned(16))) char rh[MAT];
+  __shared__ __attribute__((aligned(16))) char rl[MAT];
+  __shared__ __attribute__((aligned(16))) char qs[TB];
+  __shared__ __attribute__((aligned(16))) char dh[TB];
+  __shared__ __attribute__((aligned(16))) char dl[TB];
+  char VDN_LDS* Rh = (char VDN_LDS*)rh;
+  char VDN_LDS* Rl = (char VDN_LDS*)rl;
+  char VDN_LDS* Qs = (char VDN_LDS*)qs;
+  char VDN_LDS* Dh = (char VDN_LDS*)dh;
+  char VDN_LDS* Dl = (char VDN_LDS*)dl;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const int ch = blockIdx.x % nch;
+  const int slot = (blockIdx.x / nch) % (g.nc + 1);
+  const int bh = blockIdx.x / nch / (g.nc + 1);
+  const int b = bh / H, h = bh % H;
+  const int N = g.T * g.P;
+  const size_t mat = (size_t)D * D;
+  int f0, f1;
+  const int ntok = slot_frame_range(g, slot, f0, f1);
+  const int i0 = ch * DR_CH;
+  const int nmine = imax(0, imin(DR_CH, ntok - i0));
+  float* part = dRp + (((size_t)bh * (g.nc + 1) + slot) * nch + ch) * mat;
+  // R of the slot, hi + lo, row-major swizzled (read column-wise for dq)
+  const float* Rs = R + ((size_t)bh * (g.nc + 1) + slot) * mat;
+  for (int i = tid; i < D * D / 8; i += 256) {
+    const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+    const f32x4 a = *(const f32x4*)(Rs + r * D + c);
+    const f32x4 a2 = *(const f32x4*)(Rs + r * D + c + 4);
+    const float xv[8] = {a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+    bf16x8 hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16 hi, lo;
+      split_bf16(xv[e], hi, lo);
+      hv[e] = hi;
+      lv[e] = lo;
+    }
+    *(bf16x8 VDN_LDS*)(Rh + swz_off<D>(r, c)) = hv;
+    *(bf16x8 VDN_LDS*)(Rl + swz_off<D>(r, c)) = lv;
+  }
+  // this wave's dR blocks: (rb, cb) = wave-strided over the NBK x NBK grid
+  constexpr int BPW = NBK * NBK >= 4 ? NBK * NBK / 4 : 1;
+  f32x16 acc[BPW];
+#pragma unroll
+  for (int u = 0; u < BPW; ++u) acc[u] = f32x16{};
+  for (int t0 = 0; t0 < nmine; t0 += DR_TT) {
+    __syncthreads();                     // previous tile consumed (and R staged)
+    for (int i = tid; i < DR_TT * D / 8; i += 256) {
+      const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+      bf16x8 qv = {}, hv = {}, lv = {};
+      if (t0 + r < nmine) {
+        const int tok = slot_token(g, slot, f0, i0 + t0 + r);
+        const size_t off = (((size_t)b * N + tok) * H + h) * D + c;
+        qv = *(const bf16x8*)(q + off);
+        const f32x4 a = *(const f32x4*)(dlin + off);
+        const f32x4 a2 = *(const f32x4*)(dlin + off + 4);
+        const float xv[8] = {a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 hi, lo;
+          split_bf16(xv[e], hi, lo);
+          hv[e] = hi;
+          lv[e] = lo;
         }
-        dl[r * LD + c] = dv;
-        qs[r * LD + c] = qv;
       }
-      __syncthreads();
-      // dR block (rows ti*RB.., cols tj*RB..) += dlin^T q over the tile
-      for (int r = 0; r < nt; ++r) {
-        float dv[RB], qv[RB];
+      *(bf16x8 VDN_LDS*)(Qs + swz_off<D>(r, c)) = qv;
+      *(bf16x8 VDN_LDS*)(Dh + swz_off<D>(r, c)) = hv;
+      *(bf16x8 VDN_LDS*)(Dl + swz_off<D>(r, c)) = lv;
+    }
+    __syncthreads();
+    // dR[r][c] += sum_t dlin[t][r] q[t][c]: A = dlin^T, B = q (column reads)
 #pragma unroll
-        for (int a = 0; a < RB; ++a) dv[a] = dl[r * LD + ti * RB + a];
+    for (int u = 0; u < BPW; ++u) {
+      const int blk = wv * BPW + u;
+      if (blk >= NBK * NBK) break;       // d = 32: one block, wave 0
+      const int rb = blk / NBK, cb = blk % NBK;
 #pragma unroll
-        for (int c = 0; c < RB; ++c) qv[c] = qs[r * LD + tj * RB + c];
-#pragma unroll
-        for (int a = 0; a < RB; ++a)
-#pragma unroll
-          for (int c = 0; c < RB; ++c) acc[a][c] = fmaf(dv[a], qv[c], acc[a][c]);
+      for (int ks = 0; ks < DR_TT / 16; ++ks) {
+        const bf16x8 ah = lds_col8<D>(Dh, ks * 16, rb * 32, lane);
+        const bf16x8 al = lds_col8<D>(Dl, ks * 16, rb * 32, lane);
+        const bf16x8 bq = lds_col8<D>(Qs, ks * 16, cb * 32, lane);
+        acc[u] = mfma32(ah, bq, acc[u]);
+        acc[u] = mfma32(al, bq, acc[u]);
       }
-      // dq_i = R^T dlin_i: 8 threads per token, QC columns each
-      const int tok = tid >> 3, cg = (tid & 7) * QC;
-      if (tok < nt) {
-        float o[QC];
+    }
+    // dq[t][c] = sum_r dlin[t][r] R[r][c]: wave w takes tokens 32*(w/2) ..,
+    // column blocks (w%2)*NBK/2 ..; A = dlin rows, B = R columns
+    if (NBK >= 2 || wv % 2 == 0) {
+      const int tb = wv >> 1;
+      const int ncb = NBK >= 2 ? NBK / 2 : 1;
 #pragma unroll
-        for (int e = 0; e < QC; ++e) o[e] = 0.f;
-        for (int r = 0; r < D; ++r) {
-          const float dv = dl[tok * LD + r];
+      for (int u = 0; u < ncb; ++u) {
+        const int cb = (NBK >= 2 ? (wv & 1) * ncb : 0) + u;
+        f32x16 o = f32x16{};
 #pragma unroll
-          for (int e = 0; e < QC; ++e) o[e] = fmaf(Rs[r * D + cg + e], dv, o[e]);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 ah = lds_row8<D>(Dh, tb * 32 + (lane & 31), ks * 2 + half);
+          const bf16x8 al = lds_row8<D>(Dl, tb * 32 + (lane & 31), ks * 2 + half);
+          const bf16x8 bh_ = lds_col8<D>(Rh, ks * 16, cb * 32, lane);
+          const bf16x8 bl_ = lds_col8<D>(Rl, ks * 16, cb * 32, lane);
+          o = mfma32(ah, bh_, o);
+          o = mfma32(ah, bl_, o);
+          o = mfma32(al, bh_, o);
         }
-        float* dst = dq + (((size_t)b * N + (size_t)f * g.P + t0 + tok) * H + h) * D + cg;
 #pragma unroll
-        for (int e = 0; e < QC; e += 4) *(f32x4*)(dst + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+        for (int j = 0; j < 16; ++j) {
+          const int r = tb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+          if (t0 + r < nmine) {
+            const int tok = slot_token(g, slot, f0, i0 + t0 + r);
+            dq[(((size_t)b * N + tok) * H + h) * D + cb * 32 + (lane & 31)] = o[j];
+          }
+        }
       }
     }
   }
-  float* dst = dR + ((size_t)bh * (g.nc + 1) + slot) * mat;
 #pragma unroll
-  for (int a = 0; a < RB; ++a)
+  for (int u = 0; u < BPW; ++u) {
+    const int blk = wv * BPW + u;
+    if (blk >= NBK * NBK) break;
+    const int rb = blk / NBK, cb = blk % NBK;
 #pragma unroll
-    for (int c = 0; c < RB; ++c) dst[(size_t)(ti * RB + a) * D + tj * RB + c] = acc[a][c];
+    for (int j = 0; j < 16; ++j) {
+      const int r = rb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+      part[(size_t)r * D + cb * 32 + (lane & 31)] = acc[u][j];
+    }
+  }
+}
+
+// dR[bh][slot] = sum of the chunks' partials.
+__global__ void __launch_bounds__(256)
+dr_sum_kernel(const float4* __restrict__ part, float4* __restrict__ dR, int nch, size_t mat4,
+              size_t nslot) {
+  const size_t n = nslot * mat4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t sl = i / mat4, e = i % mat4;
+    const float4* p = part + sl * nch * mat4 + e;
+    float4 a = p[0];
+    for (int c = 1; c < nch; ++c) {
+      const float4 x = p[(size_t)c * mat4];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    }
+    dR[i] = a;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -284,110 +382,165 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
 
 // ---------------------------------------------------------------------------
 // 4. Per token of every frame (slot T: the text tokens): dk, dv (added),
-// dbeta (written; zero for frames no chain folds).
+// dbeta (written; zero for frames no chain folds).  Workgroup = (batch, head,
+// slot, chunk of GB_CH tokens), 4 waves x 32 tokens at a time.  With
+// As = dA + dA^T: U = K As^T, W = K dB^T, Z = V dB (tokens x d each) on MFMA,
+// As and dB as bf16 hi + lo in swizzled LDS (As and dB rows for U and W,
+// dB columns for Z); dk += beta (U + Z), dv += beta W,
+// dbeta = sum_r (k_r U_r / 2 + v_r W_r).
 // ---------------------------------------------------------------------------
+constexpr int GB_CH = 256;
+
 template <int D>
 __global__ void __launch_bounds__(256)
-gram_bwd_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
-                const bf16* __restrict__ tk, const bf16* __restrict__ tv,
-                const float* __restrict__ beta, const float* __restrict__ dA,
-                const float* __restrict__ dB, float* __restrict__ dk, float* __restrict__ dv,
-                float* __restrict__ dtk, float* __restrict__ dtv, float* __restrict__ dbeta,
-                Geo g, int H) {
-  constexpr int LD = D + 1;
-  constexpr int TT = 16;                 // tokens per pass
-  constexpr int RPT = D / 16;            // output rows per thread
-  __shared__ float As[D * LD];           // dA + dA^T
-  __shared__ float Bs[D * LD];           // dB
-  __shared__ float kv[TT][2][D];
-  const int tid = threadIdx.x;
-  const int slot = blockIdx.x % (g.T + 1);
-  const int bh = blockIdx.x / (g.T + 1);
+gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                     const bf16* __restrict__ tk, const bf16* __restrict__ tv,
+                     const float* __restrict__ beta, const float* __restrict__ dA,
+                     const float* __restrict__ dB, float* __restrict__ dk,
+                     float* __restrict__ dv, float* __restrict__ dtk, float* __restrict__ dtv,
+                     float* __restrict__ dbeta, Geo g, int H, int nch) {
+  constexpr int MAT = D * D * 2;
+  constexpr int NBK = D / 32;
+  __shared__ __attribute__((aligned(16))) char sah[MAT];
+  __shared__ __attribute__((aligned(16))) char sal[MAT];
+  __shared__ __attribute__((aligned(16))) char sbh[MAT];
+  __shared__ __attribute__((aligned(16))) char sbl[MAT];
+  char VDN_LDS* Ah = (char VDN_LDS*)sah;
+  char VDN_LDS* Al = (char VDN_LDS*)sal;
+  char VDN_LDS* Bh = (char VDN_LDS*)sbh;
+  char VDN_LDS* Bl = (char VDN_LDS*)sbl;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const int ch = blockIdx.x % nch;
+  const int slot = (blockIdx.x / nch) % (g.T + 1);
+  const int bh = blockIdx.x / nch / (g.T + 1);
   const int b = bh / H, h = bh % H;
   const int N = g.T * g.P;
   const bool text = slot == g.T;
   const int ntok = text ? g.L : g.P;
-  if (ntok == 0) return;
+  const int i0 = ch * GB_CH;
+  const int nmine = imin(GB_CH, ntok - i0);
+  if (nmine <= 0) return;
   const int NB = N + g.L;
-  float* dbrow = dbeta + ((size_t)b * NB + (text ? N : slot * g.P)) * H + h;
+  float* dbrow = dbeta + ((size_t)b * NB + (text ? N : slot * g.P) + i0) * H + h;
   const bool live = text || frame_needs_stats(g, slot);
   if (!live) {
-    for (int i = tid; i < ntok; i += 256) dbrow[(size_t)i * H] = 0.f;
+    for (int i = tid; i < nmine; i += 256) dbrow[(size_t)i * H] = 0.f;
     return;
   }
   const size_t mat = (size_t)D * D;
   const float* dAs = dA + ((size_t)bh * (g.T + 1) + slot) * mat;
   const float* dBs = dB + ((size_t)bh * (g.T + 1) + slot) * mat;
-  for (int i = tid; i < D * D; i += 256) {
-    const int r = i / D, c = i % D;
-    As[r * LD + c] = dAs[i] + dAs[(size_t)c * D + r];
-    Bs[r * LD + c] = dBs[i];
+  for (int i = tid; i < D * D / 8; i += 256) {
+    const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+    bf16x8 ah, al, bh_, bl_;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = dAs[(size_t)r * D + c + e] + dAs[(size_t)(c + e) * D + r];
+      const float bb = dBs[(size_t)r * D + c + e];
+      bf16 x, y;
+      split_bf16(a, x, y);
+      ah[e] = x;
+      al[e] = y;
+      split_bf16(bb, x, y);
+      bh_[e] = x;
+      bl_[e] = y;
+    }
+    *(bf16x8 VDN_LDS*)(Ah + swz_off<D>(r, c)) = ah;
+    *(bf16x8 VDN_LDS*)(Al + swz_off<D>(r, c)) = al;
+    *(bf16x8 VDN_LDS*)(Bh + swz_off<D>(r, c)) = bh_;
+    *(bf16x8 VDN_LDS*)(Bl + swz_off<D>(r, c)) = bl_;
   }
-  const bf16* kb = text ? tk + ((size_t)b * g.L * H + h) * D : k + (((size_t)b * N + (size_t)slot * g.P) * H + h) * D;
-  const bf16* vb = text ? tv + ((size_t)b * g.L * H + h) * D : v + (((size_t)b * N + (size_t)slot * g.P) * H + h) * D;
-  float* dkb = text ? dtk + ((size_t)b * g.L * H + h) * D : dk + (((size_t)b * N + (size_t)slot * g.P) * H + h) * D;
-  float* dvb = text ? dtv + ((size_t)b * g.L * H + h) * D : dv + (((size_t)b * N + (size_t)slot * g.P) * H + h) * D;
-  const float* btok = beta + ((size_t)b * NB + (text ? N : slot * g.P)) * H + h;
-  const int tk_ = tid >> 4, rl = tid & 15;
-  for (int t0 = 0; t0 < ntok; t0 += TT) {
-    __syncthreads();                     // previous tokens consumed (and matrices loaded)
-    for (int i = tid; i < TT * D; i += 256) {
-      const int t = i / D, c = i % D;
-      float kx = 0.f, vx = 0.f;
-      if (t0 + t < ntok) {
-        kx = (float)kb[(size_t)(t0 + t) * H * D + c];
-        vx = (float)vb[(size_t)(t0 + t) * H * D + c];
-      }
-      kv[t][0][c] = kx;
-      kv[t][1][c] = vx;
+  __syncthreads();
+  const size_t base = text ? ((size_t)b * g.L + i0) * H + h : ((size_t)b * N + (size_t)slot * g.P + i0) * H + h;
+  const bf16* kb = (text ? tk : k) + base * D;
+  const bf16* vb = (text ? tv : v) + base * D;
+  float* dkb = (text ? dtk : dk) + base * D;
+  float* dvb = (text ? dtv : dv) + base * D;
+  const float* bt = beta + ((size_t)b * NB + (text ? N : slot * g.P) + i0) * H + h;
+  const size_t HD = (size_t)H * D;
+  for (int t0 = wv * 32; t0 < nmine; t0 += 128) {
+    const int tl = imin(t0 + (lane & 31), nmine - 1);   // A-operand row (clamped)
+    bf16x8 ka[D / 16], va[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      ka[ks] = *(const bf16x8*)(kb + (size_t)tl * HD + ks * 16 + half * 8);
+      va[ks] = *(const bf16x8*)(vb + (size_t)tl * HD + ks * 16 + half * 8);
     }
-    __syncthreads();
-    const int t = t0 + tk_;
-    // rows r = rl + 16 m: u = (dA + dA^T) k, w = dB k, z = dB^T v
-    float u[RPT], w[RPT], z[RPT];
+    // rows of the result: register j -> token t0 + 8*(j/4) + 4*half + j%4
+    float bj[16], dbp[16];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) u[m] = w[m] = z[m] = 0.f;
-    for (int c = 0; c < D; ++c) {
-      const float kc = kv[tk_][0][c], vc = kv[tk_][1][c];
-#pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rl + 16 * m;
-        u[m] = fmaf(As[r * LD + c], kc, u[m]);
-        w[m] = fmaf(Bs[r * LD + c], kc, w[m]);
-        z[m] = fmaf(Bs[c * LD + r], vc, z[m]);
-      }
-    }
-    // dbeta = k^T dA k + v^T dB k = k . u / 2 + v . w
-    float db = 0.f;
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-      const int r = rl + 16 * m;
-      db = fmaf(0.5f * kv[tk_][0][r], u[m], db);
-      db = fmaf(kv[tk_][1][r], w[m], db);
+    for (int j = 0; j < 16; ++j) {
+      const int t = imin(t0 + (j >> 2) * 8 + half * 4 + (j & 3), nmine - 1);
+      bj[j] = bt[(size_t)t * H];
+      dbp[j] = 0.f;
     }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) db += __shfl_xor(db, o, 16);
-    if (t < ntok) {
-      const float bt = btok[(size_t)t * H];
-      float* dkr = dkb + (size_t)t * H * D;
-      float* dvr = dvb + (size_t)t * H * D;
+    for (int nb = 0; nb < NBK; ++nb) {
+      f32x16 U = f32x16{}, W = f32x16{}, Z = f32x16{};
+      const int r = nb * 32 + (lane & 31);
 #pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        const int r = rl + 16 * m;
-        dkr[r] += bt * (u[m] + z[m]);
-        dvr[r] += bt * w[m];
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a_h = lds_row8<D>(Ah, r, ks * 2 + half);
+        const bf16x8 a_l = lds_row8<D>(Al, r, ks * 2 + half);
+        const bf16x8 b_h = lds_row8<D>(Bh, r, ks * 2 + half);
+        const bf16x8 b_l = lds_row8<D>(Bl, r, ks * 2 + half);
+        const bf16x8 c_h = lds_col8<D>(Bh, ks * 16, nb * 32, lane);
+        const bf16x8 c_l = lds_col8<D>(Bl, ks * 16, nb * 32, lane);
+        U = mfma32(ka[ks], a_h, U);
+        U = mfma32(ka[ks], a_l, U);
+        W = mfma32(ka[ks], b_h, W);
+        W = mfma32(ka[ks], b_l, W);
+        Z = mfma32(va[ks], c_h, Z);
+        Z = mfma32(va[ks], c_l, Z);
       }
-      if (rl == 0) dbrow[(size_t)t * H] = db;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + (j >> 2) * 8 + half * 4 + (j & 3);
+        if (t < nmine) {
+          const size_t e = (size_t)t * HD + r;
+          dkb[e] += bj[j] * (U[j] + Z[j]);
+          dvb[e] += bj[j] * W[j];
+          dbp[j] = fmaf(0.5f * (float)kb[e], U[j], dbp[j]);
+          dbp[j] = fmaf((float)vb[e], W[j], dbp[j]);
+        }
+      }
+    }
+    // sum over the 32 columns each half holds, then one lane per token
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x = dbp[j];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o, 32);
+      dbp[j] = x;
+    }
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + (j >> 2) * 8 + half * 4 + (j & 3);
+        if (t < nmine) dbrow[(size_t)t * H] = dbp[j];
+      }
     }
   }
 }
 
+constexpr int dr_chunks(const Geo& g) {
+  return (imax(g.C, 2) * g.P + DR_CH - 1) / DR_CH;
+}
+
 template <int D>
-hipError_t launch_dr_d(const void* q, const float* dlin, const float* R, float* dR, float* dq,
-                       const vdn_layout_t& l, hipStream_t s) {
+hipError_t launch_dr_d(const void* q, const float* dlin, const float* R, float* dRp, float* dR,
+                       float* dq, const vdn_layout_t& l, hipStream_t s) {
   Geo g = make_geo(l);
-  dr_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.nc + 1))), dim3(256), 0, s>>>(
-      (const bf16*)q, dlin, R, dR, dq, g, l.heads);
+  const int nch = dr_chunks(g);
+  dr_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.nc + 1) * nch)), dim3(256), 0, s>>>(
+      (const bf16*)q, dlin, R, dRp, dq, g, l.heads, nch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t mat4 = (size_t)D * D / 4;
+  const size_t nslot = (size_t)l.batch * l.heads * (g.nc + 1);
+  const size_t n = nslot * mat4;
+  dr_sum_kernel<<<dim3((unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192)), dim3(256), 0, s>>>(
+      (const float4*)dRp, (float4*)dR, nch, mat4, nslot);
   return hipGetLastError();
 }
 
@@ -407,25 +560,31 @@ hipError_t launch_gram_bwd_d(const void* k, const void* v, const void* tk, const
                              float* dv, float* dtk, float* dtv, float* dbeta,
                              const vdn_layout_t& l, hipStream_t s) {
   Geo g = make_geo(l);
-  gram_bwd_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1))), dim3(256), 0, s>>>(
+  const int nch = (imax(g.P, g.L) + GB_CH - 1) / GB_CH;
+  gram_bwd_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1) * nch)), dim3(256), 0, s>>>(
       (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv, beta, dA, dB, dk, dv,
-      dtk, dtv, dbeta, g, l.heads);
+      dtk, dtv, dbeta, g, l.heads, nch);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t vda_bwd_partial_bytes(const vdn_layout_t& l) {
+  Geo g = make_geo(l);
+  return (size_t)l.batch * l.heads * (g.nc + 1) * dr_chunks(g) * l.head_dim_k * l.head_dim_k *
+         sizeof(float);
+}
+
 hipError_t launch_vda_bwd(const void* q, const void* k, const void* v, const void* tk,
                           const void* tv, const float* beta, const float* alpha,
                           const float* dlin, const float* R, float* GA, float* BB,
-                          const float* states, float* dR, float* dspost, float* dq, float* dk,
-                          float* dv, float* dtk, float* dtv, float* dbeta, float* dalpha,
-                          const vdn_layout_t& l, hipStream_t s) {
+                          const float* states, float* dRp, float* dR, float* dspost, float* dq,
+                          float* dalpha, const vdn_layout_t& l, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
   switch (l.head_dim_k) {
-    case 128: e = launch_dr_d<128>(q, dlin, R, dR, dq, l, s); break;
-    case 64: e = launch_dr_d<64>(q, dlin, R, dR, dq, l, s); break;
-    case 32: e = launch_dr_d<32>(q, dlin, R, dR, dq, l, s); break;
+    case 128: e = launch_dr_d<128>(q, dlin, R, dRp, dR, dq, l, s); break;
+    case 64: e = launch_dr_d<64>(q, dlin, R, dRp, dR, dq, l, s); break;
+    case 32: e = launch_dr_d<32>(q, dlin, R, dRp, dR, dq, l, s); break;
   }
   if (e != hipSuccess) return e;
   e = launch_scan_bwd(GA, dR, alpha, l, dspost, s);

@@ -262,14 +262,15 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            const void* kt, const void* qt, const void* dost,
                            const vdn_layout_t& l, float scale, float* dq, float* dk, float* dv,
                            float* dtk, float* dtv, hipStream_t s);
-// VDA backward: dR / dq (written), reverse scan, per-frame dA (over G), dB
-// (over B), dalpha; then gram_bwd adds dk, dv, dtk, dtv and writes dbeta.
+// VDA backward: dR / dq (written; dRp holds per-chunk partials of dR,
+// vda_bwd_partial_bytes), reverse scan, per-frame dA (over G), dB (over B),
+// dalpha; then gram_bwd adds dk, dv, dtk, dtv and writes dbeta.
+size_t vda_bwd_partial_bytes(const vdn_layout_t& l);
 hipError_t launch_vda_bwd(const void* q, const void* k, const void* v, const void* tk,
                           const void* tv, const float* beta, const float* alpha,
                           const float* dlin, const float* R, float* GA, float* BB,
-                          const float* states, float* dR, float* dspost, float* dq, float* dk,
-                          float* dv, float* dtk, float* dtv, float* dbeta, float* dalpha,
-                          const vdn_layout_t& l, hipStream_t s);
+                          const float* states, float* dRp, float* dR, float* dspost, float* dq,
+                          float* dalpha, const vdn_layout_t& l, hipStream_t s);
 hipError_t launch_gram_bwd(const void* k, const void* v, const void* tk, const void* tv,
                            const float* beta, const float* dA, const float* dB, float* dk,
                            float* dv, float* dtk, float* dtv, float* dbeta, const vdn_layout_t& l,

@@ -11,7 +11,8 @@ fused softmax + merge stage, timed alone with HIP events on its stream), and
 the CPU oracle timed on a bounded sample of the same workload.  It also times
 the layer followed by the two branches' separate output projections
 (d_model = H*d), the projection product alone, and the library matmul on the
-same operands for comparison.
+same operands for comparison, and the backward pass (gradients of every input
+given an upstream gradient of O).
 """
 from __future__ import annotations
 
@@ -127,6 +128,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-proj", action="store_true",
                     help="skip the layer-with-output-projections timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -253,6 +255,41 @@ def main():
                 "library_matmul_ms": round(lib_ms, 4)}
         del pws, y, y2, x2, w_o, wt
 
+    # backward pass of the layer (gradients of every input given dO), bf16
+    # layouts only: the forward recomputation plus the backward kernels
+    bwd = None
+    if w.dtype == "bf16" and not args.no_bwd:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed + 2)
+        dO = torch.randn(dev["q"].shape, generator=g, device="cuda").to(tdt)
+        bws = torch.empty(V.bwd_workspace_size(lay), dtype=torch.uint8, device="cuda")
+
+        def backward():
+            return V.hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"],
+                                     dev["alpha"], dev["gate_logits"], dO, **geo, workspace=bws)
+
+        print("[bench] backward pass", file=sys.stderr, flush=True)
+        for _ in range(2):
+            backward()
+        torch.cuda.synchronize()
+        nb = max(3, args.steps // 4)
+        e0.record(stream)
+        for _ in range(nb):
+            backward()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b_ms = e0.elapsed_time(e1) / nb
+        pairs = sum(k_ * w.tokens_per_frame for k_ in visible_keys_per_frame(w))
+        # attention flops of a backward with recomputation: 4d (forward) +
+        # 10d (dP, dS.K, dS^T.Q, P^T.dO and the recomputed S) per visible pair
+        aflops = 14.0 * w.head_dim * pairs * w.batch * w.heads
+        bwd = {"ms": round(b_ms, 3), "calls": nb,
+               "video_tokens_per_s": round(w.batch * w.video_tokens / (b_ms / 1e3), 1),
+               "attention_tflops": round(aflops / (b_ms / 1e3) / 1e12, 1),
+               "note": "vdn_hybrid_attn_bwd: forward recomputation + gradients of q, k, v, "
+                       "text k/v, beta, alpha, gate logits (fp32)"}
+        del bws, dO
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -290,6 +327,7 @@ def main():
                      "algorithmic_flops_per_launch": k1_flops, "ms_per_launch": round(k1_ms, 4)},
         "wall_s_timed_region": round(wall, 3),
         "output_projections": proj,
+        "backward": bwd,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -35,7 +35,8 @@ import torch
 
 from . import vdn_oracle as O
 
-__all__ = ["layer_forward_bh", "hybrid_attn_forward", "hybrid_attn_grad", "GRAD_KEYS"]
+__all__ = ["layer_forward_bh", "hybrid_attn_forward", "hybrid_attn_grad",
+           "hybrid_attn_grad_bh", "GRAD_KEYS"]
 
 GRAD_KEYS = ("q", "k", "v", "text_k", "text_v", "beta", "alpha", "gate_logits")
 
@@ -128,6 +129,21 @@ def hybrid_attn_forward(inputs: dict, lay: O.Layout) -> np.ndarray:
     return out
 
 
+def hybrid_attn_grad_bh(inputs: dict, lay: O.Layout, dO, b: int, h: int) -> dict:
+    """Gradients of sum(dO * O) restricted to one (batch, head): heads and
+    batch entries do not interact, so this is that slice of the full
+    gradient.  Arrays shaped like the inputs' (b, :, h) slices."""
+    x = _bh_tensors(inputs, lay, b, h, True)
+    out = _call(x, lay)
+    out.backward(torch.tensor(np.asarray(dO[b, :, h], np.float64)))
+    res = {}
+    for key in GRAD_KEYS:
+        t = x[key]
+        # an input the output does not depend on has no gradient
+        res[key] = np.zeros(tuple(t.shape)) if t.grad is None else t.grad.numpy()
+    return res
+
+
 def hybrid_attn_grad(inputs: dict, lay: O.Layout, dO) -> dict:
     """Gradient of sum(dO * O) with respect to each input of the layer, as
     float64 arrays shaped like the inputs (``GRAD_KEYS``).  beta's gradient
@@ -138,22 +154,14 @@ def hybrid_attn_grad(inputs: dict, lay: O.Layout, dO) -> dict:
              if inputs.get(key) is not None}
     for b in range(lay.batch):
         for h in range(lay.heads):
-            x = _bh_tensors(inputs, lay, b, h, True)
-            out = _call(x, lay)
-            out.backward(torch.tensor(dO[b, :, h]))
-
-            def g(key):
-                t = x[key]
-                # an input the output does not depend on has no gradient
-                return np.zeros(tuple(t.shape)) if t.grad is None else t.grad.numpy()
-
-            grads["q"][b, :, h] = g("q")
-            grads["k"][b, :, h] = g("k")
-            grads["v"][b, :, h] = g("v")
+            r = hybrid_attn_grad_bh(inputs, lay, dO, b, h)
+            grads["q"][b, :, h] = r["q"]
+            grads["k"][b, :, h] = r["k"]
+            grads["v"][b, :, h] = r["v"]
             if L > 0:
-                grads["text_k"][b, :, h] = g("text_k")
-                grads["text_v"][b, :, h] = g("text_v")
-            grads["beta"][b, :N + L, h] = g("beta")
-            grads["alpha"][b, :, h] = g("alpha")
-            grads["gate_logits"][b, :, h] = g("gate_logits")
+                grads["text_k"][b, :, h] = r["text_k"]
+                grads["text_v"][b, :, h] = r["text_v"]
+            grads["beta"][b, :N + L, h] = r["beta"]
+            grads["alpha"][b, :, h] = r["alpha"]
+            grads["gate_logits"][b, :, h] = r["gate_logits"]
     return grads

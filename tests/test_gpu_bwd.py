@@ -94,3 +94,35 @@ def test_backward_matches_oracle(case):
     print(case["name"], " ".join(f"{k_} {e:.2e}" for k_, e in errs.items()), flush=True)
     bad = {k_: e for k_, e in errs.items() if not e <= TOL}
     assert not bad, bad
+
+
+@pytest.mark.timeout(900)
+def test_backward_768p_one_head_in_full():
+    """The 768p layer (B=1, H=24, d=128, 60 x 1008 tokens, 512 text tokens)
+    in the launch configuration bench.py times: heads do not interact, so
+    head 0's slice of every gradient is compared in full with the oracle's
+    gradient of that head."""
+    require_gpu()
+    from _helpers import workload
+    w = workload("768p")
+    _announce("backward 768p head 0")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    dO = synth.round_bf16(np.random.default_rng(w.seed + 7).standard_normal(
+        inp["q"].shape).astype(np.float32))
+    dev = to_dev(inp, w.dtype)
+    got = V.hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"],
+                            dev["beta"], dev["alpha"], dev["gate_logits"],
+                            torch.from_numpy(dO).to(torch.bfloat16).cuda(), frames=w.frames,
+                            tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+                            window_chunks=w.window_chunks)
+    torch.cuda.synchronize()
+    got = {k_: (None if t is None else t[0, :, 0].cpu().numpy()) for k_, t in got.items()}
+    del dev
+    torch.cuda.empty_cache()
+    print("[case] oracle gradient of head 0 (tens of seconds)", flush=True)
+    ref = G.hybrid_attn_grad_bh(inp, lay, dO, 0, 0)
+    errs = {k_: rel_err(got[k_], ref[k_]) for k_ in G.GRAD_KEYS}
+    print("768p head 0", " ".join(f"{k_} {e:.2e}" for k_, e in errs.items()), flush=True)
+    bad = {k_: e for k_, e in errs.items() if not e <= TOL}
+    assert not bad, bad

@@ -17,6 +17,7 @@ given an upstream gradient of O).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -27,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k1_softmax_768p_hbm_traffic.md")
 K1_SOURCES = ["video_diffusion_hybrid_block_amd/csrc/k_softmax.hip",
@@ -241,10 +243,30 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / n
 
+        # FP8 (MXFP8) form: weights quantized once, activations per call
+        wq, wsc = V.mxfp8_quantize(w_o)
+        xq, xsc = V.mxfp8_quantize(x2)
+        pws8 = torch.empty(V.lib().vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay)),
+                           dtype=torch.uint8, device="cuda")
+
+        def layer_proj8():
+            V.hybrid_attn_proj_mxfp8(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"],
+                                     dev["alpha"], dev["gate_logits"], wq, wsc, **geo, out=y,
+                                     workspace=pws8)
+
+        def product8():
+            V.out_proj_mxfp8(xq, xsc, wq, wsc, out=y2)
+
+        def quant8():
+            V.mxfp8_quantize(x2)
+
         print("[bench] layer with output projections", file=sys.stderr, flush=True)
         lp_ms = timed(layer_proj, args.steps)
         pr_ms = timed(product, args.steps)
         lib_ms = timed(library_product, args.steps)
+        lp8_ms = timed(layer_proj8, args.steps)
+        pr8_ms = timed(product8, args.steps)
+        q8_ms = timed(quant8, args.steps)
         pflops = 2.0 * w.batch * w.video_tokens * (2 * H * d) * dm
         proj = {"d_model": dm, "layer_with_proj_ms": round(lp_ms, 4),
                 "video_tokens_per_s": round(w.batch * w.video_tokens / (lp_ms / 1e3), 1),
@@ -252,8 +274,16 @@ def main():
                 "proj_ms": round(pr_ms, 4),
                 "proj_tflops": round(pflops / (pr_ms / 1e3) / 1e12, 1),
                 "proj_frac": round(pflops / (pr_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "library_matmul_ms": round(lib_ms, 4)}
-        del pws, y, y2, x2, w_o, wt
+                "library_matmul_ms": round(lib_ms, 4),
+                "fp8": {"format": "MXFP8 (E4M3 codes, E8M0 scale per 32 along K)",
+                        "proj_kernel": "proj_mxfp8_kernel (v_mfma_scale_f32_32x32x64_f8f6f4)",
+                        "proj_ms": round(pr8_ms, 4),
+                        "proj_tflops": round(pflops / (pr8_ms / 1e3) / 1e12, 1),
+                        "proj_frac_fp8_peak": round(pflops / (pr8_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                        "activation_quantize_ms": round(q8_ms, 4),
+                        "layer_with_proj_ms": round(lp8_ms, 4),
+                        "video_tokens_per_s": round(w.batch * w.video_tokens / (lp8_ms / 1e3), 1)}}
+        del pws, pws8, y, y2, x2, w_o, wt, xq, xsc, wq, wsc
 
     # backward pass of the layer (gradients of every input given dO), bf16
     # layouts only: the forward recomputation plus the backward kernels

@@ -182,6 +182,43 @@ vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* 
 vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, int32_t N,
                           void* y, hipStream_t stream);
 
+/* FP8 form of the projections (the pages' block runs its linear layers in
+ * FP8; deepmagic blog, section 實測數據).  Format: OCP MXFP8 - E4M3 codes
+ * (1 byte each, OCP encoding: bias 7, largest finite 448) with one E8M0
+ * scale byte (2^(s-127)) per 32 consecutive values along the contraction.
+ * For a block with largest magnitude a: X = floor(log2 a) - 8 (X >= -127;
+ * X = 0 for an all-zero block), codes = E4M3(v / 2^X) rounded to nearest
+ * even and clamped to +-448, scale byte = X + 127.
+ *
+ * vdn_mxfp8_quantize: x bf16 [M, K] (K a multiple of 32) -> q [M, K] codes,
+ * scales [M, K/32].  x, q 16-byte aligned.  Used for the weights once and by
+ * the layer below for its activations. */
+vdn_status_t vdn_mxfp8_quantize(const void* x, int64_t M, int32_t K, void* q, void* scales,
+                                hipStream_t stream);
+
+/* y[m][n] = sum_k X[m][k] W[n][k] with X, W given as MXFP8 codes + scales
+ * ([M, K] + [M, K/32] and [N, K] + [N, K/32]); bf16 y [M, N], fp32
+ * accumulation.  K a multiple of 128, N of 8 (else VDN_ERR_UNSUPPORTED);
+ * codes 16-byte and scales 4-byte aligned. */
+vdn_status_t vdn_out_proj_mxfp8(const void* xq, const void* xs, const void* wq, const void* ws,
+                                int64_t M, int32_t K, int32_t N, void* y, hipStream_t stream);
+
+/* Bytes of workspace vdn_hybrid_attn_proj_mxfp8_fwd needs (0 if invalid). */
+size_t vdn_hybrid_attn_proj_mxfp8_workspace_size(const vdn_layout_t* layout);
+
+/* vdn_hybrid_attn_proj_fwd with FP8 projections: the gated branches (x2,
+ * bf16) are quantized to MXFP8 and multiplied with pre-quantized w_o (codes
+ * w_q [d_model, 2*H*d], scales w_scales [d_model, 2*H*d/32], e.g. from
+ * vdn_mxfp8_quantize).  2*H*d must be a multiple of 128. */
+vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const void* v,
+                                            const void* text_k, const void* text_v,
+                                            const float* beta, const float* alpha,
+                                            const float* gate_logits, const void* w_q,
+                                            const void* w_scales, int32_t d_model,
+                                            const vdn_layout_t* layout, void* y,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
 /* Bytes of workspace vdn_hybrid_attn_proj_fwd needs (0 if the layout is
  * invalid): the vdn_hybrid_attn_fwd workspace plus x2.  Host only. */
 size_t vdn_hybrid_attn_proj_workspace_size(const vdn_layout_t* layout);

@@ -16,7 +16,8 @@ of 32 values along the contraction,
                                              magnitudes past 448 clamped to 448
   v_i ~ P_i * 2^X
 
-with X stored biased by 127 (E8M0); an all-zero block gets X = 0.  E4M3 here
+with X stored biased by 127 (E8M0, so X >= -127); an all-zero block gets
+X = 0.  E4M3 here
 is the OCP format: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
 subnormals down to 2^-9, largest finite 448, no infinities.
 """
@@ -55,6 +56,7 @@ def mx_quantize(x, block: int = BLOCK):
     amax = np.abs(xb).max(axis=-1)
     with np.errstate(divide="ignore"):
         X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0).astype(np.int64)
+    X = np.maximum(X, -127)                 # E8M0 holds 2^-127 .. 2^127
     P = round_e4m3(xb / (2.0 ** X)[..., None])
     return P.reshape(x.shape), X
 

@@ -190,3 +190,100 @@ def test_layer_with_projections_768p_sampled():
     err = rel_err(got, ref)
     print(f"768p layer+proj sampled ({len(tok)} tokens): rel err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# FP8 (MXFP8) projections
+# ---------------------------------------------------------------------------
+from oracle import mx_fp8 as MX  # noqa: E402
+
+
+def _codes_to_float(q):
+    return q.view(torch.float8_e4m3fn).to(torch.float64).cpu().numpy()
+
+
+def test_mxfp8_quantize_matches_oracle_exactly():
+    """Codes and scales equal the oracle's (same bf16 inputs, so the same
+    rounding decisions): blocks spanning many binades, zero blocks, values
+    that clamp at the top and underflow at the bottom of a block."""
+    require_gpu()
+    _announce("mxfp8 quantize")
+    rng = np.random.default_rng(11)
+    M, K = 257, 320
+    x = rng.standard_normal((M, K)) * np.exp2(rng.integers(-30, 30, (M, K // 32)).repeat(32, axis=1))
+    x[:, 64:96] = 0.0                                 # zero blocks
+    x[5, :32] = np.exp2(rng.integers(-20, 1, 32))     # one block over 20 binades
+    x[6, :32] = 1.9375 * 2.0 ** 8                     # rounds up to the block's clamp
+    xb = synth.round_bf16(x.astype(np.float32))
+    q, s = V.mxfp8_quantize(_bf16(xb))
+    torch.cuda.synchronize()
+    P, X = MX.mx_quantize(xb.astype(np.float64))
+    np.testing.assert_array_equal(s.cpu().numpy().astype(np.int64) - 127, X)
+    np.testing.assert_array_equal(_codes_to_float(q), P)
+
+
+FP8_SHAPES = [(1, 128, 8), (300, 256, 264), (513, 640, 520), (2048, 6144, 512)]
+
+
+@pytest.mark.parametrize("M,K,N", FP8_SHAPES, ids=[f"{m}x{k}x{n}" for m, k, n in FP8_SHAPES])
+def test_out_proj_mxfp8_product(M, K, N):
+    """The FP8 product against the oracle's exact product of the same
+    MX-quantized operands (fp32 accumulation and the bf16 output bound the
+    difference: 4e-3)."""
+    require_gpu()
+    _announce(f"out_proj mxfp8 M={M} K={K} N={N}")
+    x, w = synth.make_gemm_operands(M, K, N, seed=M + K + N + 1)
+    xq, xs = V.mxfp8_quantize(_bf16(x))
+    wq, ws = V.mxfp8_quantize(_bf16(w))
+    y = V.out_proj_mxfp8(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    ref = MX.output_projection_mxfp8(x, w)
+    err = rel_err(y.float().cpu().numpy(), ref)
+    print(f"out_proj mxfp8 {M}x{K}x{N}: rel err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
+def test_out_proj_mxfp8_768p_sampled_rows():
+    require_gpu()
+    M, K, N = 60480, 6144, 3072
+    _announce(f"out_proj mxfp8 768p M={M} K={K} N={N}")
+    x, w = synth.make_gemm_operands(M, K, N, seed=4243)
+    xq, xs = V.mxfp8_quantize(_bf16(x))
+    wq, ws = V.mxfp8_quantize(_bf16(w))
+    y = V.out_proj_mxfp8(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 255, 256, 30000, 30257, M - 193, M - 65, M - 2, M - 1])
+    ref = MX.output_projection_mxfp8(x[rows], w)
+    got = y[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    err = rel_err(got, ref)
+    print(f"out_proj mxfp8 768p sampled rows: rel err {err:.3e}")
+    assert err <= GEMM_TOL
+
+
+@pytest.mark.parametrize("case", PROJ_LAYER_CASES[:2], ids=[c["name"] for c in PROJ_LAYER_CASES[:2]])
+def test_layer_with_fp8_projections(case):
+    """The layer with FP8 projections against the oracle's FP8 projection of
+    its gated branches (rounded to bf16 first, as the layer hands them over):
+    bound 2e-2, the bf16 layer tolerance."""
+    require_gpu()
+    case = dict(case)
+    dm = case.pop("d_model")
+    w = custom(**case)
+    _announce(f"layer+proj fp8 {case['name']} d_model={dm}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    w_o = synth.make_proj_weight(dm, w.heads, w.head_dim, seed=w.seed + 1)
+    x2 = synth.round_bf16(O.gated_branches(inp, lay).astype(np.float32))
+    ref = MX.output_projection_mxfp8(x2.reshape(w.batch, w.video_tokens, -1), w_o)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    wq, ws = V.mxfp8_quantize(_bf16(w_o))
+    y = V.hybrid_attn_proj_mxfp8(dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+                                 dev["text_v"] if L else None, dev["beta"], dev["alpha"],
+                                 dev["gate_logits"], wq, ws, frames=w.frames,
+                                 tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+                                 window_chunks=w.window_chunks)
+    torch.cuda.synchronize()
+    err = rel_err(y.float().cpu().numpy(), ref)
+    print(f"{case['name']}: layer + fp8 proj rel err {err:.3e}")
+    assert err <= TOL["bf16"]

@@ -18,7 +18,8 @@ __all__ = [
     "hybrid_attn",
     "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "vda_gram", "vda_factor_scan",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
-    "bwd_workspace_size", "make_layout",
+    "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
+    "make_layout",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,7 +36,9 @@ EXPORTED_SYMBOLS = (
     "vdn_vda_factor_scan_workspace_size",
     "vdn_vda_factor_scan", "vdn_merge", "vdn_softmax_branches_fwd", "vdn_out_proj",
     "vdn_hybrid_attn_proj_workspace_size", "vdn_hybrid_attn_proj_fwd",
-    "vdn_hybrid_attn_bwd_workspace_size", "vdn_hybrid_attn_bwd",
+    "vdn_hybrid_attn_bwd_workspace_size", "vdn_hybrid_attn_bwd", "vdn_mxfp8_quantize",
+    "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
+    "vdn_hybrid_attn_proj_mxfp8_fwd",
 )
 
 
@@ -114,6 +117,15 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_bwd_workspace_size.restype = sz
         L.vdn_hybrid_attn_bwd.argtypes = [vp] * 9 + [lp] + [vp] * 9 + [sz, vp]
         L.vdn_hybrid_attn_bwd.restype = ctypes.c_int
+        L.vdn_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+        L.vdn_mxfp8_quantize.restype = ctypes.c_int
+        L.vdn_out_proj_mxfp8.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int32, vp, vp]
+        L.vdn_out_proj_mxfp8.restype = ctypes.c_int
+        L.vdn_hybrid_attn_proj_mxfp8_workspace_size.argtypes = [lp]
+        L.vdn_hybrid_attn_proj_mxfp8_workspace_size.restype = sz
+        L.vdn_hybrid_attn_proj_mxfp8_fwd.argtypes = [vp] * 10 + [ctypes.c_int32, lp, vp, vp, sz, vp]
+        L.vdn_hybrid_attn_proj_mxfp8_fwd.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -365,6 +377,77 @@ def hybrid_attn_proj(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_o, *, 
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(w_o), dm, ctypes.byref(lay), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vdn_hybrid_attn_proj_fwd")
+    return out
+
+
+def mxfp8_quantize(x):
+    """MXFP8 quantization (``vdn_mxfp8_quantize``) of a bf16 [..., K] tensor:
+    returns (codes uint8 [..., K], E8M0 scales uint8 [..., K/32])."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("mxfp8_quantize takes bf16")
+    K = x.shape[-1]
+    _expect(x, x.shape, torch.bfloat16, "x")
+    M = x.numel() // K if K else 0
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty(tuple(x.shape[:-1]) + (K // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib().vdn_mxfp8_quantize(_ptr(x), M, K, _ptr(q), _ptr(s), _stream()),
+           "vdn_mxfp8_quantize")
+    return q, s
+
+
+def out_proj_mxfp8(xq, xs, wq, ws, out=None) -> torch.Tensor:
+    """FP8 projection (``vdn_out_proj_mxfp8``) from MXFP8 operands: x codes
+    [..., K] + scales [..., K/32], w codes [N, K] + scales [N, K/32]; returns
+    bf16 [..., N]."""
+    K = xq.shape[-1]
+    N = wq.shape[0]
+    for name, t in (("xq", xq), ("xs", xs), ("wq", wq), ("ws", ws)):
+        _expect(t, t.shape, torch.uint8, name)
+    if wq.shape != (N, K) or ws.shape != (N, K // 32) or xs.shape[-1] != K // 32:
+        raise ValueError("mxfp8 operand shapes do not match")
+    M = xq.numel() // K
+    if out is None:
+        out = torch.empty(tuple(xq.shape[:-1]) + (N,), dtype=torch.bfloat16, device=xq.device)
+    _expect(out, tuple(xq.shape[:-1]) + (N,), torch.bfloat16, "out")
+    _check(lib().vdn_out_proj_mxfp8(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, K, N, _ptr(out),
+                                    _stream()), "vdn_out_proj_mxfp8")
+    return out
+
+
+def hybrid_attn_proj_mxfp8(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_q, w_scales, *,
+                           frames, tokens_per_frame, chunk_frames=5, window_chunks=1,
+                           anchor_first=True, anchor_last=True, softmax_scale=0.0, rms_eps=0.0,
+                           out=None, workspace=None) -> torch.Tensor:
+    """The layer with FP8 output projections (``vdn_hybrid_attn_proj_mxfp8_fwd``):
+    w_q / w_scales from ``mxfp8_quantize(w_o)``; returns y bf16 [B, N, d_model]."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    K = 2 * H * d
+    if w_q.dim() != 2 or w_q.shape[1] != K or w_scales.shape != (w_q.shape[0], K // 32):
+        raise ValueError(f"w_q: expected [d_model, {K}] codes and [d_model, {K // 32}] scales")
+    _expect(w_q, w_q.shape, torch.uint8, "w_q")
+    _expect(w_scales, w_scales.shape, torch.uint8, "w_scales")
+    dm = w_q.shape[0]
+    if out is None:
+        out = torch.empty((B, N, dm), dtype=torch.bfloat16, device=q.device)
+    _expect(out, (B, N, dm), torch.bfloat16, "out")
+    if workspace is None:
+        workspace = torch.empty(lib().vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay)),
+                                dtype=torch.uint8, device=q.device)
+    st = lib().vdn_hybrid_attn_proj_mxfp8_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(w_q), _ptr(w_scales), dm,
+        ctypes.byref(lay), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_proj_mxfp8_fwd")
     return out
 
 

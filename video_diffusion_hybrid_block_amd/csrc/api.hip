@@ -166,6 +166,27 @@ vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, in
   return hip_status(launch_proj(x, w, M, K, N, y, stream));
 }
 
+vdn_status_t vdn_mxfp8_quantize(const void* x, int64_t M, int32_t K, void* q, void* scales,
+                                hipStream_t stream) {
+  if (!x || !q || !scales) return VDN_ERR_NULL_ARG;
+  if (M < 1 || K < 1) return VDN_ERR_BAD_SHAPE;
+  if (!mx_quant_shape_ok(M, K)) return VDN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(q)) return VDN_ERR_MISALIGNED;
+  return hip_status(launch_mx_quant(x, M, K, q, scales, stream));
+}
+
+vdn_status_t vdn_out_proj_mxfp8(const void* xq, const void* xs, const void* wq, const void* ws,
+                                int64_t M, int32_t K, int32_t N, void* y, hipStream_t stream) {
+  if (!xq || !xs || !wq || !ws || !y) return VDN_ERR_NULL_ARG;
+  if (M < 1 || K < 1 || N < 1) return VDN_ERR_BAD_SHAPE;
+  if (!proj_mxfp8_shape_ok(M, K, N)) return VDN_ERR_UNSUPPORTED;
+  if ((M + 255) / 256 * ((N + 255) / 256) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || ((uintptr_t)xs & 3u) ||
+      ((uintptr_t)ws & 3u))
+    return VDN_ERR_MISALIGNED;
+  return hip_status(launch_proj_mxfp8(xq, xs, wq, ws, M, K, N, y, stream));
+}
+
 vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
                           const float* beta, const vdn_layout_t* layout, float* A_out,
                           float* B_out, hipStream_t stream) {
@@ -367,6 +388,59 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   if (e == hipSuccess)
     e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
                         stream);
+  return hip_status(e);
+}
+
+size_t vdn_hybrid_attn_proj_mxfp8_workspace_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  const vdn_layout_t& l = *layout;
+  const size_t M = (size_t)l.batch * l.frames * l.tokens_per_frame;
+  const size_t K = 2 * (size_t)l.heads * l.head_dim_k;
+  return align256(align256(proj_ws_total(l) + M * K) + M * (K / 32));
+}
+
+vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const void* v,
+                                            const void* text_k, const void* text_v,
+                                            const float* beta, const float* alpha,
+                                            const float* gate_logits, const void* w_q,
+                                            const void* w_scales, int32_t d_model,
+                                            const vdn_layout_t* layout, void* y, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (d_model < 1) return VDN_ERR_BAD_SHAPE;
+  const vdn_layout_t& l = *layout;
+  const long M = (long)l.batch * l.frames * l.tokens_per_frame;
+  const int K = 2 * l.heads * l.head_dim_k;
+  if (!softmax_merge_fusable(l) || !proj_mxfp8_shape_ok(M, K, d_model)) return VDN_ERR_UNSUPPORTED;
+  if ((M + 255) / 256 * ((d_model + 255) / 256) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !w_q || !w_scales || !y ||
+      !workspace || !text_ok(l, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(w_q) || ((uintptr_t)w_scales & 3u) || !aligned16(y) ||
+      !aligned16(workspace) || !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < vdn_hybrid_attn_proj_mxfp8_workspace_size(layout))
+    return VDN_ERR_WORKSPACE_TOO_SMALL;
+  const Plan p = make_plan(l);
+  char* ws = (char*)workspace;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* Sf = (float*)(ws + p.sf_off);
+  float* Sb = (float*)(ws + p.sb_off);
+  float* R = (float*)(ws + p.r_off);
+  void* x2 = ws + proj_x2_off(l);
+  char* xq = ws + proj_ws_total(l);
+  char* xs = ws + align256(proj_ws_total(l) + (size_t)M * K);
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  if (e == hipSuccess)
+    e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
+                             true, x2, ws + p.vt_off, stream);
+  if (e == hipSuccess) e = launch_mx_quant(x2, M, K, xq, xs, stream);
+  if (e == hipSuccess) e = launch_proj_mxfp8(xq, xs, w_q, w_scales, M, K, d_model, y, stream);
   return hip_status(e);
 }
 

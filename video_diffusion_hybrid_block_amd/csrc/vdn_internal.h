@@ -279,5 +279,13 @@ hipError_t launch_gram_bwd(const void* k, const void* v, const void* tk, const v
 // accumulation); needs K a positive multiple of 64 and N a multiple of 8.
 bool proj_shape_ok(long M, int K, int N);
 hipError_t launch_proj(const void* x, const void* w, long M, int K, int N, void* y, hipStream_t s);
+// MXFP8 (E4M3 codes + one E8M0 scale per 32 values along K): quantization of
+// a bf16 [M][K] matrix (K a multiple of 32) and the product from quantized
+// operands (K a multiple of 128, N of 8).
+bool mx_quant_shape_ok(long M, int K);
+hipError_t launch_mx_quant(const void* x, long M, int K, void* q, void* scales, hipStream_t s);
+bool proj_mxfp8_shape_ok(long M, int K, int N);
+hipError_t launch_proj_mxfp8(const void* xq, const void* xs, const void* wq, const void* ws,
+                             long M, int K, int N, void* y, hipStream_t s);
 
 }  // namespace vdn

@@ -518,24 +518,32 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  // S^T = K Q^T for the tile in buffer buf: all K fragments, then the MFMAs.
+  // S^T = K Q^T for the tile in buffer buf: all K fragments (in the order the
+  // MFMAs consume them), then the MFMAs.  The scheduling groups keep that
+  // order: left alone, the compiler hoists the V^T reads of soft_pv into this
+  // phase and then, short of registers, reads K two fragments at a time with
+  // a full LDS wait before every other MFMA.
   auto scores = [&](int buf, f32x16 (&s)[2]) {
     const char VDN_LDS* kt = lds + buf * BUFB + kread;
     bf16x8 kf[2][D / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kf[kb][ks] = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
+      for (int kb = 0; kb < 2; ++kb) kf[kb][ks] = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ks], qreg[ks], s[kb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
   };
   // Online softmax of tile `it` (scores s, buffer buf) and O^T += V^T P^T.
   auto soft_pv = [&](int it, int buf, f32x16 (&s)[2]) {
-    // V^T fragments, read while the softmax runs on the VALU
+    // V^T fragments, read while the softmax runs on the VALU (not before the
+    // score MFMAs: the fence keeps their registers free for the K fragments)
+    __builtin_amdgcn_sched_barrier(0);
     const char VDN_LDS* vt = lds + buf * BUFB + vread;
     bf16x8 vf[4][D / 32];
 #pragma unroll

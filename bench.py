@@ -243,7 +243,8 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / n
 
-        # FP8 (MXFP8) form: weights quantized once, activations per call
+        # FP8 (MXFP8) form: weights quantized once; the layer's softmax kernel
+        # writes the activations (both gated branches) as MXFP8 itself
         wq, wsc = V.mxfp8_quantize(w_o)
         xq, xsc = V.mxfp8_quantize(x2)
         pws8 = torch.empty(V.lib().vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay)),
@@ -257,16 +258,12 @@ def main():
         def product8():
             V.out_proj_mxfp8(xq, xsc, wq, wsc, out=y2)
 
-        def quant8():
-            V.mxfp8_quantize(x2)
-
         print("[bench] layer with output projections", file=sys.stderr, flush=True)
         lp_ms = timed(layer_proj, args.steps)
         pr_ms = timed(product, args.steps)
         lib_ms = timed(library_product, args.steps)
         lp8_ms = timed(layer_proj8, args.steps)
         pr8_ms = timed(product8, args.steps)
-        q8_ms = timed(quant8, args.steps)
         pflops = 2.0 * w.batch * w.video_tokens * (2 * H * d) * dm
         proj = {"d_model": dm, "layer_with_proj_ms": round(lp_ms, 4),
                 "video_tokens_per_s": round(w.batch * w.video_tokens / (lp_ms / 1e3), 1),
@@ -280,7 +277,8 @@ def main():
                         "proj_ms": round(pr8_ms, 4),
                         "proj_tflops": round(pflops / (pr8_ms / 1e3) / 1e12, 1),
                         "proj_frac_fp8_peak": round(pflops / (pr8_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-                        "activation_quantize_ms": round(q8_ms, 4),
+                        "activations": "quantized in the softmax kernel's epilogue "
+                                       "(softmax_vt_kernel<128, 4>)",
                         "layer_with_proj_ms": round(lp8_ms, 4),
                         "video_tokens_per_s": round(w.batch * w.video_tokens / (lp8_ms / 1e3), 1)}}
         del pws, pws8, y, y2, x2, w_o, wt, xq, xsc, wq, wsc

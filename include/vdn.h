@@ -203,13 +203,30 @@ vdn_status_t vdn_mxfp8_quantize(const void* x, int64_t M, int32_t K, void* q, vo
 vdn_status_t vdn_out_proj_mxfp8(const void* xq, const void* xs, const void* wq, const void* ws,
                                 int64_t M, int32_t K, int32_t N, void* y, hipStream_t stream);
 
+/* vdn_softmax_branches_fwd with the two gated branches written as MXFP8
+ * instead of bf16: quantized from the fp32 values inside the same kernel, in
+ * the format above (blocks of 32 consecutive d of one head and branch).
+ * codes: [B*T*P, 2*H*d] bytes, 16-byte aligned (per token the softmax branch
+ * of every head, then the linear branch, as x2); scales: [B*T*P, 2*H*d/32]
+ * bytes.  Same inputs, workspace and support (d in {32, 64, 128}, P and L
+ * multiples of 8) as vdn_softmax_branches_fwd, else VDN_ERR_UNSUPPORTED.
+ * The activation operand of vdn_out_proj_mxfp8.
+ * [PaperDaily §三, figure 3; deepmagic blog, section 實測數據] */
+vdn_status_t vdn_softmax_branches_mxfp8_fwd(const void* q, const void* k, const void* v,
+                                            const void* text_k, const void* text_v,
+                                            const float* R, const float* gate_logits,
+                                            const vdn_layout_t* layout, void* codes,
+                                            void* scales, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace vdn_hybrid_attn_proj_mxfp8_fwd needs (0 if invalid). */
 size_t vdn_hybrid_attn_proj_mxfp8_workspace_size(const vdn_layout_t* layout);
 
-/* vdn_hybrid_attn_proj_fwd with FP8 projections: the gated branches (x2,
- * bf16) are quantized to MXFP8 and multiplied with pre-quantized w_o (codes
- * w_q [d_model, 2*H*d], scales w_scales [d_model, 2*H*d/32], e.g. from
- * vdn_mxfp8_quantize).  2*H*d must be a multiple of 128. */
+/* vdn_hybrid_attn_proj_fwd with FP8 projections: the softmax kernel writes
+ * the gated branches as MXFP8 (vdn_softmax_branches_mxfp8_fwd), which are
+ * multiplied with pre-quantized w_o (codes w_q [d_model, 2*H*d], scales
+ * w_scales [d_model, 2*H*d/32], e.g. from vdn_mxfp8_quantize).  2*H*d must
+ * be a multiple of 128; d_model of 8. */
 vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const void* v,
                                             const void* text_k, const void* text_v,
                                             const float* beta, const float* alpha,

@@ -231,3 +231,57 @@ def test_projection_entry_points_reject_bad_arguments_before_launch():
     assert lib.vdn_hybrid_attn_proj_fwd(*a) == 4
     a = list(args); a[13] = ws - 256
     assert lib.vdn_hybrid_attn_proj_fwd(*a) == 5
+
+
+def test_fp8_entry_points_reject_bad_arguments_before_launch():
+    lib = V.lib()
+    ok = ctypes.c_void_p(0x10000)         # aligned fake pointers: never dereferenced
+    odd = ctypes.c_void_p(0x10004)        # 4-byte but not 16-byte aligned
+    odd1 = ctypes.c_void_p(0x10001)
+    nul = None
+    # quantization: K a multiple of 32, M >= 1, x and q 16-byte aligned
+    assert lib.vdn_mxfp8_quantize(nul, 4, 64, ok, ok, nul) == 1
+    assert lib.vdn_mxfp8_quantize(ok, 0, 64, ok, ok, nul) == 2
+    assert lib.vdn_mxfp8_quantize(ok, 4, 48, ok, ok, nul) == 3
+    assert lib.vdn_mxfp8_quantize(odd, 4, 64, ok, ok, nul) == 4
+    # FP8 product: K a multiple of 128, N of 8; scales 4-byte aligned
+    assert lib.vdn_out_proj_mxfp8(ok, nul, ok, ok, 10, 128, 64, ok, nul) == 1
+    assert lib.vdn_out_proj_mxfp8(ok, ok, ok, ok, 0, 128, 64, ok, nul) == 2
+    assert lib.vdn_out_proj_mxfp8(ok, ok, ok, ok, 10, 96, 64, ok, nul) == 3
+    assert lib.vdn_out_proj_mxfp8(ok, ok, ok, ok, 10, 128, 60, ok, nul) == 3
+    assert lib.vdn_out_proj_mxfp8(odd, ok, ok, ok, 10, 128, 64, ok, nul) == 4
+    assert lib.vdn_out_proj_mxfp8(ok, odd1, ok, ok, 10, 128, 64, ok, nul) == 4
+    # branches quantized in the softmax kernel: same coverage as the bf16 branches
+    lay_vt = _lay(batch=1, heads=2, frames=2, tokens_per_frame=8, text_tokens=0, head_dim=32)
+    lay_16 = _lay(batch=1, heads=1, frames=2, tokens_per_frame=4, text_tokens=0, head_dim=16)
+    br = [ok, ok, ok, nul, nul, ok, ok, ctypes.byref(lay_vt), ok, ok, ok, 1 << 40, nul]
+    a = list(br); a[7] = ctypes.byref(lay_16)
+    assert lib.vdn_softmax_branches_mxfp8_fwd(*a) == 3
+    a = list(br); a[9] = nul
+    assert lib.vdn_softmax_branches_mxfp8_fwd(*a) == 1
+    a = list(br); a[8] = odd
+    assert lib.vdn_softmax_branches_mxfp8_fwd(*a) == 4
+    a = list(br); a[11] = 16
+    assert lib.vdn_softmax_branches_mxfp8_fwd(*a) == 5
+    # the layer with FP8 projections: its workspace holds the plan, the codes
+    # (N * 2*H*d bytes) and the scales, and no bf16 copy of the branches
+    ws = lib.vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay_vt))
+    n_tok, k = 2 * 8, 2 * 2 * 32
+    assert ws >= V.workspace_size(lay_vt) + n_tok * k + n_tok * k // 32
+    assert ws < V.proj_workspace_size(lay_vt) + n_tok * k + n_tok * k // 32
+    args = [ok, ok, ok, nul, nul, ok, ok, ok, ok, ok, 64, ctypes.byref(lay_vt), ok, ok, ws, nul]
+    a = list(args); a[8] = nul
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 1
+    a = list(args); a[10] = 0
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 2
+    a = list(args); a[10] = 12
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 3
+    a = list(args); a[11] = ctypes.byref(lay_16)
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 3
+    lay_k64 = _lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=0, head_dim=32)
+    a = list(args); a[11] = ctypes.byref(lay_k64)          # 2*H*d = 64: not a multiple of 128
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 3
+    a = list(args); a[12] = odd
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 4
+    a = list(args); a[14] = ws - 256
+    assert lib.vdn_hybrid_attn_proj_mxfp8_fwd(*a) == 5

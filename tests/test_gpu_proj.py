@@ -7,7 +7,11 @@ Stages checked against the oracle on the same seeded inputs:
   oracle.gated_branches, each branch on its own;
 - the layer with its projections (vdn_hybrid_attn_proj_fwd) against
   oracle.output_projection(oracle.gated_branches(...)), small shapes in full
-  and the 768p shape on sampled tokens.
+  and the 768p shape on sampled tokens;
+- the FP8 (MXFP8) forms: quantization bit-exact against oracle.mx_fp8, the
+  FP8 product against the exact product of the quantized operands, the
+  branches quantized inside the softmax kernel against the exact branches
+  and their MX quantization, and the layer with FP8 projections.
 
 Metric: relative Frobenius error.  Bounds: the product rounds each output to
 bf16 (relative 2^-9) after an fp32 sum, so 4e-3; the branch and layer outputs
@@ -222,6 +226,74 @@ def test_mxfp8_quantize_matches_oracle_exactly():
     np.testing.assert_array_equal(_codes_to_float(q), P)
 
 
+def _e4m3_half_step(v, X):
+    """Half the E4M3 spacing at |v| in a block with exponent X (scaled units
+    u = v / 2^X: 3 mantissa bits, no binade below 2^-6), plus what the clamp
+    at 448 removes; in the units of v."""
+    u = np.abs(v) / np.exp2(X)
+    with np.errstate(divide="ignore"):
+        e = np.maximum(np.floor(np.log2(np.where(u > 0, u, 1.0))), -6.0)
+    return (0.5 * np.exp2(e - 3) + np.maximum(u - 448.0, 0.0)) * np.exp2(X)
+
+
+@pytest.mark.parametrize("case", BRANCH_CASES, ids=[c["name"] for c in BRANCH_CASES])
+def test_stage_softmax_branches_mxfp8(case):
+    """The gated branches written as MXFP8 by the softmax kernel
+    (vdn_softmax_branches_mxfp8_fwd) against the oracle's exact branches and
+    their MX quantization.  The kernel quantizes its own fp32 values, so where
+    a value or a block maximum sits next to a rounding boundary either side
+    of it is a valid result; what is checked:
+    - block exponents equal the oracle's, or differ by one (a block maximum
+      next to a power of two), for at least 99 % of blocks equal;
+    - every element lies within half an E4M3 step (at the kernel's exponent)
+      of the exact branch value, plus 1e-2 of its block maximum for the
+      branch's own bf16 arithmetic (the bound of the bf16 branch test);
+    - per branch, the dequantized values are as close to the exact ones as
+      the oracle's own quantization: rel err <= 1.1 x the oracle's + 2e-3."""
+    require_gpu()
+    w = custom(**case)
+    _announce(f"branches mxfp8 {case['name']}")
+    inp = synth.make_inputs(w)
+    lay = oracle_layout(w)
+    B, N, H, d = w.batch, w.video_tokens, w.heads, w.head_dim
+    ref = O.gated_branches(inp, lay).reshape(B * N, 2 * H * d)
+    P_ref, X_ref = MX.mx_quantize(ref)
+    R = oracle_chunk_reads(inp, lay, w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    codes, scales = V.softmax_branches_mxfp8(dev["q"], dev["k"], dev["v"],
+                                             dev["text_k"] if L else None,
+                                             dev["text_v"] if L else None,
+                                             torch.from_numpy(R).cuda(), dev["gate_logits"],
+                                             frames=w.frames, tokens_per_frame=w.tokens_per_frame,
+                                             chunk_frames=w.chunk_frames,
+                                             window_chunks=w.window_chunks)
+    torch.cuda.synchronize()
+    X = scales.cpu().numpy().astype(np.int64) - 127
+    deq = MX.mx_dequantize(_codes_to_float(codes), X)
+    assert np.isfinite(deq).all()
+    assert np.abs(X - X_ref).max() <= 1
+    same = (X == X_ref).mean()
+    amax = np.abs(ref.reshape(B * N, -1, 32)).max(axis=-1)
+    delta = 1e-2 * np.repeat(amax, 32, axis=1)
+    # the spacing taken at |v| + delta covers a kernel value one binade up
+    bound = _e4m3_half_step(np.abs(ref) + delta, np.repeat(X, 32, axis=1)) * (1 + 2.0 ** -8) + delta
+    excess = (np.abs(deq - ref) - bound).max()
+    deq_ref = MX.mx_dequantize(P_ref, X_ref)
+    half = H * d
+    errs = []
+    for br in range(2):
+        cols = slice(br * half, (br + 1) * half)
+        errs.append((rel_err(deq[:, cols], ref[:, cols]), rel_err(deq_ref[:, cols], ref[:, cols])))
+    print(f"{case['name']}: exponents equal {same:.4f}, worst excess over the element bound "
+          f"{excess:.3e}; rel err (kernel, oracle quantization) softmax {errs[0][0]:.3e}, "
+          f"{errs[0][1]:.3e}; linear {errs[1][0]:.3e}, {errs[1][1]:.3e}")
+    assert same >= 0.99
+    assert excess <= 0.0
+    for e_k, e_o in errs:
+        assert e_k <= 1.1 * e_o + 2e-3
+
+
 FP8_SHAPES = [(1, 128, 8), (300, 256, 264), (513, 640, 520), (2048, 6144, 512)]
 
 
@@ -263,8 +335,8 @@ def test_out_proj_mxfp8_768p_sampled_rows():
 @pytest.mark.parametrize("case", PROJ_LAYER_CASES[:2], ids=[c["name"] for c in PROJ_LAYER_CASES[:2]])
 def test_layer_with_fp8_projections(case):
     """The layer with FP8 projections against the oracle's FP8 projection of
-    its gated branches (rounded to bf16 first, as the layer hands them over):
-    bound 2e-2, the bf16 layer tolerance."""
+    its exact gated branches (the softmax kernel quantizes its fp32 branch
+    values directly): bound 2e-2, the bf16 layer tolerance."""
     require_gpu()
     case = dict(case)
     dm = case.pop("d_model")
@@ -273,7 +345,7 @@ def test_layer_with_fp8_projections(case):
     inp = synth.make_inputs(w)
     lay = oracle_layout(w)
     w_o = synth.make_proj_weight(dm, w.heads, w.head_dim, seed=w.seed + 1)
-    x2 = synth.round_bf16(O.gated_branches(inp, lay).astype(np.float32))
+    x2 = O.gated_branches(inp, lay)
     ref = MX.output_projection_mxfp8(x2.reshape(w.batch, w.video_tokens, -1), w_o)
     dev = to_dev(inp, w.dtype)
     L = w.text_tokens

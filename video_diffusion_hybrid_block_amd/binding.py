@@ -16,7 +16,8 @@ __all__ = [
     "VdnError", "Layout", "lib", "library_path", "version", "validate_layout",
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
-    "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "vda_gram", "vda_factor_scan",
+    "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "softmax_branches_mxfp8",
+    "vda_gram", "vda_factor_scan",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
     "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
     "make_layout",
@@ -38,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "vdn_hybrid_attn_proj_workspace_size", "vdn_hybrid_attn_proj_fwd",
     "vdn_hybrid_attn_bwd_workspace_size", "vdn_hybrid_attn_bwd", "vdn_mxfp8_quantize",
     "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
-    "vdn_hybrid_attn_proj_mxfp8_fwd",
+    "vdn_hybrid_attn_proj_mxfp8_fwd", "vdn_softmax_branches_mxfp8_fwd",
 )
 
 
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_merge.argtypes = [vp, vp, vp, vp, lp, vp, vp]
         L.vdn_softmax_branches_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, vp, vp, sz, vp]
         L.vdn_softmax_branches_fwd.restype = ctypes.c_int
+        L.vdn_softmax_branches_mxfp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, lp, vp, vp, vp, sz, vp]
+        L.vdn_softmax_branches_mxfp8_fwd.restype = ctypes.c_int
         L.vdn_out_proj.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.vdn_out_proj.restype = ctypes.c_int
         L.vdn_hybrid_attn_proj_workspace_size.argtypes = [lp]
@@ -320,6 +323,37 @@ def softmax_branches_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tok
                                           _ptr(workspace), nbytes, _stream()),
            "vdn_softmax_branches_fwd")
     return out
+
+
+def softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, *, frames, tokens_per_frame,
+                           chunk_frames=5, window_chunks=1, anchor_first=True, anchor_last=True,
+                           softmax_scale=0.0, rms_eps=0.0, workspace=None):
+    """The two gated branches as MXFP8 (``vdn_softmax_branches_mxfp8_fwd``):
+    returns (codes uint8 [B*N, 2*H*d], scales uint8 [B*N, 2*H*d/32]); per
+    token the softmax branch of every head, then the linear branch."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    _expect(R, (B, H, num_chunks(lay) + 1, d, d), torch.float32, "R")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    K = 2 * H * d
+    codes = torch.empty((B * N, K), dtype=torch.uint8, device=q.device)
+    scales = torch.empty((B * N, K // 32), dtype=torch.uint8, device=q.device)
+    L = lay.text_tokens
+    need = softmax_workspace_size(lay)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().vdn_softmax_branches_mxfp8_fwd(_ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(text_k if L else None),
+                                                _ptr(text_v if L else None), _ptr(R),
+                                                _ptr(gate_logits), ctypes.byref(lay), _ptr(codes),
+                                                _ptr(scales), _ptr(workspace), nbytes, _stream()),
+           "vdn_softmax_branches_mxfp8_fwd")
+    return codes, scales
 
 
 def out_proj(x, w, out=None) -> torch.Tensor:

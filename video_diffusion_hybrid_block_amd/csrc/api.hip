@@ -156,6 +156,29 @@ vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* 
                                          stream));
 }
 
+vdn_status_t vdn_softmax_branches_mxfp8_fwd(const void* q, const void* k, const void* v,
+                                            const void* text_k, const void* text_v,
+                                            const float* R, const float* gate_logits,
+                                            const vdn_layout_t* layout, void* codes, void* scales,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!softmax_merge_fusable(*layout)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !R || !gate_logits || !codes || !scales ||
+      !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  const size_t need = softmax_ws_bytes(*layout);
+  if (need > 0 && !workspace) return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(R) || !aligned16(gate_logits) ||
+      !aligned16(codes) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
+    return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, *layout,
+                                                  eff_scale(*layout), eff_eps(*layout), codes,
+                                                  scales, workspace, stream));
+}
+
 vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, int32_t N, void* y,
                           hipStream_t stream) {
   if (!x || !w || !y) return VDN_ERR_NULL_ARG;
@@ -365,7 +388,7 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   if (e == hipSuccess) e = launch_factor(A, l, false, stream);
   if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream, states);
   // softmax forward with the merge backward in its epilogue
-  const MergeBwdIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, lse};
+  const EpilogueIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, lse};
   if (e == hipSuccess)
     e = launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
                                  eff_eps(l), io, ws + p.vt_off, stream);
@@ -391,12 +414,21 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   return hip_status(e);
 }
 
+// Workspace of the layer with FP8 projections: the layer's plan (VDA
+// buffers, V^T copy), then the MXFP8 codes [M][K] and scales [M][K/32] of the
+// two gated branches.
+static size_t fp8_codes_off(const vdn_layout_t& l) { return align256(make_plan(l).total); }
+static size_t fp8_scales_off(const vdn_layout_t& l) {
+  const size_t M = (size_t)l.batch * l.frames * l.tokens_per_frame;
+  return align256(fp8_codes_off(l) + M * 2 * l.heads * l.head_dim_k);
+}
+
 size_t vdn_hybrid_attn_proj_mxfp8_workspace_size(const vdn_layout_t* layout) {
   if (check_layout(layout) != VDN_OK) return 0;
   const vdn_layout_t& l = *layout;
   const size_t M = (size_t)l.batch * l.frames * l.tokens_per_frame;
   const size_t K = 2 * (size_t)l.heads * l.head_dim_k;
-  return align256(align256(proj_ws_total(l) + M * K) + M * (K / 32));
+  return align256(fp8_scales_off(l) + M * (K / 32));
 }
 
 vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const void* v,
@@ -430,16 +462,14 @@ vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const 
   float* Sf = (float*)(ws + p.sf_off);
   float* Sb = (float*)(ws + p.sb_off);
   float* R = (float*)(ws + p.r_off);
-  void* x2 = ws + proj_x2_off(l);
-  char* xq = ws + proj_ws_total(l);
-  char* xs = ws + align256(proj_ws_total(l) + (size_t)M * K);
+  char* xq = ws + fp8_codes_off(l);
+  char* xs = ws + fp8_scales_off(l);
   hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
   if (e == hipSuccess) e = launch_factor(A, l, false, stream);
   if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
   if (e == hipSuccess)
-    e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
-                             true, x2, ws + p.vt_off, stream);
-  if (e == hipSuccess) e = launch_mx_quant(x2, M, K, xq, xs, stream);
+    e = launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                      eff_eps(l), xq, xs, ws + p.vt_off, stream);
   if (e == hipSuccess) e = launch_proj_mxfp8(xq, xs, w_q, w_scales, M, K, d_model, y, stream);
   return hip_status(e);
 }

@@ -175,23 +175,10 @@ mx_quant_kernel(const bf16* __restrict__ x, uint8_t* __restrict__ qo, uint8_t* _
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  int X = 0;
-  if (amax > 0.f) {
-    int ex;
-    frexpf(amax, &ex);                 // amax = f 2^ex, f in [0.5, 1)
-    X = ex - 1 - 8;
-    if (X < -127) X = -127;
-  }
+  const int X = mx_block_exp(amax);
   uint32_t w[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    float c4[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c4[e] = fminf(fmaxf(ldexpf(v[u * 4 + e], -X), -448.f), 448.f);
-    int acc = __builtin_amdgcn_cvt_pk_fp8_f32(c4[0], c4[1], 0, false);   // bytes 0, 1
-    acc = __builtin_amdgcn_cvt_pk_fp8_f32(c4[2], c4[3], acc, true);      // bytes 2, 3
-    w[u] = (uint32_t)acc;
-  }
+  for (int u = 0; u < 8; ++u) w[u] = mx_pack4(v[u * 4], v[u * 4 + 1], v[u * 4 + 2], v[u * 4 + 3], X);
   u32x4* dst = (u32x4*)(qo + i * 32);
   dst[0] = u32x4{w[0], w[1], w[2], w[3]};
   dst[1] = u32x4{w[4], w[5], w[6], w[7]};

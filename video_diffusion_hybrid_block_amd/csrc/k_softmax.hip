@@ -390,14 +390,16 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // of the merged output instead and writes what the backward needs: the gate
 // logits' gradients, dO_soft = sigmoid(l0) dO (bf16), the row statistics of
 // the softmax (its log-sum-exp in exp2 units and D = dO_soft . O_soft) and
-// the gradient of the linear read before RMSNorm.
+// the gradient of the linear read before RMSNorm.  MODE 4 writes the two
+// gated branches of MODE 2 as MXFP8 codes and block scales (the activation
+// operand of the FP8 output projection), quantized from the fp32 values.
 template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                   const bf16* __restrict__ tk, const bf16* __restrict__ vtg, int nl8,
                   bf16* __restrict__ o, Geo g, int B, int H, int tpf, float c,
                   const float* __restrict__ R, const float* __restrict__ gates, float eps,
-                  MergeBwdIO bio) {
+                  EpilogueIO bio) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 3;
   constexpr int KCH = D / 8;
   constexpr int KST = 2 * D + 16, KSL = KST / 16;    // K row stride (bytes), slots
@@ -748,6 +750,36 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       return;
     }
     const float g0 = sigmoidf(gl.x) * inv, g1 = sigmoidf(gl.y) * rinv;
+    if constexpr (MODE == 4) {
+      // MXFP8 branches: block db of a branch holds d in [32 db, 32 db + 32)
+      // of this head, 16 values in this lane and 16 in lane l ^ 32 (same
+      // query, so both lanes share qvalid and the block maximum is one swap).
+      const size_t row = (size_t)w.b * N + qrow;
+      uint8_t* crow = (uint8_t*)o + row * (2 * H * D) + (size_t)w.h * D;
+      uint8_t* srow = bio.mx_scales + row * (2 * H * D / 32) + w.h * (D / 32);
+#pragma unroll
+      for (int br = 0; br < 2; ++br) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          float x[16];
+          float amax = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            x[j] = br == 0 ? g0 * oacc[db][j] : g1 * lin[db][j];
+            amax = fmaxf(amax, fabsf(x[j]));
+          }
+          const int X = mx_block_exp(xhalf_max(amax));
+          if (qvalid) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              *(uint32_t*)(crow + br * H * D + db * 32 + jj * 8 + half * 4) =
+                  mx_pack4(x[jj * 4], x[jj * 4 + 1], x[jj * 4 + 2], x[jj * 4 + 3], X);
+            if (half == 0) srow[br * (H * D / 32) + db] = (uint8_t)(X + 127);
+          }
+        }
+      }
+      return;
+    }
     if (qvalid) {
       if constexpr (MODE == 1) {
         bf16* orow = o + qoff;
@@ -823,7 +855,7 @@ template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
                        const float* R, const float* gates, float eps, int mode, hipStream_t s,
-                       const MergeBwdIO& bio = MergeBwdIO{}) {
+                       const EpilogueIO& bio = EpilogueIO{}) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
@@ -840,19 +872,23 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
     if (mode == 1)
       softmax_vt_kernel<D, 1><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, MergeBwdIO{});
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, EpilogueIO{});
     else if (mode == 2)
       softmax_vt_kernel<D, 2><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, MergeBwdIO{});
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, EpilogueIO{});
     else if (mode == 3)
       softmax_vt_kernel<D, 3><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, nullptr, g,
           l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, bio);
+    else if (mode == 4)
+      softmax_vt_kernel<D, 4><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, bio);
     else
       softmax_vt_kernel<D, 0><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
-          l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f, MergeBwdIO{});
+          l.batch, l.heads, tpf2, scale * kLog2e, nullptr, nullptr, 0.f, EpilogueIO{});
   } else {
     if (mode != 0) return hipErrorNotSupported;
     softmax_mfma_kernel<D, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
@@ -910,12 +946,28 @@ hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, 
 hipError_t launch_softmax_merge_bwd(const void* q, const void* k, const void* v, const void* tk,
                                     const void* tv, const float* R, const float* gates,
                                     const vdn_layout_t& l, float scale, float eps,
-                                    const MergeBwdIO& bio, void* ws, hipStream_t s) {
+                                    const EpilogueIO& bio, void* ws, hipStream_t s) {
   if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
   switch (l.head_dim_k) {
     case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
     case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
     case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, nullptr, ws, R, gates, eps, 3, s, bio);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_softmax_branches_mxfp8(const void* q, const void* k, const void* v,
+                                         const void* tk, const void* tv, const float* R,
+                                         const float* gates, const vdn_layout_t& l, float scale,
+                                         float eps, void* codes, void* scales, void* ws,
+                                         hipStream_t s) {
+  if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
+  EpilogueIO io{};
+  io.mx_scales = (uint8_t*)scales;
+  switch (l.head_dim_k) {
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
   }
   return hipErrorInvalidValue;
 }

@@ -86,6 +86,29 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// MXFP8 (OCP microscaling, E4M3 elements): the shared exponent X of a block
+// whose largest magnitude is amax is floor(log2 amax) - 8 (8 = exponent of
+// E4M3's largest normal, 448 = 1.75 * 2^8), at least -127 (E8M0 range); an
+// all-zero block gets X = 0.  The scale byte is X + 127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);                 // amax = f 2^ex, f in [0.5, 1)
+  const int X = ex - 1 - 8;
+  return X < -127 ? -127 : X;
+}
+// Four values v / 2^X as E4M3 codes (round to nearest even; magnitudes past
+// 448 clamp to 448), byte e of the result holding value e.
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, int X) {
+  const float a2 = fminf(fmaxf(ldexpf(a, -X), -448.f), 448.f);
+  const float b2 = fminf(fmaxf(ldexpf(b, -X), -448.f), 448.f);
+  const float c2 = fminf(fmaxf(ldexpf(c, -X), -448.f), 448.f);
+  const float d2 = fminf(fmaxf(ldexpf(d, -X), -448.f), 448.f);
+  int acc = __builtin_amdgcn_cvt_pk_fp8_f32(a2, b2, 0, false);   // bytes 0, 1
+  acc = __builtin_amdgcn_cvt_pk_fp8_f32(c2, d2, acc, true);      // bytes 2, 3
+  return (uint32_t)acc;
+}
+
 // XOR swizzle of the 16-byte chunk index inside an LDS row of D bf16 values.
 // It makes (a) 16 consecutive rows read at one logical chunk by ds_read_b128
 // and (b) 4 consecutive rows x 64 bytes read by ds_read_b64_tr_b16 fall on

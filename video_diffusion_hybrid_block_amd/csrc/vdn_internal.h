@@ -231,23 +231,36 @@ hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, con
                                 const void* tv, const float* R, const float* gates,
                                 const vdn_layout_t& l, float scale, float eps, bool split, void* o,
                                 void* ws, hipStream_t s);
-// Outputs of the merge backward written by the softmax kernel's epilogue
-// (backward pass): for every video token-head, dgates [B,N,H,2] fp32,
-// dos = sigmoid(l0) dO [B,N,H,d] bf16, dlin = gradient of the linear read
-// before RMSNorm [B,N,H,d] fp32, and per (b, h, token) the softmax's
-// log-sum-exp in exp2 units (lse) and D = dos . O_soft (dvec), [B,H,N] fp32.
-struct MergeBwdIO {
+// Extra operands of the softmax kernel's epilogue.
+// Merge backward (backward pass): for every video token-head, dgates
+// [B,N,H,2] fp32, dos = sigmoid(l0) dO [B,N,H,d] bf16, dlin = gradient of the
+// linear read before RMSNorm [B,N,H,d] fp32, and per (b, h, token) the
+// softmax's log-sum-exp in exp2 units (lse) and D = dos . O_soft (dvec),
+// [B,H,N] fp32.
+// MXFP8 branches: mx_scales [B*N][2*H*d/32] receives the E8M0 block scales
+// (the E4M3 codes go to the kernel's output pointer, [B*N][2*H*d] bytes).
+struct EpilogueIO {
   const __bf16* dO;
   float* dgates;
   __bf16* dos;
   float* dlin;
   float* dvec;
   float* lse;
+  uint8_t* mx_scales;
 };
+// The two gated branches as MXFP8 (E4M3 codes, one E8M0 scale per 32
+// consecutive d of one head and branch), quantized in the epilogue from the
+// fp32 values: codes [B*N][2*H*d] bytes (softmax branch first, as x2),
+// scales [B*N][2*H*d/32].  The activation operand of the FP8 projection.
+hipError_t launch_softmax_branches_mxfp8(const void* q, const void* k, const void* v,
+                                         const void* tk, const void* tv, const float* R,
+                                         const float* gates, const vdn_layout_t& l, float scale,
+                                         float eps, void* codes, void* scales, void* ws,
+                                         hipStream_t s);
 hipError_t launch_softmax_merge_bwd(const void* q, const void* k, const void* v, const void* tk,
                                     const void* tv, const float* R, const float* gates,
                                     const vdn_layout_t& l, float scale, float eps,
-                                    const MergeBwdIO& bio, void* ws, hipStream_t s);
+                                    const EpilogueIO& bio, void* ws, hipStream_t s);
 // Transposed copy xt[b][h][d][n] of x [B,N,H,D] followed by tx [B,L,H,D]
 // (tokens along the row, zero-padded to a multiple of 8), bf16.
 hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, int N, int L,

@@ -48,29 +48,50 @@ struct BT {
   static constexpr int TBLK = (D * VSL + 63) / 64;  // ... of a D x 64 transposed tile
 };
 
-// 16-byte chunk `lane` of block `blk` of a 64-row tile starting at sequence
-// position p0: row, chunk (clamped; the pad slot reloads the last chunk).
+// Per-lane part of a tile copy, packed in 32 bits so that nothing 64-bit per
+// lane is loop-invariant (the compiler would hoist such pointers and, short
+// of registers, spill them; a scratch reload then waits for every copy in
+// flight).  The issue loops mark the packed words as rewritten each tile, so
+// the offsets decoded from them are not hoisted either.  Row blocks: position of the lane's row in the tile (bits 0-7)
+// and its 16-byte chunk (bits 8-15); transposed blocks: the position of the
+// lane's 8-token chunk (bits 0-7) and its d row (bits 8-15).
 template <int D>
-__device__ __forceinline__ const bf16* row_src(const KeyAddr& a, int p0, int blk, int lane,
-                                               const bf16* vid, const bf16* txt, int HD) {
+__device__ __forceinline__ uint32_t row_pack(int blk, int lane) {
   const int slot = blk * 64 + lane;
-  const int row = slot / BT<D>::KSL;
-  const int ch = imin(slot % BT<D>::KSL, BT<D>::KCH - 1);
-  const int r = key_row(a, p0 + row);
-  const bool t = (r & 0x40000000) != 0;
-  return (t ? txt : vid) + (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + ch * 8;
+  return (uint32_t)(slot / BT<D>::KSL) | ((uint32_t)imin(slot % BT<D>::KSL, BT<D>::KCH - 1) << 8);
 }
-// ... of a D x 64 transposed tile read from a transposed copy xt[d][x]
-// (x = video token, then N + text token): 8 positions per chunk.
 template <int D>
-__device__ __forceinline__ const bf16* tr_src(const KeyAddr& a, int p0, int blk, int lane,
-                                              const bf16* xt, int nl8, int N) {
+__device__ __forceinline__ uint32_t tr_pack(int blk, int lane) {
   const int slot = blk * 64 + lane;
-  const int d = imin(slot / BT<D>::VSL, D - 1);
-  const int c = imin(slot % BT<D>::VSL, 7);
-  const int r = key_row(a, p0 + c * 8);
+  return (uint32_t)(imin(slot % BT<D>::VSL, 7) * 8) | ((uint32_t)imin(slot / BT<D>::VSL, D - 1) << 8);
+}
+// Byte offsets from the tile's first row / first position when the tile lies
+// in one key segment (rows HD elements apart; transposed rows nl8 apart).
+__device__ __forceinline__ uint32_t row_boff(uint32_t pk, int HD) {
+  return ((pk & 0xFFu) * (uint32_t)HD + (pk >> 8) * 8u) * 2u;
+}
+__device__ __forceinline__ uint32_t tr_boff(uint32_t pk, int nl8) {
+  return ((pk >> 8) * (uint32_t)nl8 + (pk & 0xFFu)) * 2u;
+}
+// Per-lane sources for a tile that straddles segments (key rows resolved one
+// by one): row blocks from the video or text tensor, transposed blocks from a
+// transposed copy xt[d][x] (x = video token, then N + text token).
+__device__ __forceinline__ const bf16* row_gen(const KeyAddr& a, int p0, uint32_t pk,
+                                               const bf16* vid, const bf16* txt, int HD) {
+  const int r = key_row(a, p0 + (int)(pk & 0xFFu));
+  const bool t = (r & 0x40000000) != 0;
+  return (t ? txt : vid) + (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + (pk >> 8) * 8;
+}
+__device__ __forceinline__ const bf16* tr_gen(const KeyAddr& a, int p0, uint32_t pk,
+                                              const bf16* xt, int nl8, int N) {
+  const int r = key_row(a, p0 + (int)(pk & 0xFFu));
   const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
-  return xt + (size_t)d * nl8 + tok;
+  return xt + (size_t)(pk >> 8) * nl8 + tok;
+}
+// Segment of virtual position kv (0..2 video, 3 text, 4 past the end).
+__device__ __forceinline__ int seg_of(const KeyAddr& a, int kv) {
+  return (int)(((uint32_t)(a.e0 - 1 - kv) >> 31) + ((uint32_t)(a.e1 - 1 - kv) >> 31) +
+               ((uint32_t)(a.e2 - 1 - kv) >> 31) + ((uint32_t)(a.nkeys - 1 - kv) >> 31));
 }
 
 // ---------------------------------------------------------------------------
@@ -99,8 +120,10 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int N = g.T * g.P;
   WorkItem w = decode_work_xcd(g, B, H, tpf);
   w.b = sgpr(w.b); w.h = sgpr(w.h); w.t = sgpr(w.t); w.tile = sgpr(w.tile);
-  const KeyAddr ka = key_addr(key_map(g, w.t));
-  const int nkeys = sgpr(ka.nkeys);
+  KeyAddr ka = key_addr(key_map(g, w.t));
+  ka.e0 = sgpr(ka.e0); ka.e1 = sgpr(ka.e1); ka.e2 = sgpr(ka.e2); ka.nkeys = sgpr(ka.nkeys);
+  ka.d0 = sgpr(ka.d0); ka.d1 = sgpr(ka.d1); ka.d2 = sgpr(ka.d2); ka.clamp_tok = sgpr(ka.clamp_tok);
+  const int nkeys = ka.nkeys;
 
   const int qlocal = w.tile * (NW * 32) + wv * 32 + (lane & 31);
   const bool qvalid = qlocal < g.P;
@@ -123,28 +146,50 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bf16* ktbh = kt + ((size_t)w.b * H + w.h) * D * (size_t)nl8;
 
   const int ntiles = sgpr((nkeys + BN - 1) / BN);
+  // Copy i of this wave fills block i * NW + wv of the tile: K rows, V rows,
+  // K^T, or the spare block (a reload of K block 0).
+  uint32_t pk[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = i * NW + wv;
+    pk[i] = blk < T::RBLK ? row_pack<D>(blk, lane)
+          : blk < 2 * T::RBLK ? row_pack<D>(blk - T::RBLK, lane)
+          : blk < NB ? tr_pack<D>(blk - 2 * T::RBLK, lane) : row_pack<D>(0, lane);
+  }
   auto issue = [&](int tile, int buf) {
     char VDN_LDS* bb = lds + buf * BUFB;
     const int p0 = imin(tile, ntiles - 1) * BN;
+    // keep the offsets derived from pk inside the loop (see row_pack)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(pk[i]));
+    const int s0 = seg_of(ka, p0), s1 = seg_of(ka, p0 + BN - 1);
+    if (s0 == s1 && s0 < 4) {
+      // the whole tile in one segment: wave-uniform bases
+      const bool txt = s0 == 3;
+      const int dl = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
+      const size_t r0 = (size_t)(p0 + dl) * HD;
+      const char* kb = sgpr_ptr((txt ? tkbh : kbh) + r0);
+      const char* vb = sgpr_ptr((txt ? tvbh : vbh) + r0);
+      const char* tb = sgpr_ptr(ktbh + (p0 + (txt ? N - ka.e2 : dl)));
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int blk = i * NW + wv;                 // uniform
+        if (blk < T::RBLK) g2lds16(kb + row_boff(pk[i], HD), bb + blk * 1024);
+        else if (blk < 2 * T::RBLK) g2lds16(vb + row_boff(pk[i], HD), bb + blk * 1024);
+        else if (blk < NB) g2lds16(tb + tr_boff(pk[i], nl8), bb + blk * 1024);
+        else g2lds16(kb + row_boff(pk[i], HD), bb + NB * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = i * NW + wv;                   // uniform
       const bf16* src;
-      int dst;
-      if (blk < T::RBLK) {
-        src = row_src<D>(ka, p0, blk, lane, kbh, tkbh, HD);
-        dst = blk * 1024;
-      } else if (blk < 2 * T::RBLK) {
-        src = row_src<D>(ka, p0, blk - T::RBLK, lane, vbh, tvbh, HD);
-        dst = blk * 1024;
-      } else if (blk < NB) {
-        src = tr_src<D>(ka, p0, blk - 2 * T::RBLK, lane, ktbh, nl8, N);
-        dst = blk * 1024;
-      } else {
-        src = row_src<D>(ka, p0, 0, lane, kbh, tkbh, HD);
-        dst = NB * 1024;
-      }
-      g2lds16(src, bb + dst);
+      if (blk < T::RBLK) src = row_gen(ka, p0, pk[i], kbh, tkbh, HD);
+      else if (blk < 2 * T::RBLK) src = row_gen(ka, p0, pk[i], vbh, tvbh, HD);
+      else if (blk < NB) src = tr_gen(ka, p0, pk[i], ktbh, nl8, N);
+      else src = row_gen(ka, p0, pk[i], kbh, tkbh, HD);
+      g2lds16(src, bb + (blk < NB ? blk : NB) * 1024);
     }
   };
 
@@ -286,6 +331,10 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     qa = key_addr(key_map(g, f));
     qa.nkeys = qa.e2;
   }
+  // workgroup-uniform: keep the fields in SGPRs (a per-lane copy would be
+  // indexed through scratch when a segment's offset is selected)
+  qa.e0 = sgpr(qa.e0); qa.e1 = sgpr(qa.e1); qa.e2 = sgpr(qa.e2); qa.nkeys = sgpr(qa.nkeys);
+  qa.d0 = sgpr(qa.d0); qa.d1 = sgpr(qa.d1); qa.d2 = sgpr(qa.d2); qa.clamp_tok = sgpr(qa.clamp_tok);
   const int nq = sgpr(qa.nkeys);
   const int nkr = text ? g.L : g.P;
   const int klocal = tile * (NW * 32) + wv * 32 + (lane & 31);
@@ -308,29 +357,68 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const float* dvbh = dvec + (size_t)(b * H + h) * N;
 
   const int ntiles = sgpr((nq + BM - 1) / BM);
+  // Copy i of this wave fills block i * NW + wv: Q rows, [dO_s rows], the
+  // transposed tile, lse / D, or the spare block (a reload of Q block 0).
+  uint32_t pk[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = i * NW + wv;
+    pk[i] = blk < T::RBLK ? row_pack<D>(blk, lane)
+          : (PASS == 1 && blk < 2 * T::RBLK) ? row_pack<D>(blk - T::RBLK, lane)
+          : blk < SOFF / 1024 ? tr_pack<D>(blk - TOFF / 1024, lane) : row_pack<D>(0, lane);
+  }
   auto issue = [&](int tile_, int buf) {
     char VDN_LDS* bb = lds + buf * BUFB;
     const int p0 = imin(tile_, ntiles - 1) * BM;
+    // keep the offsets derived from pk inside the loop (see row_pack)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(pk[i]));
+    const int s0 = seg_of(qa, p0), s1 = seg_of(qa, p0 + BM - 1);
+    if (s0 == s1 && s0 < 3) {
+      // the whole query tile in one video segment: wave-uniform bases
+      // token offset of the segment (a select between the struct's members
+      // would be compiled into an indexed load from a stack copy)
+      const int dl = (key_row(qa, p0) & 0x3FFFFFFF) - p0;
+      const size_t r0 = (size_t)(p0 + dl) * HD;
+      const char* qb = sgpr_ptr(qbh + r0);
+      const char* db = sgpr_ptr(dbh + r0);
+      const char* tb = sgpr_ptr(trbh + (p0 + dl));
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int blk = i * NW + wv;                 // uniform
+        if (blk < T::RBLK) {
+          g2lds16(qb + row_boff(pk[i], HD), bb + blk * 1024);
+        } else if (PASS == 1 && blk < 2 * T::RBLK) {
+          g2lds16(db + row_boff(pk[i], HD), bb + blk * 1024);
+        } else if (blk < SOFF / 1024) {
+          g2lds16(tb + tr_boff(pk[i], nq8), bb + blk * 1024);
+        } else if (blk < NB) {
+          const int tok = p0 + dl + (lane & 15) * 4;
+          g2lds16((((lane >> 4) & 1) ? dvbh : lbh) + tok, bb + blk * 1024);
+        } else {
+          g2lds16(qb + row_boff(pk[i], HD), bb + NB * 1024);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = i * NW + wv;                   // uniform
       const void* src;
-      int dst = blk * 1024;
       if (blk < T::RBLK) {
-        src = row_src<D>(qa, p0, blk, lane, qbh, qbh, HD);
+        src = row_gen(qa, p0, pk[i], qbh, qbh, HD);
       } else if (PASS == 1 && blk < 2 * T::RBLK) {
-        src = row_src<D>(qa, p0, blk - T::RBLK, lane, dbh, dbh, HD);
+        src = row_gen(qa, p0, pk[i], dbh, dbh, HD);
       } else if (blk < SOFF / 1024) {
-        src = tr_src<D>(qa, p0, blk - TOFF / 1024, lane, trbh, nq8, N);
+        src = tr_gen(qa, p0, pk[i], trbh, nq8, N);
       } else if (blk < NB) {
         const int ch = lane & 15;
         const int tok = key_row(qa, p0 + ch * 4) & 0x3FFFFFFF;
         src = (((lane >> 4) & 1) ? dvbh : lbh) + tok;
       } else {
-        src = row_src<D>(qa, p0, 0, lane, qbh, qbh, HD);
-        dst = NB * 1024;
+        src = row_gen(qa, p0, pk[i], qbh, qbh, HD);
       }
-      g2lds16(src, bb + dst);
+      g2lds16(src, bb + (blk < NB ? blk : NB) * 1024);
     }
   };
 

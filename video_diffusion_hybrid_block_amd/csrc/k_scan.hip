@@ -61,13 +61,15 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   // during this one) with 16-byte direct-to-LDS loads, one 1 KB block per
   // instruction; chunk c of row n sits at c ^ gsw(n) so the B-operand reads
   // (sixteen consecutive rows, one chunk) are conflict-free.
-  __shared__ __attribute__((aligned(1024))) char gbuf[2 * GBYTES];
-  __shared__ __attribute__((aligned(16))) float S[32 * LDF];
-  __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
-  __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
-  char VDN_LDS* Gl = (char VDN_LDS*)gbuf;
-  char VDN_LDS* Xh = (char VDN_LDS*)xh;
-  char VDN_LDS* Xl = (char VDN_LDS*)xl;
+  // One LDS allocation for the G buffers, the state rows S and X = aS + B as
+  // bf16 hi / lo: with separate __shared__ arrays the compiler cannot tell
+  // the direct-to-LDS copies of G from the other LDS accesses and waits for
+  // the next step's copy before writing X.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * GBYTES + 32 * LDF * 4 + 2 * 32 * D * 2];
+  char VDN_LDS* Gl = (char VDN_LDS*)smem;
+  float VDN_LDS* S = (float VDN_LDS*)(smem + 2 * GBYTES);
+  char VDN_LDS* Xh = (char VDN_LDS*)(smem + 2 * GBYTES + 32 * LDF * 4);
+  char VDN_LDS* Xl = Xh + 32 * D * 2;
   auto gsw = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int tid = threadIdx.x;
@@ -139,7 +141,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
       *(bf16x8 VDN_LDS*)(Xh + off) = hv;
       *(bf16x8 VDN_LDS*)(Xl + off) = lv;
     }
-    __syncthreads();
+    lds_barrier();
     const int n = wv * 32 + (lane & 31);
     const int x = gsw(n);
     const char VDN_LDS* grow = Gl + bi * GBYTES + n * (4 * D);
@@ -170,7 +172,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
       const int r = (j >> 2) * 8 + half * 4 + (j & 3);
       S[r * LDF + wv * 32 + (lane & 31)] = (acc[j] + (acc1[j] + acc2[j])) * post;
     }
-    __syncthreads();
+    lds_barrier();
   };
   auto snapshot = [&](int c) {
     float* dst = snap + (size_t)c * mat + (size_t)row0 * D;
@@ -347,7 +349,7 @@ scan_bwd_kernel(const float* __restrict__ G, const float* __restrict__ dR,
       *(bf16x8 VDN_LDS*)(Xh + off) = hv;
       *(bf16x8 VDN_LDS*)(Xl + off) = lv;
     }
-    __syncthreads();
+    lds_barrier();
     const int n = wv * 32 + (lane & 31);
     const int x = gsw(n);
     const char VDN_LDS* grow = Gl + bi * GBYTES + n * (4 * D);
@@ -377,7 +379,7 @@ scan_bwd_kernel(const float* __restrict__ G, const float* __restrict__ dR,
       const int r = (j >> 2) * 8 + half * 4 + (j & 3);
       S[r * LDF + wv * 32 + (lane & 31)] = (acc[j] + (acc1[j] + acc2[j])) * a;
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   int f = prev_frame(g, dir, -1);

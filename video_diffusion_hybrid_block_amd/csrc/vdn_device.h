@@ -164,6 +164,18 @@ __device__ __forceinline__ void g2lds16(const void* gptr, char VDN_LDS* lds_wave
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations, not for its global loads, stores or direct-to-LDS copies in
+// flight.  __syncthreads() also makes the wave's global stores visible, i.e.
+// waits for every outstanding vector memory operation, including copies
+// prefetched for the next step.  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }

@@ -48,6 +48,33 @@ struct BT {
   static constexpr int TBLK = (D * VSL + 63) / 64;  // ... of a D x 64 transposed tile
 };
 
+// Per-lane sources of chunk `lane` of block `blk` of a tile starting at
+// sequence position p0, resolved row by row: a 64-row tile (row, chunk
+// clamped; the pad slot reloads the last chunk) and a D x 64 transposed tile
+// from a transposed copy xt[d][x] (x = video token, then N + text token).
+// The pass that has registers to spare keeps these loop-invariant pointers;
+// the others use the packed form below.
+template <int D>
+__device__ __forceinline__ const bf16* row_src(const KeyAddr& a, int p0, int blk, int lane,
+                                               const bf16* vid, const bf16* txt, int HD) {
+  const int slot = blk * 64 + lane;
+  const int row = slot / BT<D>::KSL;
+  const int ch = imin(slot % BT<D>::KSL, BT<D>::KCH - 1);
+  const int r = key_row(a, p0 + row);
+  const bool t = (r & 0x40000000) != 0;
+  return (t ? txt : vid) + (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + ch * 8;
+}
+template <int D>
+__device__ __forceinline__ const bf16* tr_src(const KeyAddr& a, int p0, int blk, int lane,
+                                              const bf16* xt, int nl8, int N) {
+  const int slot = blk * 64 + lane;
+  const int d = imin(slot / BT<D>::VSL, D - 1);
+  const int c = imin(slot % BT<D>::VSL, 7);
+  const int r = key_row(a, p0 + c * 8);
+  const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
+  return xt + (size_t)d * nl8 + tok;
+}
+
 // Per-lane part of a tile copy, packed in 32 bits so that nothing 64-bit per
 // lane is loop-invariant (the compiler would hoist such pointers and, short
 // of registers, spill them; a scratch reload then waits for every copy in
@@ -331,10 +358,6 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     qa = key_addr(key_map(g, f));
     qa.nkeys = qa.e2;
   }
-  // workgroup-uniform: keep the fields in SGPRs (a per-lane copy would be
-  // indexed through scratch when a segment's offset is selected)
-  qa.e0 = sgpr(qa.e0); qa.e1 = sgpr(qa.e1); qa.e2 = sgpr(qa.e2); qa.nkeys = sgpr(qa.nkeys);
-  qa.d0 = sgpr(qa.d0); qa.d1 = sgpr(qa.d1); qa.d2 = sgpr(qa.d2); qa.clamp_tok = sgpr(qa.clamp_tok);
   const int nq = sgpr(qa.nkeys);
   const int nkr = text ? g.L : g.P;
   const int klocal = tile * (NW * 32) + wv * 32 + (lane & 31);
@@ -370,6 +393,30 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   auto issue = [&](int tile_, int buf) {
     char VDN_LDS* bb = lds + buf * BUFB;
     const int p0 = imin(tile_, ntiles - 1) * BM;
+    if constexpr (PASS == 0) {
+      // one accumulator and no dO_s rows: registers to spare for per-lane
+      // pointers (measured faster here than the packed form)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int blk = i * NW + wv;                 // uniform
+        const void* src;
+        int dst = blk * 1024;
+        if (blk < T::RBLK) {
+          src = row_src<D>(qa, p0, blk, lane, qbh, qbh, HD);
+        } else if (blk < SOFF / 1024) {
+          src = tr_src<D>(qa, p0, blk - TOFF / 1024, lane, trbh, nq8, N);
+        } else if (blk < NB) {
+          const int ch = lane & 15;
+          const int tok = key_row(qa, p0 + ch * 4) & 0x3FFFFFFF;
+          src = (((lane >> 4) & 1) ? dvbh : lbh) + tok;
+        } else {
+          src = row_src<D>(qa, p0, 0, lane, qbh, qbh, HD);
+          dst = NB * 1024;
+        }
+        g2lds16(src, bb + dst);
+      }
+      return;
+    }
     // keep the offsets derived from pk inside the loop (see row_pack)
 #pragma unroll
     for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(pk[i]));

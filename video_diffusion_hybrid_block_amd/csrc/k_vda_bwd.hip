@@ -39,29 +39,34 @@ namespace {
 constexpr int DR_CH = 256;               // tokens per workgroup
 constexpr int DR_TT = 64;                // tokens per LDS tile
 
-// Frames of read slot `slot` (a chunk's non-anchor frames; slot nc: the
-// anchors) and its token count.
-__device__ __forceinline__ int slot_frame_range(const Geo& g, int slot, int& f0, int& f1) {
+// Video tokens of read slot `slot`: a chunk's non-anchor frames, which are
+// contiguous since only the first and the last frame can be anchors, or for
+// slot nc the anchor frames (at most two).  The slot's i-th token is
+// base0 + i below `split` and base1 + i from there on; n tokens in all.
+struct SlotMap {
+  int n, split, base0, base1;
+};
+__device__ __forceinline__ SlotMap slot_map(const Geo& g, int slot) {
+  SlotMap m;
   if (slot < g.nc) {
-    f0 = slot * g.C;
-    f1 = imin(g.T, f0 + g.C);
+    int f0 = slot * g.C, f1 = imin(g.T, f0 + g.C);
+    if (is_anchor(g, f0)) ++f0;
+    if (f1 > f0 && is_anchor(g, f1 - 1)) --f1;
+    m.n = imax(0, f1 - f0) * g.P;
+    m.split = m.n;
+    m.base0 = f0 * g.P;
+    m.base1 = 0;
   } else {
-    f0 = 0;
-    f1 = g.T;
+    const bool first = g.af, last = g.al && !(g.af && g.T == 1);
+    m.n = ((first ? 1 : 0) + (last ? 1 : 0)) * g.P;
+    m.split = first ? g.P : 0;
+    m.base0 = 0;
+    m.base1 = (g.T - 1) * g.P - m.split;
   }
-  int n = 0;
-  for (int f = f0; f < f1; ++f) n += ((slot < g.nc) != is_anchor(g, f)) ? 1 : 0;
-  return n * g.P;
+  return m;
 }
-// Video token of the slot's i-th token.
-__device__ __forceinline__ int slot_token(const Geo& g, int slot, int f0, int i) {
-  int want = i / g.P;
-  for (int f = f0;; ++f) {
-    if ((slot < g.nc) != is_anchor(g, f)) {
-      if (want == 0) return f * g.P + i % g.P;
-      --want;
-    }
-  }
+__device__ __forceinline__ int slot_tok(const SlotMap& m, int i) {
+  return i < m.split ? m.base0 + i : m.base1 + i;
 }
 
 template <int D>
@@ -89,8 +94,8 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
   const int b = bh / H, h = bh % H;
   const int N = g.T * g.P;
   const size_t mat = (size_t)D * D;
-  int f0, f1;
-  const int ntok = slot_frame_range(g, slot, f0, f1);
+  const SlotMap sm = slot_map(g, slot);
+  const int ntok = sm.n;
   const int i0 = ch * DR_CH;
   const int nmine = imax(0, imin(DR_CH, ntok - i0));
   float* part = dRp + (((size_t)bh * (g.nc + 1) + slot) * nch + ch) * mat;
@@ -123,7 +128,7 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
       const int r = i / (D / 8), c = (i % (D / 8)) * 8;
       bf16x8 qv = {}, hv = {}, lv = {};
       if (t0 + r < nmine) {
-        const int tok = slot_token(g, slot, f0, i0 + t0 + r);
+        const int tok = slot_tok(sm, i0 + t0 + r);
         const size_t off = (((size_t)b * N + tok) * H + h) * D + c;
         qv = *(const bf16x8*)(q + off);
         const f32x4 a = *(const f32x4*)(dlin + off);
@@ -180,7 +185,7 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
         for (int j = 0; j < 16; ++j) {
           const int r = tb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
           if (t0 + r < nmine) {
-            const int tok = slot_token(g, slot, f0, i0 + t0 + r);
+            const int tok = slot_tok(sm, i0 + t0 + r);
             dq[(((size_t)b * N + tok) * H + h) * D + cb * 32 + (lane & 31)] = o[j];
           }
         }

@@ -403,14 +403,14 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   if (e == hipSuccess)
     e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
                        (float*)(ws + bp.dRp), dR, dspost, dq, dalpha, l, stream);
-  // softmax branch: dq (added), dk, dv, dtext_k, dtext_v (written)
-  if (e == hipSuccess)
-    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
-                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
-  // statistics: dk, dv, dtext_k, dtext_v (added), dbeta (written)
+  // statistics: dk, dv, dtext_k, dtext_v and dbeta (written)
   if (e == hipSuccess)
     e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
                         stream);
+  // softmax branch: dq, dk, dv, dtext_k, dtext_v (added)
+  if (e == hipSuccess)
+    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
+                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
   return hip_status(e);
 }
 

@@ -295,6 +295,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // Two passes over the query tiles, 8 waves x 32 keys = 256 keys per
 // workgroup, two waves per SIMD.  PASS 0 accumulates dv^T += dO_s^T P (needs
 // Q rows, dO_s^T, lse); PASS 1 dk^T += Q^T dS (Q rows, dO_s rows, Q^T, lse, D).
+// Both add to dk / dv, which already hold the statistics' part.
 // Each pass holds one d x 32 accumulator per lane, so it fits two waves per
 // SIMD, and every query tile it streams serves 256 keys.  (A single pass
 // holding both accumulators needs one wave per SIMD and 128 keys per
@@ -537,9 +538,9 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d = db * 32 + jj * 8 + half * 4;
-        f32x4 o;
+        f32x4 o = *(const f32x4*)(row + d);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = sc * acc[db][jj * 4 + e];
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(sc, acc[db][jj * 4 + e], o[e]);
         *(f32x4*)(row + d) = o;
       }
   }

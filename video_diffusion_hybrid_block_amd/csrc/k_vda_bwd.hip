@@ -386,13 +386,13 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
 }
 
 // ---------------------------------------------------------------------------
-// 4. Per token of every frame (slot T: the text tokens): dk, dv (added),
-// dbeta (written; zero for frames no chain folds).  Workgroup = (batch, head,
-// slot, chunk of GB_CH tokens), 4 waves x 32 tokens at a time.  With
-// As = dA + dA^T: U = K As^T, W = K dB^T, Z = V dB (tokens x d each) on MFMA,
-// As and dB as bf16 hi + lo in swizzled LDS (As and dB rows for U and W,
-// dB columns for Z); dk += beta (U + Z), dv += beta W,
-// dbeta = sum_r (k_r U_r / 2 + v_r W_r).
+// 4. Per token of every frame (slot T: the text tokens): dk, dv, dbeta
+// (written; zero for frames no chain folds; the softmax backward adds its
+// dk, dv afterwards).  Workgroup = (batch, head, slot, chunk of GB_CH
+// tokens), 4 waves x 32 tokens at a time.  With As = dA + dA^T:
+// U = K As^T, W = K dB^T, Z = V dB (tokens x d each) on MFMA, As and dB as
+// bf16 hi + lo in swizzled LDS (As and dB rows for U and W, dB columns for
+// Z); dk = beta (U + Z), dv = beta W, dbeta = sum_r (k_r U_r / 2 + v_r W_r).
 // ---------------------------------------------------------------------------
 constexpr int GB_CH = 256;
 
@@ -406,14 +406,13 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
                      float* __restrict__ dbeta, Geo g, int H, int nch) {
   constexpr int MAT = D * D * 2;
   constexpr int NBK = D / 32;
-  __shared__ __attribute__((aligned(16))) char sah[MAT];
-  __shared__ __attribute__((aligned(16))) char sal[MAT];
-  __shared__ __attribute__((aligned(16))) char sbh[MAT];
-  __shared__ __attribute__((aligned(16))) char sbl[MAT];
-  char VDN_LDS* Ah = (char VDN_LDS*)sah;
-  char VDN_LDS* Al = (char VDN_LDS*)sal;
-  char VDN_LDS* Bh = (char VDN_LDS*)sbh;
-  char VDN_LDS* Bl = (char VDN_LDS*)sbl;
+  // As hi, As lo, dB hi, dB lo; the two dB tiles are adjacent (they first
+  // hold dA in fp32)
+  __shared__ __attribute__((aligned(16))) char sm[4 * MAT];
+  char VDN_LDS* Ah = (char VDN_LDS*)sm;
+  char VDN_LDS* Al = Ah + MAT;
+  char VDN_LDS* Bh = Ah + 2 * MAT;
+  char VDN_LDS* Bl = Ah + 3 * MAT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, half = lane >> 5;
   const int ch = blockIdx.x % nch;
   const int slot = (blockIdx.x / nch) % (g.T + 1);
@@ -428,41 +427,66 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   const int NB = N + g.L;
   float* dbrow = dbeta + ((size_t)b * NB + (text ? N : slot * g.P) + i0) * H + h;
   const bool live = text || frame_needs_stats(g, slot);
+  const size_t base = text ? ((size_t)b * g.L + i0) * H + h : ((size_t)b * N + (size_t)slot * g.P + i0) * H + h;
+  float* dkb = (text ? dtk : dk) + base * D;
+  float* dvb = (text ? dtv : dv) + base * D;
+  const size_t HD = (size_t)H * D;
   if (!live) {
     for (int i = tid; i < nmine; i += 256) dbrow[(size_t)i * H] = 0.f;
+    for (int i = tid; i < nmine * (D / 4); i += 256) {
+      const int t = i / (D / 4), c = (i % (D / 4)) * 4;
+      *(f32x4*)(dkb + (size_t)t * HD + c) = f32x4{};
+      *(f32x4*)(dvb + (size_t)t * HD + c) = f32x4{};
+    }
     return;
   }
   const size_t mat = (size_t)D * D;
   const float* dAs = dA + ((size_t)bh * (g.T + 1) + slot) * mat;
   const float* dBs = dB + ((size_t)bh * (g.T + 1) + slot) * mat;
+  // dA in fp32 through the (not yet used) dB region, so that As = dA + dA^T
+  // is formed from coalesced row reads
+  float VDN_LDS* dAl = (float VDN_LDS*)Bh;            // d x d floats: both dB tiles
+#pragma unroll 1
+  for (int i = tid; i < D * D / 4; i += 256) *(f32x4 VDN_LDS*)(dAl + i * 4) = *(const f32x4*)(dAs + i * 4);
+  __syncthreads();
+#pragma unroll 1
   for (int i = tid; i < D * D / 8; i += 256) {
     const int r = i / (D / 8), c = (i % (D / 8)) * 8;
-    bf16x8 ah, al, bh_, bl_;
+    bf16x8 ah, al;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float a = dAs[(size_t)r * D + c + e] + dAs[(size_t)(c + e) * D + r];
-      const float bb = dBs[(size_t)r * D + c + e];
+      const float a = dAl[r * D + c + e] + dAl[(c + e) * D + r];
       bf16 x, y;
       split_bf16(a, x, y);
       ah[e] = x;
       al[e] = y;
-      split_bf16(bb, x, y);
-      bh_[e] = x;
-      bl_[e] = y;
     }
     *(bf16x8 VDN_LDS*)(Ah + swz_off<D>(r, c)) = ah;
     *(bf16x8 VDN_LDS*)(Al + swz_off<D>(r, c)) = al;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int i = tid; i < D * D / 8; i += 256) {
+    const int r = i / (D / 8), c = (i % (D / 8)) * 8;
+    const f32x4 b0 = *(const f32x4*)(dBs + (size_t)r * D + c);
+    const f32x4 b1 = *(const f32x4*)(dBs + (size_t)r * D + c + 4);
+    const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    bf16x8 bh_, bl_;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16 x, y;
+      split_bf16(bv[e], x, y);
+      bh_[e] = x;
+      bl_[e] = y;
+    }
     *(bf16x8 VDN_LDS*)(Bh + swz_off<D>(r, c)) = bh_;
     *(bf16x8 VDN_LDS*)(Bl + swz_off<D>(r, c)) = bl_;
   }
   __syncthreads();
-  const size_t base = text ? ((size_t)b * g.L + i0) * H + h : ((size_t)b * N + (size_t)slot * g.P + i0) * H + h;
   const bf16* kb = (text ? tk : k) + base * D;
   const bf16* vb = (text ? tv : v) + base * D;
-  float* dkb = (text ? dtk : dk) + base * D;
-  float* dvb = (text ? dtv : dv) + base * D;
   const float* bt = beta + ((size_t)b * NB + (text ? N : slot * g.P) + i0) * H + h;
-  const size_t HD = (size_t)H * D;
+
   for (int t0 = wv * 32; t0 < nmine; t0 += 128) {
     const int tl = imin(t0 + (lane & 31), nmine - 1);   // A-operand row (clamped)
     bf16x8 ka[D / 16], va[D / 16];
@@ -503,8 +527,8 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
         const int t = t0 + (j >> 2) * 8 + half * 4 + (j & 3);
         if (t < nmine) {
           const size_t e = (size_t)t * HD + r;
-          dkb[e] += bj[j] * (U[j] + Z[j]);
-          dvb[e] += bj[j] * W[j];
+          dkb[e] = bj[j] * (U[j] + Z[j]);
+          dvb[e] = bj[j] * W[j];
           dbp[j] = fmaf(0.5f * (float)kb[e], U[j], dbp[j]);
           dbp[j] = fmaf((float)vb[e], W[j], dbp[j]);
         }

@@ -267,7 +267,8 @@ hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, 
                             void* xt, hipStream_t s);
 // Softmax backward (bf16, d in {32, 64, 128}, P and L multiples of 8):
 // dq += scale * sum_j dS_ij k_j (dq fp32, already holding the linear read's
-// part), dk/dv (fp32, written) and dtk/dtv (text keys, written), from dos,
+// part), dk/dv and dtk/dtv (text keys) added (fp32, holding the statistics'
+// part from gram_bwd), from dos,
 // the row statistics lse/dvec, and transposed copies kt (keys + text), qt and
 // dost (video tokens).
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* tk,
@@ -277,7 +278,8 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            float* dtk, float* dtv, hipStream_t s);
 // VDA backward: dR / dq (written; dRp holds per-chunk partials of dR,
 // vda_bwd_partial_bytes), reverse scan, per-frame dA (over G), dB (over B),
-// dalpha; then gram_bwd adds dk, dv, dtk, dtv and writes dbeta.
+// dalpha; then gram_bwd writes dk, dv, dtk, dtv (zero for tokens of frames no
+// chain folds) and dbeta, before the softmax backward adds its part.
 size_t vda_bwd_partial_bytes(const vdn_layout_t& l);
 hipError_t launch_vda_bwd(const void* q, const void* k, const void* v, const void* tk,
                           const void* tv, const float* beta, const float* alpha,

@@ -224,36 +224,94 @@ dr_sum_kernel(const float4* __restrict__ part, float4* __restrict__ dR, int nch,
 
 // ---------------------------------------------------------------------------
 // d x d x d products for the per-frame step: a 16 x 16 thread grid, thread
-// (ti, tj) owning the RB x RB block at rows ti*RB, columns tj*RB.
+// (ti, tj) owning a d/16 x d/16 block made of groups of W = min(4, d/16)
+// consecutive rows: rows 16 W hh + W ti + {0..W-1} for each group hh, columns
+// likewise from tj.  W consecutive elements let every LDS read be 4 W bytes
+// wide; spreading the groups 16 W apart keeps the distinct ti (tj) of a wave
+// on different banks.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Tile {
-  static constexpr int RB = D / 16;
-  static constexpr int LD = D + 1;       // padded LDS row (floats)
+  static constexpr int RB = D / 16;              // rows (columns) per thread
+  static constexpr int W = RB < 4 ? RB : 4;      // consecutive rows per group
+  static constexpr int NH = RB / W;              // groups
+  static constexpr int LD = D + W;               // padded LDS row (floats)
+  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "d = 32, 64 or 128");
 };
+
+template <int W>
+using fvec = float __attribute__((ext_vector_type(W)));
+
+// row (column) x in [0, d/16) of thread index t in [0, 16)
+template <int D>
+__device__ __forceinline__ int blk(int t, int x) {
+  constexpr int W = Tile<D>::W;
+  return (x / W) * 16 * W + t * W + x % W;
+}
 
 // acc += op(A) * B, A and B in LDS ([D][LD]), op(A) = A or A^T.
 template <int D, bool TA>
 __device__ __forceinline__ void mm_acc(const float* A, const float* B, int ti, int tj,
                                        float (&acc)[D / 16][D / 16]) {
-  constexpr int RB = D / 16, LD = D + 1;
-  for (int k = 0; k < D; ++k) {
-    float av[RB], bv[RB];
+  constexpr int RB = Tile<D>::RB, W = Tile<D>::W, NH = Tile<D>::NH, LD = Tile<D>::LD;
+#pragma unroll 2
+  for (int k = 0; k < D; k += W) {
+    float av[RB][W], bv[W][RB];          // av[row][kk], bv[kk][col]
+    if constexpr (TA) {
 #pragma unroll
-    for (int a = 0; a < RB; ++a) av[a] = TA ? A[k * LD + ti * RB + a] : A[(ti * RB + a) * LD + k];
+      for (int kk = 0; kk < W; ++kk)
 #pragma unroll
-    for (int c = 0; c < RB; ++c) bv[c] = B[k * LD + tj * RB + c];
+        for (int hh = 0; hh < NH; ++hh) {
+          const fvec<W> x = *(const fvec<W>*)(A + (k + kk) * LD + hh * 16 * W + ti * W);
 #pragma unroll
-    for (int a = 0; a < RB; ++a)
+          for (int q = 0; q < W; ++q) av[hh * W + q][kk] = x[q];
+        }
+    } else {
 #pragma unroll
-      for (int c = 0; c < RB; ++c) acc[a][c] = fmaf(av[a], bv[c], acc[a][c]);
+      for (int a = 0; a < RB; ++a) {
+        const fvec<W> x = *(const fvec<W>*)(A + blk<D>(ti, a) * LD + k);
+#pragma unroll
+        for (int q = 0; q < W; ++q) av[a][q] = x[q];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < W; ++kk)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const fvec<W> x = *(const fvec<W>*)(B + (k + kk) * LD + hh * 16 * W + tj * W);
+#pragma unroll
+        for (int q = 0; q < W; ++q) bv[kk][hh * W + q] = x[q];
+      }
+#pragma unroll
+    for (int kk = 0; kk < W; ++kk)
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int c = 0; c < RB; ++c) acc[a][c] = fmaf(av[a][kk], bv[kk][c], acc[a][c]);
+  }
+}
+
+// dst (LDS, [D][LD]) = f(src0, src1) elementwise over [D][D] global inputs,
+// W floats per access
+template <int D, typename F>
+__device__ __forceinline__ void stage_mat(float* dst, const float* s0, const float* s1, F f,
+                                          int tid) {
+  constexpr int W = Tile<D>::W, LD = Tile<D>::LD;
+  for (int i = tid; i < D * D / W; i += 256) {
+    const fvec<W> x = *(const fvec<W>*)(s0 + i * W);
+    const fvec<W> y = *(const fvec<W>*)(s1 + i * W);
+    fvec<W> r;
+#pragma unroll
+    for (int q = 0; q < W; ++q) r[q] = f(x[q], y[q]);
+    *(fvec<W>*)(dst + (i * W / D) * LD + (i * W) % D) = r;
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_mat(float* dst, const float* src, float scale, int tid) {
-  constexpr int LD = D + 1;
-  for (int i = tid; i < D * D; i += 256) dst[(i / D) * LD + i % D] = scale * src[i];
+__device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) {
+  constexpr int W = Tile<D>::W, LD = Tile<D>::LD;
+  for (int i = tid; i < D * D / W; i += 256)
+    *(fvec<W>*)(dst + (i * W / D) * LD + (i * W) % D) = *(const fvec<W>*)(src + i * W);
 }
 
 // ---------------------------------------------------------------------------
@@ -264,9 +322,9 @@ __global__ void __launch_bounds__(256)
 vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
                      const float* __restrict__ alpha, const float* __restrict__ states,
                      const float* __restrict__ dspost, float* __restrict__ dalpha, Geo g, int H) {
-  constexpr int RB = D / 16, LD = D + 1;
-  __shared__ float L1[D * LD];
-  __shared__ float L2[D * LD];
+  constexpr int RB = Tile<D>::RB, LD = Tile<D>::LD;
+  __shared__ __attribute__((aligned(16))) float L1[D * LD];
+  __shared__ __attribute__((aligned(16))) float L2[D * LD];
   __shared__ float red[256];
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tj = tid & 15;
@@ -302,12 +360,12 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
     // dS_x = (dS_0^fwd + dS_0^bwd) / 2; dB_x = dS_x G_x; dG_x = B_x^T dS_x
     const float* p0 = post;
     const float* p1 = post + (size_t)(g.T + 1) * mat;
-    for (int i = tid; i < D * D; i += 256) L1[(i / D) * LD + i % D] = 0.5f * (p0[i] + p1[i]);
-    load_mat<D>(L2, Gs, 1.0f, tid);
+    stage_mat<D>(L1, p0, p1, [](float x, float y) { return 0.5f * (x + y); }, tid);
+    load_mat<D>(L2, Gs, tid);
     __syncthreads();
     mm_acc<D, false>(L1, L2, ti, tj, dB);
     __syncthreads();
-    load_mat<D>(L2, Bs, 1.0f, tid);
+    load_mat<D>(L2, Bs, tid);
     __syncthreads();
     mm_acc<D, true>(L2, L1, ti, tj, dG);
     __syncthreads();
@@ -318,8 +376,8 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
       if (j == 0) continue;
       const float* dSj = post + ((size_t)dir * (g.T + 1) + j) * mat;
       const float* Sp = st + ((size_t)dir * (g.T + 1) + j - 1) * mat;
-      load_mat<D>(L1, dSj, 1.0f, tid);
-      load_mat<D>(L2, Gs, 1.0f, tid);
+      load_mat<D>(L1, dSj, tid);
+      load_mat<D>(L2, Gs, tid);
       __syncthreads();
       float dX[RB][RB];
 #pragma unroll
@@ -332,11 +390,11 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
 #pragma unroll
         for (int c = 0; c < RB; ++c) {
           dB[x][c] += dX[x][c];
-          dal = fmaf(dX[x][c], Sp[(size_t)(ti * RB + x) * D + tj * RB + c], dal);
+          dal = fmaf(dX[x][c], Sp[(size_t)blk<D>(ti, x) * D + blk<D>(tj, c)], dal);
         }
       __syncthreads();
       // X = alpha S_{j-1} + B_f
-      for (int i = tid; i < D * D; i += 256) L2[(i / D) * LD + i % D] = fmaf(a, Sp[i], Bs[i]);
+      stage_mat<D>(L2, Sp, Bs, [a](float x, float y) { return fmaf(a, x, y); }, tid);
       __syncthreads();
       mm_acc<D, true>(L2, L1, ti, tj, dG);
       __syncthreads();
@@ -350,11 +408,11 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
     if (tid == 0) dalpha[((size_t)b * g.T + slot) * H + h] = red[0];
   }
   // dA = -G dG G
-  load_mat<D>(L2, Gs, 1.0f, tid);
+  load_mat<D>(L2, Gs, tid);
 #pragma unroll
   for (int x = 0; x < RB; ++x)
 #pragma unroll
-    for (int c = 0; c < RB; ++c) L1[(ti * RB + x) * LD + tj * RB + c] = dG[x][c];
+    for (int c = 0; c < RB; ++c) L1[blk<D>(ti, x) * LD + blk<D>(tj, c)] = dG[x][c];
   __syncthreads();
   float t1[RB][RB];
 #pragma unroll
@@ -366,7 +424,7 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
 #pragma unroll
   for (int x = 0; x < RB; ++x)
 #pragma unroll
-    for (int c = 0; c < RB; ++c) L1[(ti * RB + x) * LD + tj * RB + c] = t1[x][c];
+    for (int c = 0; c < RB; ++c) L1[blk<D>(ti, x) * LD + blk<D>(tj, c)] = t1[x][c];
   __syncthreads();
   float t2[RB][RB];
 #pragma unroll
@@ -379,7 +437,7 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
   for (int x = 0; x < RB; ++x)
 #pragma unroll
     for (int c = 0; c < RB; ++c) {
-      const size_t e = (size_t)(ti * RB + x) * D + tj * RB + c;
+      const size_t e = (size_t)blk<D>(ti, x) * D + blk<D>(tj, c);
       Gs[e] = -t2[x][c];
       Bs[e] = dB[x][c];
     }

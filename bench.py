@@ -316,7 +316,49 @@ def main():
                "attention_tflops": round(aflops / (b_ms / 1e3) / 1e12, 1),
                "note": "vdn_hybrid_attn_bwd: forward recomputation + gradients of q, k, v, "
                        "text k/v, beta, alpha, gate logits (fp32)"}
-        del bws, dO
+        del bws
+
+        # training pair: a forward that keeps its residuals, then the backward
+        # from them (no recomputation of the softmax forward)
+        saved = torch.empty(V.train_saved_size(lay), dtype=torch.uint8, device="cuda")
+        o_t = torch.empty_like(dev["q"])
+
+        def fwd_train():
+            V.hybrid_attn_fwd_train(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"],
+                                    dev["alpha"], dev["gate_logits"], **geo, out=o_t,
+                                    saved=saved)
+
+        def bwd_saved():
+            return V.hybrid_attn_bwd_saved(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"],
+                                           dev["alpha"], dev["gate_logits"], dO, saved, **geo)
+
+        print("[bench] training pair", file=sys.stderr, flush=True)
+        for _ in range(2):
+            fwd_train()
+            bwd_saved()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(nb):
+            fwd_train()
+            bwd_saved()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1) / nb
+        e0.record(stream)
+        for _ in range(nb):
+            fwd_train()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ft_ms = e0.elapsed_time(e1) / nb
+        bwd["training_pair"] = {
+            "ms": round(t_ms, 3), "fwd_train_ms": round(ft_ms, 3),
+            "bwd_saved_ms": round(t_ms - ft_ms, 3),
+            "video_tokens_per_s": round(w.batch * w.video_tokens / (t_ms / 1e3), 1),
+            "attention_tflops": round(aflops / (t_ms / 1e3) / 1e12, 1),
+            "note": "vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: forward (same "
+                    "output) keeping O_soft, RMSNorm(R q), lse, 1/r and the scan states; "
+                    "backward from them; 14d flops per visible pair over the pair"}
+        del saved, o_t, dO
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -291,6 +291,48 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v,
                                  float* dalpha, float* dgate_logits, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Training pair: forward that keeps its residuals, backward from them ---- */
+
+/* Bytes of the saved-residual buffer of vdn_hybrid_attn_fwd_train /
+ * vdn_hybrid_attn_bwd_saved (0 if the layout is invalid).  It holds the
+ * backward's workspace plus O_soft and RMSNorm(R q) in float32 and one float
+ * per token-head: about 8 d bytes per token-head more than
+ * vdn_hybrid_attn_bwd_workspace_size.  Host only. */
+size_t vdn_hybrid_attn_train_saved_size(const vdn_layout_t* layout);
+
+/* vdn_hybrid_attn_fwd that also leaves in `saved` what the backward needs
+ * (the VDA statistics, factor, read slots and every scan state; the softmax
+ * branch output, the RMS-normalised linear read and the RMS factor; the
+ * softmax's log-sum-exp), so that vdn_hybrid_attn_bwd_saved skips the
+ * recomputation.  o is the same output as vdn_hybrid_attn_fwd's, bit for
+ * bit.  Covers the layouts vdn_hybrid_attn_bwd covers; else
+ * VDN_ERR_UNSUPPORTED.  saved: device memory owned by the caller, at least
+ * vdn_hybrid_attn_train_saved_size(layout) bytes, 256-byte aligned; it must
+ * stay untouched until the matching vdn_hybrid_attn_bwd_saved call.
+ * [PaperDaily §三, figure 3; deepmagic blog, 用兩條分支取代一條] */
+vdn_status_t vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void* v,
+                                       const void* text_k, const void* text_v,
+                                       const float* beta, const float* alpha,
+                                       const float* gate_logits, const vdn_layout_t* layout,
+                                       void* o, void* saved, size_t saved_bytes,
+                                       hipStream_t stream);
+
+/* vdn_hybrid_attn_bwd from the residuals a vdn_hybrid_attn_fwd_train call left
+ * in `saved`, with the same inputs (q, k, v, text, beta, alpha, gate logits
+ * unchanged since that call) and the same outputs and coverage.  The merge
+ * backward runs as an elementwise pass over the saved branch outputs instead
+ * of a second softmax forward.  The call consumes `saved` (the statistics
+ * are overwritten by their gradients): one backward per training forward.
+ * Outputs must not alias inputs, `saved` or each other. */
+vdn_status_t vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void* v,
+                                       const void* text_k, const void* text_v,
+                                       const float* beta, const float* alpha,
+                                       const float* gate_logits, const void* dO,
+                                       const vdn_layout_t* layout, float* dq, float* dk,
+                                       float* dv, float* dtext_k, float* dtext_v,
+                                       float* dbeta, float* dalpha, float* dgate_logits,
+                                       void* saved, size_t saved_bytes, hipStream_t stream);
+
 /* Frame statistics: for every frame f < T and for the text block (slot T),
  * A[b,h,slot] = sum_i beta_i k_i k_i^T and B[b,h,slot] = sum_i beta_i v_i k_i^T
  * over the slot's tokens.  A_out, B_out: float32 [B, H, T+1, d, d] (row index

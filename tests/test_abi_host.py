@@ -121,6 +121,42 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.vdn_softmax_merge_fwd(*a) == 5
 
 
+def test_backward_and_training_entry_points_reject_bad_arguments_before_launch():
+    """vdn_hybrid_attn_bwd, vdn_hybrid_attn_fwd_train and
+    vdn_hybrid_attn_bwd_saved return their error codes for one bad argument
+    at a time, before any launch (the fake pointers are never used)."""
+    lib = V.lib()
+    ok = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
+    nul = None
+    lay = _lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=0, head_dim=32)
+    ref = ctypes.byref(lay)
+    small = ctypes.byref(_lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=0,
+                              head_dim=16))
+    text = ctypes.byref(_lay(batch=1, heads=1, frames=2, tokens_per_frame=8, text_tokens=8,
+                             head_dim=32))
+    need_bwd = V.bwd_workspace_size(lay)
+    need = V.train_saved_size(lay)
+    assert need > need_bwd > 0
+    assert V.train_saved_size(_lay(frames=0)) == 0
+    # forward that keeps its residuals: 8 inputs, layout, o, saved, bytes, stream
+    fw = [ok, ok, ok, nul, nul, ok, ok, ok, ref, ok, ok, need, nul]
+    for i, val, code in ((9, nul, 1), (10, nul, 1), (0, nul, 1), (9, odd, 4), (10, odd, 4),
+                         (11, need - 1, 5), (8, small, 3), (8, text, 1)):
+        a = list(fw)
+        a[i] = val
+        assert lib.vdn_hybrid_attn_fwd_train(*a) == code, (i, code)
+    # the two backward calls: 9 inputs, layout, 8 gradients, buffer, bytes, stream
+    for fn, size in ((lib.vdn_hybrid_attn_bwd, need_bwd), (lib.vdn_hybrid_attn_bwd_saved, need)):
+        bw = [ok, ok, ok, nul, nul, ok, ok, ok, ok, ref,
+              ok, ok, ok, nul, nul, ok, ok, ok, ok, size, nul]
+        for i, val, code in ((8, nul, 1), (18, nul, 1), (17, nul, 1), (12, odd, 4),
+                             (18, odd, 4), (19, size - 1, 5), (9, small, 3), (9, text, 1)):
+            a = list(bw)
+            a[i] = val
+            assert fn(*a) == code, (fn.__name__, i, code)
+
+
 @pytest.fixture(scope="module")
 def geometry_probe(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("geo") / "geometry_probe")

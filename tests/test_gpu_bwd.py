@@ -126,3 +126,102 @@ def test_backward_768p_one_head_in_full():
     print("768p head 0", " ".join(f"{k_} {e:.2e}" for k_, e in errs.items()), flush=True)
     bad = {k_: e for k_, e in errs.items() if not e <= TOL}
     assert not bad, bad
+
+
+def _grads_close(got, ref):
+    errs = {}
+    for key in G.GRAD_KEYS:
+        if ref.get(key) is None:
+            continue
+        a, b = got[key].double(), ref[key].double()
+        assert torch.isfinite(a).all(), key
+        nb = torch.linalg.vector_norm(b)
+        errs[key] = float(torch.linalg.vector_norm(a - b) / nb) if nb > 0 else \
+            float(a.abs().max())
+    return errs
+
+
+TRAIN_CASES = [CASES[0], CASES[2], CASES[4], CASES[5]]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", TRAIN_CASES, ids=[c["name"] for c in TRAIN_CASES])
+def test_training_pair_matches_recompute_and_oracle(case):
+    """vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: the output is
+    vdn_hybrid_attn_fwd's bit for bit; the gradients equal
+    vdn_hybrid_attn_bwd's up to the summation order of the merge backward's
+    dot products (bound 1e-5) and meet the oracle bound."""
+    require_gpu()
+    case = dict(case)
+    af = case.pop("anchor_first", True)
+    al = case.pop("anchor_last", True)
+    gates = case.pop("gates", None)
+    w = custom(**case)
+    _announce(f"training pair {case['name']}")
+    inp = synth.make_inputs(w)
+    if gates is not None:
+        inp["gate_logits"][..., 0] += gates[0]
+        inp["gate_logits"][..., 1] += gates[1]
+    lay = oracle_layout(w, anchor_first=af, anchor_last=al)
+    dO = synth.round_bf16(np.random.default_rng(w.seed + 7).standard_normal(inp["q"].shape))
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    args = (dev["q"], dev["k"], dev["v"], dev["text_k"] if L else None,
+            dev["text_v"] if L else None, dev["beta"], dev["alpha"], dev["gate_logits"])
+    geo = dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame,
+               chunk_frames=w.chunk_frames, window_chunks=w.window_chunks,
+               anchor_first=af, anchor_last=al)
+    dOd = torch.from_numpy(dO).to(torch.bfloat16).cuda()
+    o_ref = V.hybrid_attn(*args, **geo)
+    o, saved = V.hybrid_attn_fwd_train(*args, **geo)
+    g_saved = V.hybrid_attn_bwd_saved(*args, dOd, saved, **geo)
+    g_re = V.hybrid_attn_bwd(*args, dOd, **geo)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    errs = _grads_close(g_saved, g_re)
+    print(case["name"], "saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
+          flush=True)
+    bad = {k_: e for k_, e in errs.items() if not e <= 1e-5}
+    assert not bad, bad
+    ref = G.hybrid_attn_grad({k_: np.asarray(a, np.float64) for k_, a in inp.items()}, lay, dO)
+    oerr = {}
+    for key in G.GRAD_KEYS:
+        if g_saved.get(key) is None:
+            continue
+        g = g_saved[key].cpu().numpy()
+        oerr[key] = (float(np.abs(g).max()) if np.linalg.norm(ref[key]) < 1e-30
+                     else rel_err(g, ref[key]))
+    bad = {k_: e for k_, e in oerr.items() if not e <= TOL}
+    assert not bad, bad
+
+
+@pytest.mark.timeout(600)
+def test_training_pair_768p_matches_recompute():
+    """The 768p layer in the launch configuration bench.py times: every
+    gradient of the saved-residual backward against the recomputing backward
+    over all heads (bound 1e-5), and the output bit for bit."""
+    require_gpu()
+    from _helpers import workload
+    w = workload("768p")
+    _announce("training pair 768p")
+    inp = synth.make_inputs(w)
+    dO = synth.round_bf16(np.random.default_rng(w.seed + 7).standard_normal(
+        inp["q"].shape).astype(np.float32))
+    dev = to_dev(inp, w.dtype)
+    args = (dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["beta"],
+            dev["alpha"], dev["gate_logits"])
+    geo = dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame,
+               chunk_frames=w.chunk_frames, window_chunks=w.window_chunks)
+    dOd = torch.from_numpy(dO).to(torch.bfloat16).cuda()
+    o_ref = V.hybrid_attn(*args, **geo)
+    o, saved = V.hybrid_attn_fwd_train(*args, **geo)
+    g_saved = V.hybrid_attn_bwd_saved(*args, dOd, saved, **geo)
+    del saved
+    g_re = V.hybrid_attn_bwd(*args, dOd, **geo)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    errs = _grads_close(g_saved, g_re)
+    print("768p saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
+          flush=True)
+    bad = {k_: e for k_, e in errs.items() if not e <= 1e-5}
+    assert not bad, bad

@@ -20,6 +20,7 @@ __all__ = [
     "vda_gram", "vda_factor_scan",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
     "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
+    "train_saved_size", "hybrid_attn_fwd_train", "hybrid_attn_bwd_saved",
     "make_layout",
     "EXPORTED_SYMBOLS",
 ]
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "vdn_hybrid_attn_bwd_workspace_size", "vdn_hybrid_attn_bwd", "vdn_mxfp8_quantize",
     "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
     "vdn_hybrid_attn_proj_mxfp8_fwd", "vdn_softmax_branches_mxfp8_fwd",
+    "vdn_hybrid_attn_train_saved_size", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
 )
 
 
@@ -120,6 +122,12 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_bwd_workspace_size.restype = sz
         L.vdn_hybrid_attn_bwd.argtypes = [vp] * 9 + [lp] + [vp] * 9 + [sz, vp]
         L.vdn_hybrid_attn_bwd.restype = ctypes.c_int
+        L.vdn_hybrid_attn_train_saved_size.argtypes = [lp]
+        L.vdn_hybrid_attn_train_saved_size.restype = sz
+        L.vdn_hybrid_attn_fwd_train.argtypes = [vp] * 8 + [lp, vp, vp, sz, vp]
+        L.vdn_hybrid_attn_fwd_train.restype = ctypes.c_int
+        L.vdn_hybrid_attn_bwd_saved.argtypes = [vp] * 9 + [lp] + [vp] * 9 + [sz, vp]
+        L.vdn_hybrid_attn_bwd_saved.restype = ctypes.c_int
         L.vdn_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
         L.vdn_mxfp8_quantize.restype = ctypes.c_int
         L.vdn_out_proj_mxfp8.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int32,
@@ -524,6 +532,75 @@ def hybrid_attn_bwd(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, *, fr
         _ptr(g["alpha"]), _ptr(g["gate_logits"]), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vdn_hybrid_attn_bwd")
+    return g
+
+
+def train_saved_size(layout: Layout) -> int:
+    return lib().vdn_hybrid_attn_train_saved_size(ctypes.byref(layout))
+
+
+def hybrid_attn_fwd_train(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, frames,
+                          tokens_per_frame, chunk_frames=5, window_chunks=1, anchor_first=True,
+                          anchor_last=True, softmax_scale=0.0, rms_eps=0.0, out=None,
+                          saved=None):
+    """The layer keeping its residuals (``vdn_hybrid_attn_fwd_train``).
+    Returns (O, saved): O as ``hybrid_attn`` returns it and the uint8 buffer
+    that ``hybrid_attn_bwd_saved`` consumes."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, _ = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    if saved is None:
+        saved = torch.empty(train_saved_size(lay), dtype=torch.uint8, device=q.device)
+    st = lib().vdn_hybrid_attn_fwd_train(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out), _ptr(saved),
+        saved.numel() * saved.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_fwd_train")
+    return out, saved
+
+
+def hybrid_attn_bwd_saved(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, saved, *,
+                          frames, tokens_per_frame, chunk_frames=5, window_chunks=1,
+                          anchor_first=True, anchor_last=True, softmax_scale=0.0,
+                          rms_eps=0.0) -> dict:
+    """Gradients of the layer from the residuals of ``hybrid_attn_fwd_train``
+    (``vdn_hybrid_attn_bwd_saved``); same inputs, returns what
+    ``hybrid_attn_bwd`` returns.  Consumes ``saved``."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, d = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    _expect(dO, q.shape, q.dtype, "dO")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"q": torch.empty(q.shape, **f32), "k": torch.empty(q.shape, **f32),
+         "v": torch.empty(q.shape, **f32),
+         "text_k": torch.empty((B, L, H, d), **f32) if L else None,
+         "text_v": torch.empty((B, L, H, d), **f32) if L else None,
+         "beta": torch.empty((B, N + L, H), **f32), "alpha": torch.empty((B, frames, H), **f32),
+         "gate_logits": torch.empty((B, N, H, 2), **f32)}
+    st = lib().vdn_hybrid_attn_bwd_saved(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(dO), ctypes.byref(lay), _ptr(g["q"]),
+        _ptr(g["k"]), _ptr(g["v"]), _ptr(g["text_k"]), _ptr(g["text_v"]), _ptr(g["beta"]),
+        _ptr(g["alpha"]), _ptr(g["gate_logits"]), _ptr(saved),
+        saved.numel() * saved.element_size(), _stream())
+    _check(st, "vdn_hybrid_attn_bwd_saved")
     return g
 
 

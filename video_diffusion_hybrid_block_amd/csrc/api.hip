@@ -338,6 +338,98 @@ bool proj_layer_ok(const vdn_layout_t& l, int32_t d_model) {
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+// The backward after the merge backward (whose dos, dlin, lse and dvec sit in
+// the backward plan's buffers, beside the statistics, factor, read slots and
+// per-step states of the forward): transposed copies, the linear branch's
+// backward, the statistics backward, then the softmax backward.
+hipError_t bwd_tail(const void* q, const void* k, const void* v, const void* text_k,
+                    const void* text_v, const float* beta, const float* alpha,
+                    const vdn_layout_t& l, float* dq, float* dk, float* dv, float* dtext_k,
+                    float* dtext_v, float* dbeta, float* dalpha, char* ws, hipStream_t stream) {
+  const Plan p = make_plan(l);
+  const BwdPlan bp = make_bwd_plan(l);
+  const Geo g = make_geo(l);
+  const int N = g.T * g.P;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* R = (float*)(ws + p.r_off);
+  float* states = (float*)(ws + bp.states);
+  __bf16* dos = (__bf16*)(ws + bp.dos);
+  float* dlin = (float*)(ws + bp.dlin);
+  float* lse = (float*)(ws + bp.lse);
+  float* dvec = (float*)(ws + bp.dvec);
+  // transposed copies for the softmax backward
+  hipError_t e =
+      launch_transpose(k, text_k, l.batch, l.heads, l.head_dim_k, N, g.L, ws + bp.kt, stream);
+  if (e == hipSuccess)
+    e = launch_transpose(q, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.qt, stream);
+  if (e == hipSuccess)
+    e = launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream);
+  // linear branch: dq (its part), dA over G, dB over B, dalpha
+  if (e == hipSuccess)
+    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
+                       (float*)(ws + bp.dRp), (float*)(ws + bp.dR), (float*)(ws + bp.dspost), dq,
+                       dalpha, l, stream);
+  // statistics: dk, dv, dtext_k, dtext_v and dbeta (written)
+  if (e == hipSuccess)
+    e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
+                        stream);
+  // softmax branch: dq, dk, dv, dtext_k, dtext_v (added)
+  if (e == hipSuccess)
+    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
+                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
+  return e;
+}
+
+// Saved residuals of the training pair: the backward plan (whose statistics,
+// factor, read slots, per-step states and lse buffers the training forward
+// fills), then O_soft and RMSNorm(R q) (fp32, [B,N,H,d] each) and 1/r
+// ([B,H,N] fp32).
+struct TrainPlan {
+  size_t o_soft, o_lin, rinv, total;
+};
+
+TrainPlan make_train_plan(const vdn_layout_t& l) {
+  const BwdPlan bp = make_bwd_plan(l);
+  const size_t rows = (size_t)l.batch * l.frames * l.tokens_per_frame * l.heads;
+  TrainPlan t;
+  t.o_soft = bp.total;
+  t.o_lin = align256(t.o_soft + rows * l.head_dim_k * 4);
+  t.rinv = align256(t.o_lin + rows * l.head_dim_k * 4);
+  t.total = align256(t.rinv + rows * 4);
+  return t;
+}
+
+// Argument checks shared by the two backward entry points.
+vdn_status_t check_bwd_args(const void* q, const void* k, const void* v, const void* text_k,
+                            const void* text_v, const float* beta, const float* alpha,
+                            const float* gate_logits, const void* dO, const vdn_layout_t& l,
+                            const float* dq, const float* dk, const float* dv,
+                            const float* dtext_k, const float* dtext_v, const float* dbeta,
+                            const float* dalpha, const float* dgate_logits, const void* buf) {
+  if (!softmax_merge_fusable(l)) return VDN_ERR_UNSUPPORTED;
+  const bool txt = l.text_tokens > 0;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !dO || !dq || !dk || !dv || !dbeta ||
+      !dalpha || !dgate_logits || !buf || !text_ok(l, text_k, text_v) ||
+      (txt && (!dtext_k || !dtext_v)))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(dbeta) || !aligned16(dalpha) || !aligned16(dgate_logits) ||
+      !aligned16(buf) || !text_aligned(text_k, text_v) || (dtext_k && !aligned16(dtext_k)) ||
+      (dtext_v && !aligned16(dtext_v)))
+    return VDN_ERR_MISALIGNED;
+  return VDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t vdn_hybrid_attn_bwd_workspace_size(const vdn_layout_t* layout) {
   if (check_layout(layout) != VDN_OK) return 0;
   return make_bwd_plan(*layout).total;
@@ -353,18 +445,9 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   vdn_status_t st = check_layout(layout);
   if (st != VDN_OK) return st;
   const vdn_layout_t& l = *layout;
-  if (!softmax_merge_fusable(l)) return VDN_ERR_UNSUPPORTED;
-  const bool txt = l.text_tokens > 0;
-  if (!q || !k || !v || !beta || !alpha || !gate_logits || !dO || !dq || !dk || !dv || !dbeta ||
-      !dalpha || !dgate_logits || !workspace || !text_ok(l, text_k, text_v) ||
-      (txt && (!dtext_k || !dtext_v)))
-    return VDN_ERR_NULL_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
-      !aligned16(gate_logits) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv) || !aligned16(dbeta) || !aligned16(dalpha) || !aligned16(dgate_logits) ||
-      !aligned16(workspace) || !text_aligned(text_k, text_v) ||
-      (dtext_k && !aligned16(dtext_k)) || (dtext_v && !aligned16(dtext_v)))
-    return VDN_ERR_MISALIGNED;
+  st = check_bwd_args(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, l, dq, dk, dv,
+                      dtext_k, dtext_v, dbeta, dalpha, dgate_logits, workspace);
+  if (st != VDN_OK) return st;
   const BwdPlan bp = make_bwd_plan(l);
   if (workspace_bytes < bp.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
   const Plan p = make_plan(l);
@@ -375,14 +458,10 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   float* Sb = (float*)(ws + p.sb_off);
   float* R = (float*)(ws + p.r_off);
   float* states = (float*)(ws + bp.states);
-  float* dspost = (float*)(ws + bp.dspost);
-  float* dR = (float*)(ws + bp.dR);
   __bf16* dos = (__bf16*)(ws + bp.dos);
   float* dlin = (float*)(ws + bp.dlin);
   float* lse = (float*)(ws + bp.lse);
   float* dvec = (float*)(ws + bp.dvec);
-  const Geo g = make_geo(l);
-  const int N = g.T * g.P;
   // forward recomputation: statistics, factor, scan (keeping every state)
   hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
   if (e == hipSuccess) e = launch_factor(A, l, false, stream);
@@ -392,25 +471,81 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   if (e == hipSuccess)
     e = launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
                                  eff_eps(l), io, ws + p.vt_off, stream);
-  // transposed copies for the softmax backward
   if (e == hipSuccess)
-    e = launch_transpose(k, text_k, l.batch, l.heads, l.head_dim_k, N, g.L, ws + bp.kt, stream);
+    e = bwd_tail(q, k, v, text_k, text_v, beta, alpha, l, dq, dk, dv, dtext_k, dtext_v, dbeta,
+                 dalpha, ws, stream);
+  return hip_status(e);
+}
+
+size_t vdn_hybrid_attn_train_saved_size(const vdn_layout_t* layout) {
+  if (check_layout(layout) != VDN_OK) return 0;
+  return make_train_plan(*layout).total;
+}
+
+vdn_status_t vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void* v,
+                                       const void* text_k, const void* text_v, const float* beta,
+                                       const float* alpha, const float* gate_logits,
+                                       const vdn_layout_t* layout, void* o, void* saved,
+                                       size_t saved_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  const vdn_layout_t& l = *layout;
+  if (!softmax_merge_fusable(l)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !o || !saved ||
+      !text_ok(l, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(o) || !aligned16(saved) ||
+      !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  const TrainPlan tp = make_train_plan(l);
+  if (saved_bytes < tp.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  const Plan p = make_plan(l);
+  const BwdPlan bp = make_bwd_plan(l);
+  char* ws = (char*)saved;
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* R = (float*)(ws + p.r_off);
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
   if (e == hipSuccess)
-    e = launch_transpose(q, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.qt, stream);
+    e = launch_scan(A, B, alpha, l, (float*)(ws + p.sf_off), (float*)(ws + p.sb_off), R, stream,
+                    (float*)(ws + bp.states));
+  EpilogueIO io{};
+  io.lse = (float*)(ws + bp.lse);
+  io.o_soft = (float*)(ws + tp.o_soft);
+  io.o_lin = (float*)(ws + tp.o_lin);
+  io.rinv = (float*)(ws + tp.rinv);
   if (e == hipSuccess)
-    e = launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream);
-  // linear branch: dq (its part), dA over G, dB over B, dalpha
+    e = launch_softmax_merge_train(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                   eff_eps(l), o, io, ws + p.vt_off, stream);
+  return hip_status(e);
+}
+
+vdn_status_t vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void* v,
+                                       const void* text_k, const void* text_v, const float* beta,
+                                       const float* alpha, const float* gate_logits,
+                                       const void* dO, const vdn_layout_t* layout, float* dq,
+                                       float* dk, float* dv, float* dtext_k, float* dtext_v,
+                                       float* dbeta, float* dalpha, float* dgate_logits,
+                                       void* saved, size_t saved_bytes, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  const vdn_layout_t& l = *layout;
+  st = check_bwd_args(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, l, dq, dk, dv,
+                      dtext_k, dtext_v, dbeta, dalpha, dgate_logits, saved);
+  if (st != VDN_OK) return st;
+  const TrainPlan tp = make_train_plan(l);
+  if (saved_bytes < tp.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  const BwdPlan bp = make_bwd_plan(l);
+  char* ws = (char*)saved;
+  hipError_t e = launch_merge_bwd_saved(
+      dO, gate_logits, (const float*)(ws + tp.o_soft), (const float*)(ws + tp.o_lin),
+      (const float*)(ws + tp.rinv), l, dgate_logits, ws + bp.dos, (float*)(ws + bp.dlin),
+      (float*)(ws + bp.dvec), stream);
   if (e == hipSuccess)
-    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
-                       (float*)(ws + bp.dRp), dR, dspost, dq, dalpha, l, stream);
-  // statistics: dk, dv, dtext_k, dtext_v and dbeta (written)
-  if (e == hipSuccess)
-    e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
-                        stream);
-  // softmax branch: dq, dk, dv, dtext_k, dtext_v (added)
-  if (e == hipSuccess)
-    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
-                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
+    e = bwd_tail(q, k, v, text_k, text_v, beta, alpha, l, dq, dk, dv, dtext_k, dtext_v, dbeta,
+                 dalpha, ws, stream);
   return hip_status(e);
 }
 

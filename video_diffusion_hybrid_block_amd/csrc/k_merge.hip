@@ -164,7 +164,96 @@ hipError_t launch_valu(const void* q, const void* o_soft, const float* R, const 
   return hipGetLastError();
 }
 
+// Merge backward from saved residuals.  With s0, s1 the gate sigmoids, O_s
+// the softmax branch and n = RMSNorm(o_lin) = o_lin / r of one token-head:
+// dl0 = (dO . O_s) s0 (1 - s0), dl1 = (dO . n) s1 (1 - s1), dO_s = s0 dO
+// (bf16, the softmax backward's operand), D = dO_s . O_s, and through the
+// normalisation do_lin = (s1 dO - n (s1 dO . n) / d) / r.  32 lanes per
+// token-head (d/32 consecutive values each, 16-byte loads for d = 128),
+// 8 token-heads per workgroup; HBM-bound.
+template <int D>
+__global__ void __launch_bounds__(256)
+merge_bwd_saved_kernel(const bf16* __restrict__ dO, const float* __restrict__ gates,
+                       const float* __restrict__ o_soft, const float* __restrict__ o_lin,
+                       const float* __restrict__ rinv, float* __restrict__ dgates,
+                       bf16* __restrict__ dos, float* __restrict__ dlin,
+                       float* __restrict__ dvec, long rows, int N, int H) {
+  constexpr int NE = D / 32;
+  using fv = float __attribute__((ext_vector_type(NE)));
+  using bv = bf16 __attribute__((ext_vector_type(NE)));
+  const long r = (long)blockIdx.x * 8 + (threadIdx.x >> 5);   // (b N + token) H + h
+  const int l32 = threadIdx.x & 31;
+  if (r >= rows) return;                 // whole 32-lane groups leave together
+  const size_t off = (size_t)r * D + l32 * NE;
+  const bv dov = *(const bv*)(dO + off);
+  const fv os = *(const fv*)(o_soft + off);
+  const fv n = *(const fv*)(o_lin + off);
+  const float2 gl = *(const float2*)(gates + r * 2);
+  const long bt = r / H;
+  const int h = (int)(r - bt * H);
+  const long b = bt / N;
+  const size_t ri = ((size_t)b * H + h) * N + (size_t)(bt - b * N);
+  const float ir = rinv[ri];
+  const float s0 = sigmoidf(gl.x), s1 = sigmoidf(gl.y);
+  float dot0 = 0.f, dot1 = 0.f, dsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const float dv = (float)dov[e];
+    dot0 = fmaf(dv, os[e], dot0);
+    dot1 = fmaf(dv, n[e], dot1);
+    dsum = fmaf((float)(bf16)(s0 * dv), os[e], dsum);
+  }
+#pragma unroll
+  for (int m = 16; m > 0; m >>= 1) {
+    dot0 += __shfl_xor(dot0, m, 32);
+    dot1 += __shfl_xor(dot1, m, 32);
+    dsum += __shfl_xor(dsum, m, 32);
+  }
+  const float kn = s1 * dot1 * (1.0f / D);
+  bv vs;
+  fv vl;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const float dv = (float)dov[e];
+    vs[e] = (bf16)(s0 * dv);
+    vl[e] = ir * fmaf(-n[e], kn, s1 * dv);
+  }
+  *(bv*)(dos + off) = vs;
+  *(fv*)(dlin + off) = vl;
+  if (l32 == 0) {
+    *(float2*)(dgates + r * 2) = make_float2(dot0 * s0 * (1.0f - s0), dot1 * s1 * (1.0f - s1));
+    dvec[ri] = dsum;
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_saved(const void* dO, const float* gates, const float* o_soft,
+                            const float* o_lin, const float* rinv, const vdn_layout_t& l,
+                            float* dgates, void* dos, float* dlin, float* dvec, hipStream_t s) {
+  const int N = l.frames * l.tokens_per_frame;
+  const long rows = (long)l.batch * N * l.heads;
+  const long grid = (rows + 7) / 8;
+  if (grid >= (1L << 31)) return hipErrorInvalidValue;
+  merge_bwd_saved_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
+      (const bf16*)dO, gates, o_soft, o_lin, rinv, dgates, (bf16*)dos, dlin, dvec, rows, N,
+      l.heads);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_merge_bwd_saved(const void* dO, const float* gates, const float* o_soft,
+                                  const float* o_lin, const float* rinv, const vdn_layout_t& l,
+                                  float* dgates, void* dos, float* dlin, float* dvec,
+                                  hipStream_t s) {
+  if (l.dtype != VDN_BF16) return hipErrorNotSupported;
+  switch (l.head_dim_k) {
+    case 128: return launch_bwd_saved<128>(dO, gates, o_soft, o_lin, rinv, l, dgates, dos, dlin, dvec, s);
+    case 64: return launch_bwd_saved<64>(dO, gates, o_soft, o_lin, rinv, l, dgates, dos, dlin, dvec, s);
+    case 32: return launch_bwd_saved<32>(dO, gates, o_soft, o_lin, rinv, l, dgates, dos, dlin, dvec, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const float* gates,
                         const vdn_layout_t& l, float eps, void* o, hipStream_t s) {

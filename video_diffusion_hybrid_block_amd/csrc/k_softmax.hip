@@ -393,6 +393,9 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // the gradient of the linear read before RMSNorm.  MODE 4 writes the two
 // gated branches of MODE 2 as MXFP8 codes and block scales (the activation
 // operand of the FP8 output projection), quantized from the fp32 values.
+// MODE 5 (training forward) writes MODE 1's output and keeps, for a later
+// backward, O_soft and n = RMSNorm(R q) in fp32 and per row the log-sum-exp
+// and the RMS factor 1/r.
 template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -750,6 +753,35 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       return;
     }
     const float g0 = sigmoidf(gl.x) * inv, g1 = sigmoidf(gl.y) * rinv;
+    if constexpr (MODE == 5) {
+      // Training forward: besides the merged output, keep what the merge
+      // backward needs: O_s = oacc * inv and n = lin * rinv (fp32, the
+      // layout of q), and per (b, h, token) the log-sum-exp in exp2 units
+      // and 1 / r.
+      if (qvalid) {
+        float* osrow = bio.o_soft + qoff;
+        float* onrow = bio.o_lin + qoff;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = db * 32 + jj * 8 + half * 4;
+            f32x4 vs, vn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              vs[e] = oacc[db][jj * 4 + e] * inv;
+              vn[e] = lin[db][jj * 4 + e] * rinv;
+            }
+            *(f32x4*)(osrow + d) = vs;
+            *(f32x4*)(onrow + d) = vn;
+          }
+        if (half == 0) {
+          const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
+          bio.lse[ri] = fmaf(m_run, c, __log2f(1.0f / inv));
+          bio.rinv[ri] = rinv;
+        }
+      }
+    }
     if constexpr (MODE == 4) {
       // MXFP8 branches: block db of a branch holds d in [32 db, 32 db + 32)
       // of this head, 16 values in this lane and 16 in lane l ^ 32 (same
@@ -781,7 +813,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       return;
     }
     if (qvalid) {
-      if constexpr (MODE == 1) {
+      if constexpr (MODE == 1 || MODE == 5) {
         bf16* orow = o + qoff;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -885,6 +917,10 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
       softmax_vt_kernel<D, 4><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
           l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, bio);
+    else if (mode == 5)
+      softmax_vt_kernel<D, 5><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, bio);
     else
       softmax_vt_kernel<D, 0><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
@@ -968,6 +1004,20 @@ hipError_t launch_softmax_branches_mxfp8(const void* q, const void* k, const voi
     case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
     case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
     case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_softmax_merge_train(const void* q, const void* k, const void* v,
+                                      const void* tk, const void* tv, const float* R,
+                                      const float* gates, const vdn_layout_t& l, float scale,
+                                      float eps, void* o, const EpilogueIO& io, void* ws,
+                                      hipStream_t s) {
+  if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
+  switch (l.head_dim_k) {
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
   }
   return hipErrorInvalidValue;
 }

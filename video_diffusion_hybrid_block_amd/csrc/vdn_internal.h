@@ -239,6 +239,8 @@ hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, con
 // [B,H,N] fp32.
 // MXFP8 branches: mx_scales [B*N][2*H*d/32] receives the E8M0 block scales
 // (the E4M3 codes go to the kernel's output pointer, [B*N][2*H*d] bytes).
+// Training forward: o_soft = O_soft and o_lin = RMSNorm(R q), [B,N,H,d] fp32,
+// and per (b, h, token) lse (as above) and rinv = 1 / r, [B,H,N] fp32.
 struct EpilogueIO {
   const __bf16* dO;
   float* dgates;
@@ -247,7 +249,24 @@ struct EpilogueIO {
   float* dvec;
   float* lse;
   uint8_t* mx_scales;
+  float* o_soft;
+  float* o_lin;
+  float* rinv;
 };
+// Training forward: the merged output of launch_softmax_merge plus the
+// residuals named under EpilogueIO (o_soft, o_lin, lse, rinv).
+hipError_t launch_softmax_merge_train(const void* q, const void* k, const void* v,
+                                      const void* tk, const void* tv, const float* R,
+                                      const float* gates, const vdn_layout_t& l, float scale,
+                                      float eps, void* o, const EpilogueIO& io, void* ws,
+                                      hipStream_t s);
+// Merge backward from the training forward's residuals (bf16 dO, d = 32, 64
+// or 128): dgates, dos, dlin and dvec as the backward softmax epilogue
+// writes them, from o_soft, o_lin and rinv instead of a recomputation.
+hipError_t launch_merge_bwd_saved(const void* dO, const float* gates, const float* o_soft,
+                                  const float* o_lin, const float* rinv, const vdn_layout_t& l,
+                                  float* dgates, void* dos, float* dlin, float* dvec,
+                                  hipStream_t s);
 // The two gated branches as MXFP8 (E4M3 codes, one E8M0 scale per 32
 // consecutive d of one head and branch), quantized in the epilogue from the
 // fp32 values: codes [B*N][2*H*d] bytes (softmax branch first, as x2),

@@ -141,7 +141,7 @@ def _grads_close(got, ref):
     return errs
 
 
-TRAIN_CASES = [CASES[0], CASES[2], CASES[4], CASES[5]]
+TRAIN_CASES = [CASES[0], CASES[1], CASES[2], CASES[4], CASES[5]]
 
 
 @pytest.mark.timeout(600)
@@ -150,7 +150,9 @@ def test_training_pair_matches_recompute_and_oracle(case):
     """vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: the output is
     vdn_hybrid_attn_fwd's bit for bit; the gradients equal
     vdn_hybrid_attn_bwd's up to the summation order of the merge backward's
-    dot products (bound 1e-5) and meet the oracle bound."""
+    dot products (bound 1e-5) and meet the oracle bound.  Layouts: d = 64
+    with text, d = 128 with batch 2 and a ragged tile, d = 32 without text,
+    the softmax branch gated off, one frame."""
     require_gpu()
     case = dict(case)
     af = case.pop("anchor_first", True)

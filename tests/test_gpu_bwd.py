@@ -227,3 +227,44 @@ def test_training_pair_768p_matches_recompute():
           flush=True)
     bad = {k_: e for k_, e in errs.items() if not e <= 1e-5}
     assert not bad, bad
+
+
+@pytest.mark.timeout(600)
+def test_training_pair_reuses_one_saved_buffer():
+    """One saved buffer serves consecutive training steps: a step on new
+    inputs (other q, v and gate logits) after a step on the first ones gives
+    bit for bit what a fresh buffer gives, so nothing of the first step
+    leaks into the second."""
+    require_gpu()
+    case = dict(CASES[0])
+    case.pop("anchor_first", None)
+    case.pop("anchor_last", None)
+    w = custom(**case)
+    _announce("training pair, saved buffer reused")
+    inp = synth.make_inputs(w)
+    dO = synth.round_bf16(np.random.default_rng(w.seed + 7).standard_normal(inp["q"].shape))
+    dev = to_dev(inp, w.dtype)
+    dev2 = dict(dev)
+    dev2["q"] = dev["q"].flip(1).contiguous()
+    dev2["v"] = dev["v"].flip(1).contiguous()
+    dev2["gate_logits"] = -dev["gate_logits"]
+    geo = dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame,
+               chunk_frames=w.chunk_frames, window_chunks=w.window_chunks)
+    dOd = torch.from_numpy(dO).to(torch.bfloat16).cuda()
+
+    def step(d, saved):
+        args = (d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["beta"], d["alpha"],
+                d["gate_logits"])
+        o, saved = V.hybrid_attn_fwd_train(*args, **geo, saved=saved)
+        g = V.hybrid_attn_bwd_saved(*args, dOd, saved, **geo)
+        return o, g, saved
+
+    _, _, saved = step(dev, None)
+    o_reused, g_reused, _ = step(dev2, saved)
+    o_fresh, g_fresh, _ = step(dev2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o_reused.view(torch.int16), o_fresh.view(torch.int16))
+    for key in G.GRAD_KEYS:
+        if g_fresh.get(key) is None:
+            continue
+        assert torch.equal(g_reused[key], g_fresh[key]), key

@@ -360,6 +360,42 @@ def test_bitwise_deterministic_and_workspace_independent():
     assert torch.equal(a, b_) and torch.equal(a, c)
 
 
+def test_layer_replays_from_a_hip_graph_bit_exact():
+    """The layer enqueues only kernels on the caller's stream (no memset, no
+    allocation, no host synchronisation), so it can be captured into a HIP
+    graph.  Three replays, with eager layer calls on other inputs and host
+    synchronisations between them, each reproduce the eager output bit for
+    bit, and the eager calls in between are unaffected."""
+    require_gpu()
+    w = workload("small_bf16")
+    _announce("graph capture small_bf16")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    other = dict(dev)
+    other["q"] = dev["q"].flip(1).contiguous()
+    ref = run_layer(w, dev).clone()
+    ref_other = run_layer(w, other).clone()
+    lay = V.make_layout(batch=w.batch, heads=w.heads, head_dim=w.head_dim, frames=w.frames,
+                        tokens_per_frame=w.tokens_per_frame, text_tokens=w.text_tokens, dtype="bf16")
+    ws = torch.empty(V.workspace_size(lay), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_layer(w, dev, out=out, workspace=ws)       # warm-up off the default stream
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        V.hybrid_attn(dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["beta"],
+                      dev["alpha"], dev["gate_logits"], **geo_kw(w), out=out, workspace=ws)
+    for r in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+        assert torch.equal(run_layer(w, other), ref_other), f"eager call after replay {r}"
+
+
 def test_output_guard_bands_untouched():
     """Writes stay inside O: a larger buffer around it keeps its sentinel."""
     require_gpu()

@@ -447,15 +447,18 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
 // 4. Per token of every frame (slot T: the text tokens): dk, dv, dbeta
 // (written; zero for frames no chain folds; the softmax backward adds its
 // dk, dv afterwards).  Workgroup = (batch, head, slot, chunk of GB_CH
-// tokens), 4 waves x 32 tokens at a time.  With As = dA + dA^T:
+// tokens: a whole frame up to 1024 tokens, so the staging of As and dB below
+// serves as many tokens as possible), GB_NT / 64 waves x 32 tokens at a
+// time.  With As = dA + dA^T:
 // U = K As^T, W = K dB^T, Z = V dB (tokens x d each) on MFMA, As and dB as
 // bf16 hi + lo in swizzled LDS (As and dB rows for U and W, dB columns for
 // Z); dk = beta (U + Z), dv = beta W, dbeta = sum_r (k_r U_r / 2 + v_r W_r).
 // ---------------------------------------------------------------------------
-constexpr int GB_CH = 256;
+constexpr int GB_CH = 1024;
+constexpr int GB_NT = 512;
 
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(GB_NT)
 gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
                      const bf16* __restrict__ tk, const bf16* __restrict__ tv,
                      const float* __restrict__ beta, const float* __restrict__ dA,
@@ -490,8 +493,8 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   float* dvb = (text ? dtv : dv) + base * D;
   const size_t HD = (size_t)H * D;
   if (!live) {
-    for (int i = tid; i < nmine; i += 256) dbrow[(size_t)i * H] = 0.f;
-    for (int i = tid; i < nmine * (D / 4); i += 256) {
+    for (int i = tid; i < nmine; i += GB_NT) dbrow[(size_t)i * H] = 0.f;
+    for (int i = tid; i < nmine * (D / 4); i += GB_NT) {
       const int t = i / (D / 4), c = (i % (D / 4)) * 4;
       *(f32x4*)(dkb + (size_t)t * HD + c) = f32x4{};
       *(f32x4*)(dvb + (size_t)t * HD + c) = f32x4{};
@@ -505,10 +508,10 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   // is formed from coalesced row reads
   float VDN_LDS* dAl = (float VDN_LDS*)Bh;            // d x d floats: both dB tiles
 #pragma unroll 1
-  for (int i = tid; i < D * D / 4; i += 256) *(f32x4 VDN_LDS*)(dAl + i * 4) = *(const f32x4*)(dAs + i * 4);
+  for (int i = tid; i < D * D / 4; i += GB_NT) *(f32x4 VDN_LDS*)(dAl + i * 4) = *(const f32x4*)(dAs + i * 4);
   __syncthreads();
 #pragma unroll 1
-  for (int i = tid; i < D * D / 8; i += 256) {
+  for (int i = tid; i < D * D / 8; i += GB_NT) {
     const int r = i / (D / 8), c = (i % (D / 8)) * 8;
     bf16x8 ah, al;
 #pragma unroll
@@ -524,7 +527,7 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   }
   __syncthreads();
 #pragma unroll 1
-  for (int i = tid; i < D * D / 8; i += 256) {
+  for (int i = tid; i < D * D / 8; i += GB_NT) {
     const int r = i / (D / 8), c = (i % (D / 8)) * 8;
     const f32x4 b0 = *(const f32x4*)(dBs + (size_t)r * D + c);
     const f32x4 b1 = *(const f32x4*)(dBs + (size_t)r * D + c + 4);
@@ -545,7 +548,7 @@ gram_bwd_mfma_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   const bf16* vb = (text ? tv : v) + base * D;
   const float* bt = beta + ((size_t)b * NB + (text ? N : slot * g.P) + i0) * H + h;
 
-  for (int t0 = wv * 32; t0 < nmine; t0 += 128) {
+  for (int t0 = wv * 32; t0 < nmine; t0 += GB_NT / 2) {
     const int tl = imin(t0 + (lane & 31), nmine - 1);   // A-operand row (clamped)
     bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
@@ -648,7 +651,7 @@ hipError_t launch_gram_bwd_d(const void* k, const void* v, const void* tk, const
                              const vdn_layout_t& l, hipStream_t s) {
   Geo g = make_geo(l);
   const int nch = (imax(g.P, g.L) + GB_CH - 1) / GB_CH;
-  gram_bwd_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1) * nch)), dim3(256), 0, s>>>(
+  gram_bwd_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1) * nch)), dim3(GB_NT), 0, s>>>(
       (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv, beta, dA, dB, dk, dv,
       dtk, dtv, dbeta, g, l.heads, nch);
   return hipGetLastError();

@@ -36,7 +36,7 @@ namespace {
 // 1. dR and the linear part of dq.  Workgroup = (batch, head, slot, chunk of
 // DR_CH of the slot's tokens); partial dR per chunk, summed by dr_sum_kernel.
 // ---------------------------------------------------------------------------
-constexpr int DR_CH = 256;               // tokens per workgroup
+constexpr int DR_CH = 1024;              // tokens per workgroup
 constexpr int DR_TT = 64;                // tokens per LDS tile
 
 // Video tokens of read slot `slot`: a chunk's non-anchor frames, which are
@@ -223,53 +223,66 @@ dr_sum_kernel(const float4* __restrict__ part, float4* __restrict__ dR, int nch,
 }
 
 // ---------------------------------------------------------------------------
-// d x d x d products for the per-frame step: a 16 x 16 thread grid, thread
-// (ti, tj) owning a d/16 x d/16 block made of groups of W = min(4, d/16)
-// consecutive rows: rows 16 W hh + W ti + {0..W-1} for each group hh, columns
-// likewise from tj.  W consecutive elements let every LDS read be 4 W bytes
-// wide; spreading the groups 16 W apart keeps the distinct ti (tj) of a wave
-// on different banks.
+// d x d x d products for the per-frame step: a 32 x 16 thread grid (512
+// threads, two waves per SIMD on the one workgroup the LDS allows per CU),
+// thread (ti, tj) owning a d/32 x d/16 block.  Rows come in groups of
+// WR = min(4, d/32) consecutive rows, group hh at 32 WR hh + WR ti; columns
+// in groups of W = min(4, d/16), group hh at 16 W hh + W tj.  Consecutive
+// rows / columns let every LDS read be 4 W (4 WR) bytes wide; spreading the
+// groups keeps the distinct ti (tj) of a wave on different banks.
 // ---------------------------------------------------------------------------
+constexpr int FR_NT = 512;
+
 template <int D>
 struct Tile {
-  static constexpr int RB = D / 16;              // rows (columns) per thread
-  static constexpr int W = RB < 4 ? RB : 4;      // consecutive rows per group
-  static constexpr int NH = RB / W;              // groups
-  static constexpr int LD = D + W;               // padded LDS row (floats)
-  static_assert(D % 16 == 0 && D >= 32 && D <= 128, "d = 32, 64 or 128");
+  static constexpr int RR = D / 32;              // rows per thread
+  static constexpr int RB = D / 16;              // columns per thread
+  static constexpr int WR = RR < 4 ? RR : 4;     // consecutive rows per group
+  static constexpr int W = RB < 4 ? RB : 4;      // consecutive columns per group
+  static constexpr int NHR = RR / WR;            // row groups
+  static constexpr int NH = RB / W;              // column groups
+  static constexpr int LD = D + 4;               // padded LDS row (floats)
+  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "d = 32, 64 or 128");
 };
 
 template <int W>
 using fvec = float __attribute__((ext_vector_type(W)));
 
-// row (column) x in [0, d/16) of thread index t in [0, 16)
+// row x in [0, d/32) of thread row index ti in [0, 32)
 template <int D>
-__device__ __forceinline__ int blk(int t, int x) {
+__device__ __forceinline__ int blk_r(int ti, int x) {
+  constexpr int WR = Tile<D>::WR;
+  return (x / WR) * 32 * WR + ti * WR + x % WR;
+}
+// column c in [0, d/16) of thread column index tj in [0, 16)
+template <int D>
+__device__ __forceinline__ int blk_c(int tj, int c) {
   constexpr int W = Tile<D>::W;
-  return (x / W) * 16 * W + t * W + x % W;
+  return (c / W) * 16 * W + tj * W + c % W;
 }
 
 // acc += op(A) * B, A and B in LDS ([D][LD]), op(A) = A or A^T.
 template <int D, bool TA>
 __device__ __forceinline__ void mm_acc(const float* A, const float* B, int ti, int tj,
-                                       float (&acc)[D / 16][D / 16]) {
-  constexpr int RB = Tile<D>::RB, W = Tile<D>::W, NH = Tile<D>::NH, LD = Tile<D>::LD;
+                                       float (&acc)[D / 32][D / 16]) {
+  constexpr int RR = Tile<D>::RR, RB = Tile<D>::RB, W = Tile<D>::W, WR = Tile<D>::WR;
+  constexpr int NHR = Tile<D>::NHR, NH = Tile<D>::NH, LD = Tile<D>::LD;
 #pragma unroll 2
   for (int k = 0; k < D; k += W) {
-    float av[RB][W], bv[W][RB];          // av[row][kk], bv[kk][col]
+    float av[RR][W], bv[W][RB];          // av[row][kk], bv[kk][col]
     if constexpr (TA) {
 #pragma unroll
       for (int kk = 0; kk < W; ++kk)
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          const fvec<W> x = *(const fvec<W>*)(A + (k + kk) * LD + hh * 16 * W + ti * W);
+        for (int hh = 0; hh < NHR; ++hh) {
+          const fvec<WR> x = *(const fvec<WR>*)(A + (k + kk) * LD + hh * 32 * WR + ti * WR);
 #pragma unroll
-          for (int q = 0; q < W; ++q) av[hh * W + q][kk] = x[q];
+          for (int q = 0; q < WR; ++q) av[hh * WR + q][kk] = x[q];
         }
     } else {
 #pragma unroll
-      for (int a = 0; a < RB; ++a) {
-        const fvec<W> x = *(const fvec<W>*)(A + blk<D>(ti, a) * LD + k);
+      for (int a = 0; a < RR; ++a) {
+        const fvec<W> x = *(const fvec<W>*)(A + blk_r<D>(ti, a) * LD + k);
 #pragma unroll
         for (int q = 0; q < W; ++q) av[a][q] = x[q];
       }
@@ -285,7 +298,7 @@ __device__ __forceinline__ void mm_acc(const float* A, const float* B, int ti, i
 #pragma unroll
     for (int kk = 0; kk < W; ++kk)
 #pragma unroll
-      for (int a = 0; a < RB; ++a)
+      for (int a = 0; a < RR; ++a)
 #pragma unroll
         for (int c = 0; c < RB; ++c) acc[a][c] = fmaf(av[a][kk], bv[kk][c], acc[a][c]);
   }
@@ -297,7 +310,7 @@ template <int D, typename F>
 __device__ __forceinline__ void stage_mat(float* dst, const float* s0, const float* s1, F f,
                                           int tid) {
   constexpr int W = Tile<D>::W, LD = Tile<D>::LD;
-  for (int i = tid; i < D * D / W; i += 256) {
+  for (int i = tid; i < D * D / W; i += FR_NT) {
     const fvec<W> x = *(const fvec<W>*)(s0 + i * W);
     const fvec<W> y = *(const fvec<W>*)(s1 + i * W);
     fvec<W> r;
@@ -310,7 +323,7 @@ __device__ __forceinline__ void stage_mat(float* dst, const float* s0, const flo
 template <int D>
 __device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) {
   constexpr int W = Tile<D>::W, LD = Tile<D>::LD;
-  for (int i = tid; i < D * D / W; i += 256)
+  for (int i = tid; i < D * D / W; i += FR_NT)
     *(fvec<W>*)(dst + (i * W / D) * LD + (i * W) % D) = *(const fvec<W>*)(src + i * W);
 }
 
@@ -318,14 +331,14 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) 
 // 3. Per frame (and the text slot T): dA, dB in place of G, B; dalpha.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(FR_NT)
 vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
                      const float* __restrict__ alpha, const float* __restrict__ states,
                      const float* __restrict__ dspost, float* __restrict__ dalpha, Geo g, int H) {
-  constexpr int RB = Tile<D>::RB, LD = Tile<D>::LD;
+  constexpr int RR = Tile<D>::RR, RB = Tile<D>::RB, LD = Tile<D>::LD;
   __shared__ __attribute__((aligned(16))) float L1[D * LD];
   __shared__ __attribute__((aligned(16))) float L2[D * LD];
-  __shared__ float red[256];
+  __shared__ float red[FR_NT];
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tj = tid & 15;
   const int slot = blockIdx.x % (g.T + 1);
@@ -341,16 +354,16 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
   if (!live) {
     // no chain reads this slot: zero gradients (its statistics were never
     // formed)
-    for (int i = tid; i < D * D; i += 256) {
+    for (int i = tid; i < D * D; i += FR_NT) {
       Gs[i] = 0.f;
       Bs[i] = 0.f;
     }
     if (!text && tid == 0) dalpha[((size_t)b * g.T + slot) * H + h] = 0.f;
     return;
   }
-  float dB[RB][RB], dG[RB][RB];
+  float dB[RR][RB], dG[RR][RB];
 #pragma unroll
-  for (int a = 0; a < RB; ++a)
+  for (int a = 0; a < RR; ++a)
 #pragma unroll
     for (int c = 0; c < RB; ++c) dB[a][c] = dG[a][c] = 0.f;
   float dal = 0.f;
@@ -379,18 +392,18 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
       load_mat<D>(L1, dSj, tid);
       load_mat<D>(L2, Gs, tid);
       __syncthreads();
-      float dX[RB][RB];
+      float dX[RR][RB];
 #pragma unroll
-      for (int x = 0; x < RB; ++x)
+      for (int x = 0; x < RR; ++x)
 #pragma unroll
         for (int c = 0; c < RB; ++c) dX[x][c] = 0.f;
       mm_acc<D, false>(L1, L2, ti, tj, dX);
 #pragma unroll
-      for (int x = 0; x < RB; ++x)
+      for (int x = 0; x < RR; ++x)
 #pragma unroll
         for (int c = 0; c < RB; ++c) {
           dB[x][c] += dX[x][c];
-          dal = fmaf(dX[x][c], Sp[(size_t)blk<D>(ti, x) * D + blk<D>(tj, c)], dal);
+          dal = fmaf(dX[x][c], Sp[(size_t)blk_r<D>(ti, x) * D + blk_c<D>(tj, c)], dal);
         }
       __syncthreads();
       // X = alpha S_{j-1} + B_f
@@ -401,7 +414,7 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
     }
     red[tid] = dal;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
+    for (int s = FR_NT / 2; s > 0; s >>= 1) {
       if (tid < s) red[tid] += red[tid + s];
       __syncthreads();
     }
@@ -410,34 +423,34 @@ vda_frame_bwd_kernel(float* __restrict__ GA, float* __restrict__ BB,
   // dA = -G dG G
   load_mat<D>(L2, Gs, tid);
 #pragma unroll
-  for (int x = 0; x < RB; ++x)
+  for (int x = 0; x < RR; ++x)
 #pragma unroll
-    for (int c = 0; c < RB; ++c) L1[blk<D>(ti, x) * LD + blk<D>(tj, c)] = dG[x][c];
+    for (int c = 0; c < RB; ++c) L1[blk_r<D>(ti, x) * LD + blk_c<D>(tj, c)] = dG[x][c];
   __syncthreads();
-  float t1[RB][RB];
+  float t1[RR][RB];
 #pragma unroll
-  for (int x = 0; x < RB; ++x)
+  for (int x = 0; x < RR; ++x)
 #pragma unroll
     for (int c = 0; c < RB; ++c) t1[x][c] = 0.f;
   mm_acc<D, false>(L2, L1, ti, tj, t1);     // G dG
   __syncthreads();
 #pragma unroll
-  for (int x = 0; x < RB; ++x)
+  for (int x = 0; x < RR; ++x)
 #pragma unroll
-    for (int c = 0; c < RB; ++c) L1[blk<D>(ti, x) * LD + blk<D>(tj, c)] = t1[x][c];
+    for (int c = 0; c < RB; ++c) L1[blk_r<D>(ti, x) * LD + blk_c<D>(tj, c)] = t1[x][c];
   __syncthreads();
-  float t2[RB][RB];
+  float t2[RR][RB];
 #pragma unroll
-  for (int x = 0; x < RB; ++x)
+  for (int x = 0; x < RR; ++x)
 #pragma unroll
     for (int c = 0; c < RB; ++c) t2[x][c] = 0.f;
   mm_acc<D, false>(L1, L2, ti, tj, t2);     // (G dG) G
   __syncthreads();                          // every read of G_f / B_f done
 #pragma unroll
-  for (int x = 0; x < RB; ++x)
+  for (int x = 0; x < RR; ++x)
 #pragma unroll
     for (int c = 0; c < RB; ++c) {
-      const size_t e = (size_t)blk<D>(ti, x) * D + blk<D>(tj, c);
+      const size_t e = (size_t)blk_r<D>(ti, x) * D + blk_c<D>(tj, c);
       Gs[e] = -t2[x][c];
       Bs[e] = dB[x][c];
     }
@@ -639,7 +652,7 @@ hipError_t launch_frame_d(float* GA, float* BB, const float* alpha, const float*
                           const float* dspost, float* dalpha, const vdn_layout_t& l,
                           hipStream_t s) {
   Geo g = make_geo(l);
-  vda_frame_bwd_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1))), dim3(256), 0, s>>>(
+  vda_frame_bwd_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.T + 1))), dim3(FR_NT), 0, s>>>(
       GA, BB, alpha, states, dspost, dalpha, g, l.heads);
   return hipGetLastError();
 }

@@ -69,14 +69,19 @@ __device__ __forceinline__ int slot_tok(const SlotMap& m, int i) {
   return i < m.split ? m.base0 + i : m.base1 + i;
 }
 
+// Threads of a dR workgroup: its LDS (R hi + lo, three token tiles) allows
+// one workgroup per CU at d = 128, so eight waves there (two per SIMD).
+constexpr int dr_threads(int d) { return d == 128 ? 512 : 256; }
+
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(dr_threads(D))
 dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
                const float* __restrict__ R, float* __restrict__ dRp, float* __restrict__ dq,
                Geo g, int H, int nch) {
   constexpr int MAT = D * D * 2;         // bf16 d x d tile, bytes
   constexpr int TB = DR_TT * D * 2;      // bf16 token tile, bytes
   constexpr int NBK = D / 32;
+  constexpr int NT = dr_threads(D), NW = NT / 64;
   __shared__ __attribute__((aligned(16))) char rh[MAT];
   __shared__ __attribute__((aligned(16))) char rl[MAT];
   __shared__ __attribute__((aligned(16))) char qs[TB];
@@ -101,7 +106,7 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
   float* part = dRp + (((size_t)bh * (g.nc + 1) + slot) * nch + ch) * mat;
   // R of the slot, hi + lo, row-major swizzled (read column-wise for dq)
   const float* Rs = R + ((size_t)bh * (g.nc + 1) + slot) * mat;
-  for (int i = tid; i < D * D / 8; i += 256) {
+  for (int i = tid; i < D * D / 8; i += NT) {
     const int r = i / (D / 8), c = (i % (D / 8)) * 8;
     const f32x4 a = *(const f32x4*)(Rs + r * D + c);
     const f32x4 a2 = *(const f32x4*)(Rs + r * D + c + 4);
@@ -118,13 +123,13 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
     *(bf16x8 VDN_LDS*)(Rl + swz_off<D>(r, c)) = lv;
   }
   // this wave's dR blocks: (rb, cb) = wave-strided over the NBK x NBK grid
-  constexpr int BPW = NBK * NBK >= 4 ? NBK * NBK / 4 : 1;
+  constexpr int BPW = NBK * NBK >= NW ? NBK * NBK / NW : 1;
   f32x16 acc[BPW];
 #pragma unroll
   for (int u = 0; u < BPW; ++u) acc[u] = f32x16{};
   for (int t0 = 0; t0 < nmine; t0 += DR_TT) {
     __syncthreads();                     // previous tile consumed (and R staged)
-    for (int i = tid; i < DR_TT * D / 8; i += 256) {
+    for (int i = tid; i < DR_TT * D / 8; i += NT) {
       const int r = i / (D / 8), c = (i % (D / 8)) * 8;
       bf16x8 qv = {}, hv = {}, lv = {};
       if (t0 + r < nmine) {
@@ -162,14 +167,13 @@ dr_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ dlin,
         acc[u] = mfma32(al, bq, acc[u]);
       }
     }
-    // dq[t][c] = sum_r dlin[t][r] R[r][c]: wave w takes tokens 32*(w/2) ..,
-    // column blocks (w%2)*NBK/2 ..; A = dlin rows, B = R columns
-    if (NBK >= 2 || wv % 2 == 0) {
-      const int tb = wv >> 1;
-      const int ncb = NBK >= 2 ? NBK / 2 : 1;
+    // dq[t][c] = sum_r dlin[t][r] R[r][c] over (token block, column block)
+    // pairs, wave-strided; A = dlin rows, B = R columns
+    {
+      constexpr int NPAIR = (DR_TT / 32) * NBK;
 #pragma unroll
-      for (int u = 0; u < ncb; ++u) {
-        const int cb = (NBK >= 2 ? (wv & 1) * ncb : 0) + u;
+      for (int pi = wv; pi < NPAIR; pi += NW) {
+        const int tb = pi / NBK, cb = pi % NBK;
         f32x16 o = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
@@ -635,7 +639,7 @@ hipError_t launch_dr_d(const void* q, const float* dlin, const float* R, float* 
                        float* dq, const vdn_layout_t& l, hipStream_t s) {
   Geo g = make_geo(l);
   const int nch = dr_chunks(g);
-  dr_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.nc + 1) * nch)), dim3(256), 0, s>>>(
+  dr_mfma_kernel<D><<<dim3((unsigned)((long)l.batch * l.heads * (g.nc + 1) * nch)), dim3(dr_threads(D)), 0, s>>>(
       (const bf16*)q, dlin, R, dRp, dq, g, l.heads, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -1,6 +1,7 @@
 // Backward pass of the linear (VDA) branch, after the merge backward:
 //
-//  1. read slots (dr_kernel): each video token reads o = R_c q with R_c its
+//  1. read slots (dr_mfma_kernel + dr_sum_kernel): each video token reads
+//     o = R_c q with R_c its
 //     chunk's summed state (slot nc, the text write, for anchor frames), so
 //     dR_c = sum_i do_i q_i^T over the slot's tokens and q_i gets R_c^T do_i
 //     (written as the first part of dq);
@@ -12,8 +13,9 @@
 //     the chains that fold f; G = (I + A)^-1 gives dA_f = -G dG_f G.  The text
 //     write S_x = B_x G_x starts both chains at S_x / 2, so
 //     dS_x = (dS_0^fwd + dS_0^bwd) / 2, dB_x = dS_x G_x, dG_x = B_x^T dS_x;
-//  4. per token (gram_bwd_kernel): A = sum beta k k^T, B = sum beta v k^T give
-//     dk_i += beta_i ((dA + dA^T) k_i + dB^T v_i), dv_i += beta_i dB k_i,
+//  4. per token (gram_bwd_mfma_kernel): A = sum beta k k^T, B = sum beta v k^T
+//     give dk_i = beta_i ((dA + dA^T) k_i + dB^T v_i), dv_i = beta_i dB k_i
+//     (written; the softmax backward adds its part afterwards) and
 //     dbeta_i = k_i^T dA k_i + v_i^T dB k_i.
 // [the forward: deepmagic blog "生成比播放還快", section 用兩條分支取代一條
 //  (S = (S̄ + B)(I + A)^-1); PaperDaily "伯克利与Impossible视频生成" §三 (two

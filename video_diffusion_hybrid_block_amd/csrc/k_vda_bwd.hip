@@ -1,10 +1,9 @@
 // Backward pass of the linear (VDA) branch, after the merge backward:
 //
 //  1. read slots (dr_mfma_kernel + dr_sum_kernel): each video token reads
-//     o = R_c q with R_c its
-//     chunk's summed state (slot nc, the text write, for anchor frames), so
-//     dR_c = sum_i do_i q_i^T over the slot's tokens and q_i gets R_c^T do_i
-//     (written as the first part of dq);
+//     o = R_c q with R_c its chunk's summed state (slot nc, the text write,
+//     for anchor frames), so dR_c = sum_i do_i q_i^T over the slot's tokens
+//     and q_i gets R_c^T do_i (written as the first part of dq);
 //  2. the reverse scan (k_scan.hip) turns dR into dS_j, the gradient of each
 //     chain's state after each step;
 //  3. per frame (vda_frame_bwd_kernel): a step S_j = X_j G_j with

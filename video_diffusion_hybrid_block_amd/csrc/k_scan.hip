@@ -278,13 +278,13 @@ scan_bwd_kernel(const float* __restrict__ G, const float* __restrict__ dR,
   constexpr int CPR = D / 4;
   constexpr int GBYTES = D * D * 4;
   constexpr int NGI = GBYTES / 1024 / NRB;
-  __shared__ __attribute__((aligned(1024))) char gbuf[2 * GBYTES];
-  __shared__ __attribute__((aligned(16))) float S[32 * LDF];
-  __shared__ __attribute__((aligned(16))) char xh[32 * D * 2];
-  __shared__ __attribute__((aligned(16))) char xl[32 * D * 2];
-  char VDN_LDS* Gl = (char VDN_LDS*)gbuf;
-  char VDN_LDS* Xh = (char VDN_LDS*)xh;
-  char VDN_LDS* Xl = (char VDN_LDS*)xl;
+  // one allocation, as in the forward scan: with separate __shared__ arrays
+  // the compiler waits for the next G copy before writing X
+  __shared__ __attribute__((aligned(1024))) char smem[2 * GBYTES + 32 * LDF * 4 + 2 * 32 * D * 2];
+  char VDN_LDS* Gl = (char VDN_LDS*)smem;
+  float VDN_LDS* S = (float VDN_LDS*)(smem + 2 * GBYTES);
+  char VDN_LDS* Xh = (char VDN_LDS*)(smem + 2 * GBYTES + 32 * LDF * 4);
+  char VDN_LDS* Xl = Xh + 32 * D * 2;
   auto gsw = [](int row) { return CPR >= 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int tid = threadIdx.x;

@@ -135,7 +135,7 @@ def main():
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the layer shards by head; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

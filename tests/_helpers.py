@@ -57,11 +57,13 @@ def rel_err(got, ref) -> float:
 
 
 def sample_tokens(w: synth.Workload, rng) -> np.ndarray:
-    """Tokens spanning anchor, edge and interior frames, tile starts and the
-    ragged tail of every frame."""
+    """Tokens spanning anchor, edge and interior frames, and inside every
+    frame both sides of each 256-query work-item edge of the softmax kernel
+    (255/256, 511/512, 767/768), the 32-query wave edges (31/32), the start of
+    the ragged last item (P - 240 at P = 1008) and the frame's last rows."""
     T, P = w.frames, w.tokens_per_frame
     frames = sorted({f for f in (0, 1, 4, 5, 9, 10, T // 2, T - 6, T - 5, T - 2, T - 1) if 0 <= f < T})
-    local = {0, 1, 31, 32, 127, 128, P - 113, P - 33, P - 2, P - 1}
+    local = {0, 1, 31, 32, 255, 256, 511, 512, 767, 768, P - 240, P - 113, P - 33, P - 2, P - 1}
     local |= set(rng.integers(0, P, size=4).tolist())
     local = sorted(x for x in local if 0 <= x < P)
     return np.array([f * P + x for f in frames for x in local], dtype=np.int64)
@@ -88,3 +90,24 @@ def oracle_chunk_reads(inp: dict, lay, w: synth.Workload) -> np.ndarray:
                     R[b, h, c] = per_frame[frames[0]]
             R[b, h, nc] = per_frame[min(anchors)] if anchors else 0.0
     return R
+
+
+def max_abs_ratio(got, ref) -> float:
+    """max |got - ref| / max |ref| (reported beside the Frobenius metric)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def write_parity_summary(name: str, record: dict) -> None:
+    """Append one JSON line per checked configuration to
+    gpurun_out/parity_summary.jsonl under the repository root (a results
+    folder that is not part of the source tree)."""
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = os.path.join(root, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    with open(os.path.join(out, "parity_summary.jsonl"), "a") as fh:
+        fh.write(json.dumps({"config": name, **record}) + "\n")

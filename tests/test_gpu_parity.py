@@ -13,8 +13,8 @@ from oracle import vdn_oracle as O
 from video_diffusion_hybrid_block_amd import binding as V
 from video_diffusion_hybrid_block_amd import synth
 
-from _helpers import (TOL, custom, oracle_chunk_reads, oracle_layout, rel_err, require_gpu,
-                      sample_tokens, to_dev, workload)
+from _helpers import (TOL, custom, max_abs_ratio, oracle_chunk_reads, oracle_layout, rel_err,
+                      require_gpu, sample_tokens, to_dev, workload, write_parity_summary)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,19 +131,29 @@ def test_layer_full_size_sampled(name):
     out = run_layer(w, to_dev(inp, w.dtype))
     lay = oracle_layout(w)
     rng = np.random.default_rng(0)
-    got_all, ref_all = [], []
+    got_all, ref_all, per_head = [], [], {}
     for b in range(w.batch):
         for h in sorted({0, w.heads // 2, w.heads - 1}):
             tok = sample_tokens(w, rng)
             ref = O.hybrid_attn_rows(inp, lay, b, h, tok)
             got = out[b, torch.from_numpy(tok).cuda(), h].float().cpu().numpy()
             e = rel_err(got, ref)
-            print(f"{name} b{b} h{h}: {len(tok)} tokens rel err {e:.3e}")
+            print(f"{name} b{b} h{h}: {len(tok)} tokens rel err {e:.3e}, "
+                  f"max|d|/max|ref| {max_abs_ratio(got, ref):.3e}")
+            per_head[f"b{b}h{h}"] = e
             got_all.append(got)
             ref_all.append(ref)
-    err = rel_err(np.concatenate(got_all), np.concatenate(ref_all))
+    got_all, ref_all = np.concatenate(got_all), np.concatenate(ref_all)
+    err = rel_err(got_all, ref_all)
+    worst = max(per_head, key=per_head.get)
+    write_parity_summary(name, {"tokens_per_head": int(len(tok)), "heads": sorted(per_head),
+                                "rel_frobenius": err, "worst_head": worst,
+                                "worst_head_rel_frobenius": per_head[worst],
+                                "max_abs_over_max_ref": max_abs_ratio(got_all, ref_all),
+                                "tol": TOL[w.dtype]})
     assert torch.isfinite(out).all().item()
     assert err <= TOL[w.dtype]
+    assert per_head[worst] <= TOL[w.dtype], f"worst head {worst}: {per_head[worst]:.3e}"
 
 
 # ---------------------------------------------------------------------------

@@ -397,3 +397,102 @@ def test_readings_alternatives_differ_only_where_expected():
     assert not np.allclose(base, alt7)
     alt6 = O.hybrid_attn(inp, lay, O.Readings(anchor_decay=True))
     assert not np.allclose(base, alt6)
+
+
+# --------------------------------------------------------------------------
+# Alternative readings, each pinned outside its own formula
+# --------------------------------------------------------------------------
+def test_r5_zero_anchor_read_leaves_the_gated_dense_softmax():
+    """R5 alternative (anchor frames read nothing from the linear branch):
+    RMSNorm of a zero read is zero, so an anchor row is sigmoid(l0) times
+    dense attention over every video and text key (an anchor frame sees the
+    whole sequence), computed here by library attention; other rows keep the
+    primary reading's values."""
+    rng = np.random.default_rng(21)
+    lay = O.Layout(batch=1, heads=2, head_dim=6, frames=11, tokens_per_frame=3,
+                   text_tokens=4, chunk_frames=2, window_chunks=1)
+    inp = _rand_inputs(rng, lay)
+    N, P = lay.video_tokens, lay.tokens_per_frame
+    alt = O.hybrid_attn(inp, lay, O.Readings(anchor_read="zero"))
+    base = O.hybrid_attn(inp, lay)
+    anchor_rows = np.r_[0:P, N - P:N]
+    for h in range(lay.heads):
+        km = np.concatenate([inp["k"][0, :, h], inp["text_k"][0, :, h]])
+        vm = np.concatenate([inp["v"][0, :, h], inp["text_v"][0, :, h]])
+        dense = _sdpa(inp["q"][0, anchor_rows, h], km, vm, None)
+        sig0 = 1.0 / (1.0 + np.exp(-inp["gate_logits"][0, anchor_rows, h, 0]))
+        assert np.allclose(alt[0, anchor_rows, h], sig0[:, None] * dense, atol=1e-12)
+    assert np.allclose(alt[:, P:N - P], base[:, P:N - P], atol=0)
+
+
+def _rank_one_update(S_bar, k, v, beta):
+    """One token's joint update by Sherman-Morrison:
+    (S_bar + b v k^T)(I + b k k^T)^-1 = S_bar + b'(v - S_bar k) k^T, b' = b/(1 + b|k|^2)."""
+    bp = beta / (1.0 + beta * (k @ k))
+    return S_bar + bp * np.outer(v - S_bar @ k, k)
+
+
+def test_r6_decay_without_write_matches_token_loop():
+    """R6 alternative (an anchor frame on the far side of a window decays the
+    state but writes nothing).  With one token per frame and one text token
+    every update is rank one, so both states follow from a plain loop over
+    frames with chunk arithmetic: the forward state of query frame t starts at
+    half the text write, decays by alpha_0 at anchor frame 0 when some frame
+    lies before the window, then takes the token update of every frame before
+    the window; the backward state mirrors this from frame T-1 down."""
+    rng = np.random.default_rng(22)
+    C, w, T, d = 2, 1, 15, 5
+    lay = O.Layout(batch=1, heads=1, head_dim=d, frames=T, tokens_per_frame=1,
+                   text_tokens=1, chunk_frames=C, window_chunks=w)
+    inp = _rand_inputs(rng, lay, beta_scale=3.0)
+    inp["alpha"][:] = rng.uniform(0.3, 0.9, size=inp["alpha"].shape)   # decay far from 1
+    k, v, q = inp["k"][0, :, 0], inp["v"][0, :, 0], inp["q"][0, :, 0]
+    beta, alpha = inp["beta"][0, :, 0], inp["alpha"][0, :, 0]
+    S_x = _rank_one_update(np.zeros((d, d)), inp["text_k"][0, 0, 0], inp["text_v"][0, 0, 0], beta[T])
+    _, _, o_lin, _ = O.hybrid_attn_rows(inp, lay, 0, 0, np.arange(T),
+                                        O.Readings(anchor_decay=True), parts=True)
+    for t in range(T):
+        if t in (0, T - 1):
+            assert np.allclose(o_lin[t], S_x @ q[t], atol=1e-12)
+            continue
+        c = t // C
+        lo, hi = max(0, (c - w) * C), min(T, (c + w + 1) * C) - 1
+        Sf = 0.5 * S_x
+        if lo > 1:                          # frames 1 .. lo-1 are far
+            Sf = alpha[0] * Sf
+            for f in range(1, lo):
+                Sf = _rank_one_update(alpha[f] * Sf, k[f], v[f], beta[f])
+        Sb = 0.5 * S_x
+        if hi < T - 2:                      # frames hi+1 .. T-2 are far
+            Sb = alpha[T - 1] * Sb
+            for f in range(T - 2, hi, -1):
+                Sb = _rank_one_update(alpha[f] * Sb, k[f], v[f], beta[f])
+        assert np.allclose(o_lin[t], (Sf + Sb) @ q[t], atol=1e-12)
+
+
+def test_r7_raw_half_write_closed_form():
+    """R7: with orthonormal text keys, video tokens that write nothing
+    (beta = 0) and no decay (alpha = 1), every frame reads twice its start
+    state.  Reading a text key k_j then gives beta_j v_j under the raw half
+    write (0.5 * B_x) and beta_j / (1 + beta_j) v_j under the primary one (the
+    joint update from zero): the evidence weight of an independent direction."""
+    rng = np.random.default_rng(23)
+    d, L = 7, 3
+    lay = O.Layout(batch=1, heads=1, head_dim=d, frames=9, tokens_per_frame=L,
+                   text_tokens=L, chunk_frames=2, window_chunks=1)
+    inp = _rand_inputs(rng, lay)
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, L)))
+    inp["text_k"][0, :, 0] = Qm.T
+    N = lay.video_tokens
+    inp["beta"][0, :N, 0] = 0.0
+    inp["beta"][0, N:, 0] = rng.uniform(0.2, 4.0, size=L)
+    inp["alpha"][:] = 1.0
+    bt, tv = inp["beta"][0, N:, 0], inp["text_v"][0, :, 0]
+    for t in range(lay.frames):
+        inp["q"][0, t * L:(t + 1) * L, 0] = Qm.T        # frame t's queries are the text keys
+    toks = np.arange(N)
+    for reading, weight in (("raw", bt), ("vda", bt / (1 + bt))):
+        _, _, o_lin, _ = O.hybrid_attn_rows(inp, lay, 0, 0, toks, O.Readings(half_write=reading),
+                                            parts=True)
+        want = np.tile(weight[:, None] * tv, (lay.frames, 1))
+        assert np.allclose(o_lin, want, atol=1e-12), reading

@@ -119,6 +119,16 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.vdn_softmax_merge_fwd(*a) == 4
     a = list(sm); a[10] = 16
     assert lib.vdn_softmax_merge_fwd(*a) == 5
+    # the layer's VDA branch: same argument checks as the layer
+    vb = [ok, ok, nul, nul, ok, ok, ref, ok, ok, 1 << 40, nul]
+    a = list(vb); a[7] = nul
+    assert lib.vdn_vda_branch(*a) == 1
+    a = list(vb); a[5] = odd
+    assert lib.vdn_vda_branch(*a) == 4
+    a = list(vb); a[9] = 16
+    assert lib.vdn_vda_branch(*a) == 5
+    a = list(vb); a[6] = ctypes.byref(lay_t)
+    assert lib.vdn_vda_branch(*a) == 1                  # text tensors missing
 
 
 def test_backward_and_training_entry_points_reject_bad_arguments_before_launch():

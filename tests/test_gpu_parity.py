@@ -241,6 +241,57 @@ def test_stage_factor_scan(name):
     assert max(errs) <= tol
 
 
+VDA_BRANCH_CASES = ["small_bf16", "768p", "stress_lowrank"]
+VDA_BRANCH_EDGE = [
+    # P not a multiple of 8: statistics and factor without the V^T copy
+    dict(name="vda_ragged_d64", batch=2, heads=3, head_dim=64, frames=13, tokens_per_frame=50,
+         text_tokens=5, dtype="bf16", chunk_frames=2),
+    dict(name="vda_d32_no_text", batch=1, heads=2, head_dim=32, frames=17, tokens_per_frame=24,
+         text_tokens=0, dtype="bf16", chunk_frames=3),
+    dict(name="vda_d128_one_token", batch=1, heads=2, head_dim=128, frames=14, tokens_per_frame=1,
+         text_tokens=1, dtype="bf16", chunk_frames=2),
+]
+
+
+@pytest.mark.parametrize("case", VDA_BRANCH_CASES + [c["name"] for c in VDA_BRANCH_EDGE])
+def test_stage_vda_branch(case):
+    """The layer's VDA branch as the layer runs it (one pass for statistics,
+    factor and the V^T copy, then the scan from the pre-split G planes),
+    against the oracle's summed states recomputed from scratch per chunk in
+    float64.  Statistics from bf16 hi/lo products (~2^-16), the fp32 sweep
+    (~cond * 6e-8) and the three-pass scan (~2^-16 per step): 2e-3."""
+    require_gpu()
+    edge = {c["name"]: c for c in VDA_BRANCH_EDGE}
+    w = custom(**edge[case]) if case in edge else workload(case)
+    _announce(f"vda branch {case}")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    R = V.vda_branch(dev["k"], dev["v"], dev["text_k"] if L else None,
+                     dev["text_v"] if L else None, dev["beta"], dev["alpha"], **geo_kw(w))
+    torch.cuda.synchronize()
+    R = R.cpu().numpy()
+    lay = oracle_layout(w)
+    nc = lay.num_chunks
+    anchors = O.anchor_frames(lay)
+    heads = range(w.heads) if w.heads <= 8 else [0, w.heads - 1]
+    errs = []
+    for b in range(w.batch):
+        for h in heads:
+            per_frame = O.chunk_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"],
+                                       inp["beta"], inp["alpha"], lay, b, h)
+            if anchors:
+                errs.append(rel_err(R[b, h, nc], per_frame[min(anchors)]))
+            for c in range(nc):
+                t = [f for f in range(c * lay.chunk_frames, min((c + 1) * lay.chunk_frames, w.frames))
+                     if f not in anchors]
+                if t:
+                    errs.append(rel_err(R[b, h, c], per_frame[t[0]]))
+    print(f"{case}: vda branch worst rel err {max(errs):.3e} over {len(errs)} states")
+    assert np.isfinite(R).all()
+    assert max(errs) <= 2e-3
+
+
 @pytest.mark.parametrize("name", STAGE_CASES + ["768p"])
 def test_stage_softmax(name):
     """Softmax branch alone: bf16 P and bf16 output rounding (~2^-9) bound the

@@ -17,7 +17,7 @@ __all__ = [
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
     "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "softmax_branches_mxfp8",
-    "vda_gram", "vda_factor_scan",
+    "vda_gram", "vda_factor_scan", "vda_branch",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
     "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
     "train_saved_size", "hybrid_attn_fwd_train", "hybrid_attn_bwd_saved",
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
     "vdn_hybrid_attn_proj_mxfp8_fwd", "vdn_softmax_branches_mxfp8_fwd",
     "vdn_hybrid_attn_train_saved_size", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
+    "vdn_vda_branch",
 )
 
 
@@ -137,6 +138,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_proj_mxfp8_workspace_size.restype = sz
         L.vdn_hybrid_attn_proj_mxfp8_fwd.argtypes = [vp] * 10 + [ctypes.c_int32, lp, vp, vp, sz, vp]
         L.vdn_hybrid_attn_proj_mxfp8_fwd.restype = ctypes.c_int
+        L.vdn_vda_branch.argtypes = [vp] * 6 + [lp, vp, vp, sz, vp]
+        L.vdn_vda_branch.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -213,6 +216,22 @@ def _layout_from(q, text_k, frames, tokens_per_frame, **kw) -> Layout:
                        tokens_per_frame=tokens_per_frame, text_tokens=L, dtype=q.dtype, **kw)
 
 
+def _workspace(ws, need: int, device, name="workspace"):
+    """A caller-provided scratch buffer: a contiguous device uint8 tensor of at
+    least `need` bytes (allocated when None)."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8:
+        raise ValueError(f"{name}: expected torch.uint8 (view other buffers as bytes)")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ws.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if ws.numel() < need:
+        raise ValueError(f"{name}: {ws.numel()} bytes, {need} needed")
+    return ws
+
+
 def _check_inputs(lay: Layout, q, k, v, text_k, text_v):
     B, H, d = lay.batch, lay.heads, lay.head_dim_k
     N = lay.frames * lay.tokens_per_frame
@@ -244,8 +263,7 @@ def hybrid_attn(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, frames,
         out = torch.empty_like(q)
     _expect(out, q.shape, q.dtype, "out")
     need = workspace_size(lay)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     st = lib().vdn_hybrid_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
@@ -268,9 +286,9 @@ def softmax_fwd(q, k, v, text_k, text_v, *, frames, tokens_per_frame, chunk_fram
     _expect(out, q.shape, q.dtype, "out")
     L = lay.text_tokens
     need = softmax_workspace_size(lay)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None or need:
+        workspace = _workspace(workspace, need, q.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().vdn_softmax_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
                                  _ptr(text_v if L else None), ctypes.byref(lay), _ptr(out),
                                  _ptr(workspace), nbytes, _stream()), "vdn_softmax_fwd")
@@ -294,9 +312,9 @@ def softmax_merge_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tokens
     _expect(out, q.shape, q.dtype, "out")
     L = lay.text_tokens
     need = softmax_workspace_size(lay)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None or need:
+        workspace = _workspace(workspace, need, q.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().vdn_softmax_merge_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
                                        _ptr(text_v if L else None), _ptr(R), _ptr(gate_logits),
                                        ctypes.byref(lay), _ptr(out), _ptr(workspace), nbytes,
@@ -322,9 +340,9 @@ def softmax_branches_fwd(q, k, v, text_k, text_v, R, gate_logits, *, frames, tok
     _expect(out, (B, N, 2, H, d), q.dtype, "out")
     L = lay.text_tokens
     need = softmax_workspace_size(lay)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None or need:
+        workspace = _workspace(workspace, need, q.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().vdn_softmax_branches_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None),
                                           _ptr(text_v if L else None), _ptr(R),
                                           _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
@@ -352,9 +370,9 @@ def softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, *, frames, t
     scales = torch.empty((B * N, K // 32), dtype=torch.uint8, device=q.device)
     L = lay.text_tokens
     need = softmax_workspace_size(lay)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None or need:
+        workspace = _workspace(workspace, need, q.device)
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().vdn_softmax_branches_mxfp8_fwd(_ptr(q), _ptr(k), _ptr(v),
                                                 _ptr(text_k if L else None),
                                                 _ptr(text_v if L else None), _ptr(R),
@@ -412,8 +430,7 @@ def hybrid_attn_proj(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_o, *, 
         out = torch.empty((B, N, dm), dtype=q.dtype, device=q.device)
     _expect(out, (B, N, dm), q.dtype, "out")
     need = proj_workspace_size(lay)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     st = lib().vdn_hybrid_attn_proj_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(w_o), dm, ctypes.byref(lay), _ptr(out),
@@ -445,7 +462,8 @@ def out_proj_mxfp8(xq, xs, wq, ws, out=None) -> torch.Tensor:
     N = wq.shape[0]
     for name, t in (("xq", xq), ("xs", xs), ("wq", wq), ("ws", ws)):
         _expect(t, t.shape, torch.uint8, name)
-    if wq.shape != (N, K) or ws.shape != (N, K // 32) or xs.shape[-1] != K // 32:
+    if (tuple(wq.shape) != (N, K) or tuple(ws.shape) != (N, K // 32)
+            or tuple(xs.shape) != tuple(xq.shape[:-1]) + (K // 32,)):
         raise ValueError("mxfp8 operand shapes do not match")
     M = xq.numel() // K
     if out is None:
@@ -481,9 +499,9 @@ def hybrid_attn_proj_mxfp8(q, k, v, text_k, text_v, beta, alpha, gate_logits, w_
     if out is None:
         out = torch.empty((B, N, dm), dtype=torch.bfloat16, device=q.device)
     _expect(out, (B, N, dm), torch.bfloat16, "out")
-    if workspace is None:
-        workspace = torch.empty(lib().vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay)),
-                                dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace,
+                           lib().vdn_hybrid_attn_proj_mxfp8_workspace_size(ctypes.byref(lay)),
+                           q.device)
     st = lib().vdn_hybrid_attn_proj_mxfp8_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(w_q), _ptr(w_scales), dm,
@@ -523,8 +541,7 @@ def hybrid_attn_bwd(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO, *, fr
          "beta": torch.empty((B, N + L, H), **f32), "alpha": torch.empty((B, frames, H), **f32),
          "gate_logits": torch.empty((B, N, H, 2), **f32)}
     need = bwd_workspace_size(lay)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     st = lib().vdn_hybrid_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(dO), ctypes.byref(lay), _ptr(g["q"]),
@@ -559,8 +576,7 @@ def hybrid_attn_fwd_train(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, 
     if out is None:
         out = torch.empty_like(q)
     _expect(out, q.shape, q.dtype, "out")
-    if saved is None:
-        saved = torch.empty(train_saved_size(lay), dtype=torch.uint8, device=q.device)
+    saved = _workspace(saved, train_saved_size(lay), q.device, "saved")
     st = lib().vdn_hybrid_attn_fwd_train(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out), _ptr(saved),
@@ -594,6 +610,9 @@ def hybrid_attn_bwd_saved(q, k, v, text_k, text_v, beta, alpha, gate_logits, dO,
          "text_v": torch.empty((B, L, H, d), **f32) if L else None,
          "beta": torch.empty((B, N + L, H), **f32), "alpha": torch.empty((B, frames, H), **f32),
          "gate_logits": torch.empty((B, N, H, 2), **f32)}
+    if saved is None:
+        raise ValueError("saved: the buffer hybrid_attn_fwd_train filled is required")
+    saved = _workspace(saved, train_saved_size(lay), q.device, "saved")
     st = lib().vdn_hybrid_attn_bwd_saved(
         _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), _ptr(dO), ctypes.byref(lay), _ptr(g["q"]),
@@ -644,6 +663,32 @@ def vda_factor_scan(A, Bm, alpha, *, dtype, text_tokens, frames, tokens_per_fram
     _check(lib().vdn_vda_factor_scan(_ptr(A), _ptr(Bm), _ptr(alpha), ctypes.byref(lay), _ptr(R),
                                      _ptr(ws), ws.numel(), _stream()), "vdn_vda_factor_scan")
     return R
+
+
+def vda_branch(k, v, text_k, text_v, beta, alpha, *, frames, tokens_per_frame, chunk_frames=5,
+               window_chunks=1, anchor_first=True, anchor_last=True, out=None,
+               workspace=None) -> torch.Tensor:
+    """The layer's VDA branch up to the summed states (``vdn_vda_branch``):
+    returns R, float32 [B, H, nc+1, d, d] (slot nc = text write)."""
+    lay = _layout_from(k, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, k, k, v, text_k, text_v)
+    B, N, H, d = k.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    nc = num_chunks(lay)
+    if out is None:
+        out = torch.empty((B, H, nc + 1, d, d), dtype=torch.float32, device=k.device)
+    _expect(out, (B, H, nc + 1, d, d), torch.float32, "out")
+    workspace = _workspace(workspace, workspace_size(lay), k.device)
+    _check(lib().vdn_vda_branch(_ptr(k), _ptr(v), _ptr(text_k if L else None),
+                                _ptr(text_v if L else None), _ptr(beta), _ptr(alpha),
+                                ctypes.byref(lay), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream()), "vdn_vda_branch")
+    return out
 
 
 def merge(q, o_soft, R, gate_logits, *, frames, tokens_per_frame, chunk_frames=5,

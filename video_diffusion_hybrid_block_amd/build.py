@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdn.so")
 ARCH = os.environ.get("VDN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "k_softmax.hip", "k_gram.hip", "k_factor.hip", "k_scan.hip", "k_merge.hip",
+SOURCES = ["api.hip", "k_softmax.hip", "k_gram.hip", "k_factor.hip", "k_vda_stats.hip",
+           "k_scan.hip", "k_merge.hip",
            "k_proj.hip", "k_attn_bwd.hip", "k_vda_bwd.hip"]
 
 COMMON = [

@@ -56,6 +56,36 @@ bool text_aligned(const void* tk, const void* tv) {
   return (!tk || aligned16(tk)) && (!tv || aligned16(tv));
 }
 
+// The VDA branch of the layer's forward, up to R (the summed states each
+// chunk reads, slot nc the text write) in the plan's buffers.  bf16 layouts
+// with d >= 32 take the fused path: statistics and factor in one pass (which
+// also writes the softmax's V^T copy when the softmax reads one; *vt_done
+// tells), then the scan from the pre-split G planes.  Other layouts take the
+// separate gram, factor and scan kernels.
+hipError_t vda_forward(const void* k, const void* v, const void* text_k, const void* text_v,
+                       const float* beta, const float* alpha, const vdn_layout_t& l, char* ws,
+                       hipStream_t stream, bool* vt_done, float* R_out = nullptr) {
+  const Plan p = make_plan(l);
+  float* A = (float*)(ws + p.a_off);
+  float* B = (float*)(ws + p.b_off);
+  float* Sf = (float*)(ws + p.sf_off);
+  float* Sb = (float*)(ws + p.sb_off);
+  float* R = R_out ? R_out : (float*)(ws + p.r_off);
+  *vt_done = false;
+  if (l.dtype == VDN_BF16 && l.head_dim_k >= 32) {
+    const bool vt = softmax_uses_vt(l);
+    hipError_t e = launch_vda_stats(k, v, text_k, text_v, beta, l, A, B, vt ? ws + p.vt_off : nullptr,
+                                    stream);
+    if (e == hipSuccess) e = launch_scan_split(A, B, alpha, l, Sf, Sb, R, stream);
+    *vt_done = vt && e == hipSuccess;
+    return e;
+  }
+  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
+  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -254,6 +284,24 @@ vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R, const 
   return hip_status(launch_merge(q, o_soft, R, gate_logits, *layout, eff_eps(*layout), o, stream));
 }
 
+vdn_status_t vdn_vda_branch(const void* k, const void* v, const void* text_k, const void* text_v,
+                            const float* beta, const float* alpha, const vdn_layout_t* layout,
+                            float* R_out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!k || !v || !beta || !alpha || !R_out || !workspace || !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(R_out) || !aligned16(workspace) || !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  const Plan p = make_plan(*layout);
+  if (workspace_bytes < p.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  bool vt_done = false;
+  return hip_status(
+      vda_forward(k, v, text_k, text_v, beta, alpha, *layout, (char*)workspace, stream, &vt_done, R_out));
+}
+
 vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_k,
                                  const void* text_v, const float* beta, const float* alpha,
                                  const float* gate_logits, const vdn_layout_t* layout, void* o,
@@ -270,19 +318,14 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
   const Plan p = make_plan(*layout);
   if (workspace_bytes < p.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
   char* ws = (char*)workspace;
-  float* A = (float*)(ws + p.a_off);
-  float* B = (float*)(ws + p.b_off);
-  float* Sf = (float*)(ws + p.sf_off);
-  float* Sb = (float*)(ws + p.sb_off);
   float* R = (float*)(ws + p.r_off);
   const vdn_layout_t& l = *layout;
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
-  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  bool vt_done = false;
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
   if (e != hipSuccess) return hip_status(e);
   if (softmax_merge_fusable(l))
     return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                           eff_eps(l), false, o, ws + p.vt_off, stream));
+                                           eff_eps(l), false, o, ws + p.vt_off, stream, vt_done));
   e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
   if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
   return hip_status(e);
@@ -592,19 +635,14 @@ vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const 
     return VDN_ERR_WORKSPACE_TOO_SMALL;
   const Plan p = make_plan(l);
   char* ws = (char*)workspace;
-  float* A = (float*)(ws + p.a_off);
-  float* B = (float*)(ws + p.b_off);
-  float* Sf = (float*)(ws + p.sf_off);
-  float* Sb = (float*)(ws + p.sb_off);
   float* R = (float*)(ws + p.r_off);
   char* xq = ws + fp8_codes_off(l);
   char* xs = ws + fp8_scales_off(l);
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
-  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  bool vt_done = false;
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
   if (e == hipSuccess)
     e = launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                      eff_eps(l), xq, xs, ws + p.vt_off, stream);
+                                      eff_eps(l), xq, xs, ws + p.vt_off, stream, vt_done);
   if (e == hipSuccess) e = launch_proj_mxfp8(xq, xs, w_q, w_scales, M, K, d_model, y, stream);
   return hip_status(e);
 }
@@ -637,18 +675,13 @@ vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* 
   if (workspace_bytes < proj_ws_total(l)) return VDN_ERR_WORKSPACE_TOO_SMALL;
   const Plan p = make_plan(l);
   char* ws = (char*)workspace;
-  float* A = (float*)(ws + p.a_off);
-  float* B = (float*)(ws + p.b_off);
-  float* Sf = (float*)(ws + p.sf_off);
-  float* Sb = (float*)(ws + p.sb_off);
   float* R = (float*)(ws + p.r_off);
   void* x2 = ws + proj_x2_off(l);
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
-  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  bool vt_done = false;
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
   if (e == hipSuccess)
     e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
-                             true, x2, ws + p.vt_off, stream);
+                             true, x2, ws + p.vt_off, stream, vt_done);
   if (e == hipSuccess) e = launch_proj(x2, w_o, M, 2 * l.heads * l.head_dim_k, d_model, y, stream);
   return hip_status(e);
 }

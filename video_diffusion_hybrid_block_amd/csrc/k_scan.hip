@@ -240,6 +240,232 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   }
 }
 
+// The same scan for the layer's forward path, with G_f supplied as two bf16
+// planes (hi, lo; hi + lo = G_f to 2^-16) by the fused statistics pass: the
+// planes go straight from LDS into the MFMA B operand, so a step converts
+// only X = a S + B (one 32 x d block per workgroup), not G.  The state, the
+// snapshots, the step order and the three-pass products are those of
+// scan_mfma_kernel.  The 64 KB copy of the next step's planes runs at the
+// CU's L2 -> LDS rate (about a microsecond at d = 128) and stalls the wave
+// that issues it, so a workgroup pairs each of its d/32 compute waves with a
+// copy wave on the same SIMD: the copy waves issue half of the next step's
+// copies while the compute waves build X and the other half during the
+// products.
+template <int D>
+__global__ void __launch_bounds__(4 * D)
+scan_split_kernel(const bf16* __restrict__ Gp, const float* __restrict__ Bm,
+                  const float* __restrict__ alpha, float* __restrict__ Sf,
+                  float* __restrict__ Sb, Geo g, int H) {
+  constexpr int NRB = D / 32;           // row blocks per chain = compute waves per workgroup
+  constexpr int NT = 64 * NRB;          // compute threads; waves NRB .. 2 NRB - 1 copy
+  constexpr int LDF = D;                // fp32 state row stride (floats)
+  constexpr int NCH = 32 * D / 8 / NT;  // 8-value chunks of X per thread per step
+  constexpr int CPR = D / 8;            // 16-byte chunks per bf16 plane row
+  constexpr int PBYTES = D * D * 2;     // one plane
+  constexpr int GBYTES = 2 * PBYTES;    // hi + lo
+  constexpr int PBLK = PBYTES / 1024;   // 1 KB DMA blocks per plane
+  constexpr int NGI = 2 * PBLK / NRB;   // DMA blocks per copy wave per G
+  constexpr int KH = D / 32;            // k steps whose fragments are read ahead at once
+  static_assert(NCH >= 1 && NCH * 8 * NT == 32 * D, "X build split");
+  static_assert(NGI * NRB == 2 * PBLK && NGI % 2 == 0, "G copy split");
+  // One LDS allocation: two G buffers (planes with XOR-swizzled 16-byte
+  // chunks, conflict-free B-operand reads), the state rows S (fp32) and
+  // X = aS + B as bf16 hi / lo.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * GBYTES + 32 * LDF * 4 + 2 * 32 * D * 2];
+  char VDN_LDS* Gl = (char VDN_LDS*)smem;
+  float VDN_LDS* S = (float VDN_LDS*)(smem + 2 * GBYTES);
+  char VDN_LDS* Xh = (char VDN_LDS*)(smem + 2 * GBYTES + 32 * LDF * 4);
+  char VDN_LDS* Xl = Xh + 32 * D * 2;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const bool copier = wv >= NRB;
+  const int cw = wv - NRB;              // copy wave index
+  // Workgroup i runs on XCD i % 8; with an even split each XCD gets whole
+  // chains, so the row blocks of a chain share one L2.
+  int wid = blockIdx.x;
+  if (gridDim.x % (8 * NRB) == 0) wid = (wid & 7) * (gridDim.x >> 3) + (wid >> 3);
+  const int rb = wid % NRB;
+  const int chain = wid / NRB;
+  const int dir = chain & 1;
+  const int bh = chain >> 1;
+  const int b = bh / H, h = bh % H;
+  const int row0 = rb * 32;
+  const size_t mat = (size_t)D * D;
+  const bf16* Gbh = Gp + (size_t)bh * (g.T + 1) * 2 * mat;
+  const float* Bbh = Bm + (size_t)bh * (g.T + 1) * mat;
+  float* snap = (dir == 0 ? Sf : Sb) + (size_t)bh * (g.nc + 1) * mat;
+  const float* al = alpha + (size_t)b * g.T * H + h;
+
+  // Copies i0 .. i0 + n - 1 of copy wave cw for the planes of `slot` into
+  // LDS buffer bi: block blk = cw * NGI + i covers 16-byte slots 64 * (blk %
+  // PBLK) .. +63 of plane blk / PBLK; slot j holds row j / CPR, logical chunk
+  // (j % CPR) ^ swz(row).
+  auto copy_part = [&](int slot, int bi, int i0, int n) {
+    const bf16* Gs = Gbh + (size_t)slot * 2 * mat;
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i) {
+      const int blk = cw * NGI + i;
+      const int pl = blk / PBLK;
+      const int j = (blk % PBLK) * 64 + lane;
+      const int row = j / CPR;
+      const int ch = (j % CPR) ^ swz<D>(row);
+      g2lds16(Gs + pl * mat + (size_t)row * D + ch * 8, Gl + bi * GBYTES + blk * 1024);
+    }
+  };
+  float4 bcur[2 * NCH], bnxt[2 * NCH];
+  auto load_b = [&](int slot, float4* br) {
+    const float* Bs = Bbh + (size_t)slot * mat + (size_t)row0 * D;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + i * NT;
+      const float4* bp = (const float4*)(Bs + (q / (D / 8)) * D + (q % (D / 8)) * 8);
+      br[2 * i] = bp[0];
+      br[2 * i + 1] = bp[1];
+    }
+  };
+  // X = a S + B as bf16 hi / lo (compute waves)
+  auto build_x = [&](float a) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + i * NT;
+      const int r = q / (D / 8), c = (q % (D / 8)) * 8;
+      const f32x4 s0 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c);
+      const f32x4 s1 = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + c + 4);
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float4 b0 = bcur[2 * i], b1 = bcur[2 * i + 1];
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hi, lo;
+        split_bf16(fmaf(a, sv[e], bv[e]), hi, lo);
+        hv[e] = hi;
+        lv[e] = lo;
+      }
+      const int off = swz_off<D>(r, c);
+      *(bf16x8 VDN_LDS*)(Xh + off) = hv;
+      *(bf16x8 VDN_LDS*)(Xl + off) = lv;
+    }
+  };
+  // S <- X G, times `post`, G from LDS buffer bi (symmetric: its B-operand
+  // columns are plane rows); compute waves.  Fragments are read KH k steps
+  // at a time ahead of their products.
+  auto product = [&](float post, int bi) {
+    const int n = wv * 32 + (lane & 31);
+    const char VDN_LDS* gh = Gl + bi * GBYTES;
+    const char VDN_LDS* gl = gh + PBYTES;
+    f32x16 acc = f32x16{}, acc1 = f32x16{}, acc2 = f32x16{};
+#pragma unroll
+    for (int k0 = 0; k0 < D / 16; k0 += KH) {
+      bf16x8 fbh[KH], fbl[KH], fah[KH], fal[KH];
+#pragma unroll
+      for (int u = 0; u < KH; ++u) {
+        fah[u] = lds_row8<D>(Xh, lane & 31, (k0 + u) * 2 + half);
+        fbh[u] = lds_row8<D>(gh, n, (k0 + u) * 2 + half);
+        fbl[u] = lds_row8<D>(gl, n, (k0 + u) * 2 + half);
+        fal[u] = lds_row8<D>(Xl, lane & 31, (k0 + u) * 2 + half);
+      }
+#pragma unroll
+      for (int u = 0; u < KH; ++u) {
+        acc = mfma32(fah[u], fbh[u], acc);
+        acc1 = mfma32(fah[u], fbl[u], acc1);
+        acc2 = mfma32(fal[u], fbh[u], acc2);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = (j >> 2) * 8 + half * 4 + (j & 3);
+      S[r * LDF + wv * 32 + (lane & 31)] = (acc[j] + (acc1[j] + acc2[j])) * post;
+    }
+  };
+  auto snapshot = [&](int c) {
+    if (copier) return;
+    float* dst = snap + (size_t)c * mat + (size_t)row0 * D;
+    for (int i = tid; i < 32 * D / 4; i += NT) {
+      const int r = (4 * i) / D, cc = (4 * i) % D;
+      *(f32x4*)(dst + 4 * i) = *(const f32x4 VDN_LDS*)((const float VDN_LDS*)S + r * LDF + cc);
+    }
+  };
+
+  // frames the chain folds: (fend: forward bound, fbeg: backward bound)
+  const int fend = sgpr(fwd_scan_end(g)), fbeg = sgpr(bwd_scan_begin(g));
+  auto next = [&](int f) {
+    if (dir == 0) {
+      int m = f + 1;
+      while (m < fend && is_anchor(g, m)) ++m;
+      return m < fend ? m : -1;
+    }
+    int m = f < 0 ? g.T - 1 : f - 1;
+    while (m > fbeg && is_anchor(g, m)) --m;
+    return m > fbeg ? m : -1;
+  };
+  // Step sequence: the text write (slot T, a = 0, times 1/2) when there is
+  // text, then the frames the chain folds.  Step k reads G from LDS buffer
+  // k & 1; the copy waves fill the other buffer for step k+1 during step k
+  // and wait for their copies before the next step's first barrier.  Every
+  // wave passes three barriers per step.
+  bool text = g.L > 0;
+  int slot = text ? g.T : next(-1);
+  // decay of the current and the next step, loaded with the step's B
+  float acur = 0.f, anxt = 0.f;
+  if (copier) {
+    if (slot >= 0) copy_part(slot, 0, 0, NGI);
+  } else {
+    if (slot >= 0) {
+      load_b(slot, bcur);
+      acur = text ? 0.f : al[(size_t)slot * H];
+    }
+    for (int i = tid; i < 32 * LDF; i += NT) S[i] = 0.f;
+  }
+  wait_vmem();
+  __syncthreads();
+  if (!text) snapshot(g.nc);
+  int c = dir == 0 ? 0 : g.nc - 1;
+  int bi = 0;
+  while (slot >= 0) {
+    const int nslot = next(text ? -1 : slot);
+    if (!text) {
+      // chunks whose state is the one before frame `slot` (anchors in
+      // between do not change the state)
+      if (dir == 0) {
+        while (c < g.nc && win_lo(g, c) <= slot) snapshot(c++);
+      } else {
+        while (c >= 0 && win_hi(g, c) >= slot) snapshot(c--);
+      }
+    }
+    lds_barrier();                        // G of this step landed; step k-1 done with buffer bi ^ 1
+    if (copier) {
+      if (nslot >= 0) copy_part(nslot, bi ^ 1, 0, NGI / 2);
+      lds_barrier();
+      if (nslot >= 0) copy_part(nslot, bi ^ 1, NGI / 2, NGI / 2);
+      lds_barrier();
+      wait_vmem();                        // this wave's copies for the next step
+    } else {
+      if (nslot >= 0) {
+        load_b(nslot, bnxt);
+        anxt = al[(size_t)nslot * H];
+      }
+      build_x(acur);
+      lds_barrier();
+      product(text ? 0.5f : 1.0f, bi);
+      lds_barrier();
+    }
+    if (text) snapshot(g.nc);
+#pragma unroll
+    for (int i = 0; i < 2 * NCH; ++i) bcur[i] = bnxt[i];
+    acur = anxt;
+    bi ^= 1;
+    text = false;
+    slot = nslot;
+  }
+  if (dir == 0) {
+    while (c < g.nc) snapshot(c++);
+  } else {
+    while (c >= 0) snapshot(c--);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Backward pass of the scan.  A chain folds frames f_1, f_2, ..., f_n (fold
 // order) from S_0: S_j = (alpha_j S_{j-1} + B_j) G_j.  With dS_j the gradient
@@ -526,6 +752,37 @@ hipError_t launch_scan(const float* G, const float* B, const float* alpha, const
     case 16: return launch_d<16>(G, B, alpha, l, Sf, Sb, R, states, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan_split(const void* Gp, const float* B, const float* alpha,
+                             const vdn_layout_t& l, float* Sf, float* Sb, float* R, hipStream_t s) {
+  if (l.dtype != VDN_BF16) return hipErrorNotSupported;
+  const Geo g = make_geo(l);
+  const long chains = (long)l.batch * l.heads * 2;
+  const int D = l.head_dim_k;
+  switch (D) {
+    case 128:
+      scan_split_kernel<128><<<dim3((unsigned)(chains * 4)), dim3(512), 0, s>>>(
+          (const bf16*)Gp, B, alpha, Sf, Sb, g, l.heads);
+      break;
+    case 64:
+      scan_split_kernel<64><<<dim3((unsigned)(chains * 2)), dim3(256), 0, s>>>(
+          (const bf16*)Gp, B, alpha, Sf, Sb, g, l.heads);
+      break;
+    case 32:
+      scan_split_kernel<32><<<dim3((unsigned)chains), dim3(128), 0, s>>>(
+          (const bf16*)Gp, B, alpha, Sf, Sb, g, l.heads);
+      break;
+    default:
+      return hipErrorNotSupported;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n4 = (size_t)l.batch * l.heads * (g.nc + 1) * D * D / 4;
+  const unsigned blocks = (unsigned)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  combine_kernel<<<dim3(blocks), dim3(256), 0, s>>>((const float4*)Sf, (const float4*)Sb,
+                                                     (float4*)R, n4);
+  return hipGetLastError();
 }
 
 hipError_t launch_scan_bwd(const float* G, const float* dR, const float* alpha,

@@ -887,7 +887,7 @@ template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
                        const float* R, const float* gates, float eps, int mode, hipStream_t s,
-                       const EpilogueIO& bio = EpilogueIO{}) {
+                       const EpilogueIO& bio = EpilogueIO{}, bool vt_ready = false) {
   Geo g = make_geo(l);
   int tpf = (g.P + 127) / 128;
   long grid = (long)l.batch * l.heads * g.T * tpf;
@@ -897,10 +897,12 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
     const int N = g.T * g.P;
     const int nl8 = (N + g.L + 7) / 8 * 8;
     const int ntile = (nl8 + 63) / 64;
-    vt_transpose_kernel<D><<<dim3((unsigned)(l.batch * l.heads * ntile)), dim3(256), 0, s>>>(
-        (const bf16*)v, (const bf16*)tv, (bf16*)ws, N, g.L, l.heads, nl8, ntile);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!vt_ready) {
+      vt_transpose_kernel<D><<<dim3((unsigned)(l.batch * l.heads * ntile)), dim3(256), 0, s>>>(
+          (const bf16*)v, (const bf16*)tv, (bf16*)ws, N, g.L, l.heads, nl8, ntile);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     if (mode == 1)
       softmax_vt_kernel<D, 1><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
@@ -996,14 +998,14 @@ hipError_t launch_softmax_branches_mxfp8(const void* q, const void* k, const voi
                                          const void* tk, const void* tv, const float* R,
                                          const float* gates, const vdn_layout_t& l, float scale,
                                          float eps, void* codes, void* scales, void* ws,
-                                         hipStream_t s) {
+                                         hipStream_t s, bool vt_ready) {
   if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
   EpilogueIO io{};
   io.mx_scales = (uint8_t*)scales;
   switch (l.head_dim_k) {
-    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
-    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
-    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io);
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io, vt_ready);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io, vt_ready);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, codes, ws, R, gates, eps, 4, s, io, vt_ready);
   }
   return hipErrorInvalidValue;
 }
@@ -1029,13 +1031,14 @@ bool softmax_merge_fusable(const vdn_layout_t& l) {
 hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
                                 const void* tv, const float* R, const float* gates,
                                 const vdn_layout_t& l, float scale, float eps, bool split, void* o,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, bool vt_ready) {
   if (!softmax_merge_fusable(l)) return hipErrorNotSupported;
   const int mode = split ? 2 : 1;
+  const EpilogueIO none{};
   switch (l.head_dim_k) {
-    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
-    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
-    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s);
+    case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s, none, vt_ready);
+    case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s, none, vt_ready);
+    case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, mode, s, none, vt_ready);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,308 @@
+// Frame statistics and factor of the VDA branch in one pass, for the layer's
+// forward path: for every frame the scans fold (and the text block)
+//   A = sum_i beta_i k_i k_i^T   (the key Gram of the frame),
+//   B = sum_i beta_i v_i k_i^T   (its write),
+//   G = (I + A)^-1               (the non-expansive transition),
+// with A kept on chip: it goes from the MFMA accumulators through LDS into
+// the inverse and never reaches HBM.  The same pass writes the V^T copy the
+// softmax reads (every frame and the text block), from the V tiles it has in
+// LDS anyway, so V is read from HBM once for both branches.
+// [deepmagic blog "生成比播放還快：Video DeltaNet 用 11 秒產出 14 秒 768p 影片",
+//  section 用兩條分支取代一條 (closed form S = (S̄ + B)(I + A)^-1, non-expansive);
+//  PaperDaily "伯克利与Impossible视频生成" §四 (A holds the key correlation of
+//  the spatial tokens of one frame; the (I + A) inverse couples them)]
+//
+// gfx950 design (bf16, d in {32, 64, 128}): one workgroup of 8 waves per
+// (batch, head, slot); two workgroups per CU, so one streams its tiles while
+// the other inverts.
+//  * Tiles of 64 tokens go global -> LDS with 16-byte direct-to-LDS loads into
+//    an XOR-swizzled [token][d] layout.  beta*k is formed in fp32 and split
+//    into bf16 hi + lo, so A = K^T (bK)_hi + K^T (bK)_lo and B likewise with V
+//    (two bf16 MFMA passes; a single rounding of beta*k moves the small
+//    eigen-directions of I + A on ill-conditioned key sets).
+//  * V^T: ds_read_b64_tr_b16 pairs give each lane 8 consecutive tokens of one
+//    d, stored as 16 bytes into row d of the copy.
+//  * Inverse: I + A is read from A's lower triangle (exactly symmetric) into
+//    a 16 x 32 thread grid, (d/16) x (d/32) values per thread, and inverted
+//    in place by the symmetric sweep (Gauss-Jordan on an SPD matrix, pivots
+//    in order, all positive; sweeping every pivot leaves -(I + A)^-1).  With
+//    w = M[k][.] / sqrt(M[k][k]) the update is m[i][j] -= w_i w_j, bitwise
+//    symmetric; one pivot row broadcast through LDS per step.
+//  * G is stored as two bf16 planes, hi and lo (hi + lo = G to 2^-16), the
+//    operand format of the scan's three-pass products, so the scan converts
+//    nothing per step.
+#include "vdn_device.h"
+#include "vdn_internal.h"
+
+namespace vdn {
+
+namespace {
+
+template <int D>
+__global__ void __launch_bounds__(512, 2)
+vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
+                 const bf16* __restrict__ tk, const bf16* __restrict__ tv,
+                 const float* __restrict__ beta, bf16* __restrict__ Gp, float* __restrict__ Bout,
+                 bf16* __restrict__ vt, int nl8, Geo g, int H, int nitems) {
+  constexpr int BT = 64;                     // tokens per tile
+  constexpr int KCH = D / 8;                 // 16-byte chunks per token row
+  constexpr int TILE = BT * D * 2;
+  constexpr int NW = 8, NT = 64 * NW;
+  constexpr int NI = (BT * KCH + NT - 1) / NT;   // DMA instructions per thread per operand
+  constexpr int NB = D / 32;
+  constexpr int NBLK = 2 * NB * NB;          // 32 x 32 blocks of A and B
+  constexpr int BLK_PER_WAVE = NBLK >= NW ? NBLK / NW : 1;
+  constexpr int ABYTES = D * D * 4;
+  constexpr int SMEM = 4 * TILE > ABYTES ? 4 * TILE : ABYTES;
+  constexpr int NVT = 4 * NB;                // 16-token x 32-d transposed reads per tile
+  constexpr int RB = D / 16, CB = D / 32;    // sweep: rows / columns per thread
+  static_assert(RB == 2 * CB, "sweep grid");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ float bsh[BT];
+  __shared__ __attribute__((aligned(16))) float rowbuf[2][D];
+  char VDN_LDS* lds = (char VDN_LDS*)smem;
+  char VDN_LDS* Kt = lds;
+  char VDN_LDS* Vt = lds + TILE;
+  char VDN_LDS* Ht = lds + 2 * TILE;         // (beta k) hi
+  char VDN_LDS* Lt = lds + 3 * TILE;         // (beta k) lo
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int N = g.T * g.P;
+  const int task = blockIdx.x;
+  const int bh = task / nitems;
+  const int b = bh / H, h = bh % H;
+  const int idx = task % nitems;
+  const int slot = vt ? idx : slot_of(g, idx, false);
+  const bool text = slot == g.T;
+  const bool stats = text || frame_needs_stats(g, slot);
+  const int ntok = text ? g.L : g.P;
+  const bf16* kb = text ? tk : k;
+  const bf16* vb = text ? tv : v;
+  const int tok0 = text ? 0 : slot * g.P;
+  const int rows_total = text ? g.L : N;
+  const float* bptr = beta + (size_t)b * (N + g.L) * H + h + (size_t)(text ? N : slot * g.P) * H;
+  // V^T row d of this head; the slot's tokens start at column vcol0
+  bf16* vtbh = vt ? vt + (size_t)bh * D * nl8 : nullptr;
+  const int vcol0 = text ? N : slot * g.P;
+
+  // 32 x 32 output blocks of this wave: matrix (0: A, rows from K; 1: B,
+  // rows from V), block row bi, block column bj.  At d = 128 a wave owns a
+  // 2 x 2 square of one matrix, so per 16 tokens it reads 2 row-side and 2
+  // column-side (hi, lo) fragments instead of 1 + 4 (transposed LDS reads
+  // bound this loop); otherwise block wv.
+  auto block_of = [&](int i, int& mat, int& bi, int& bj) {
+    if constexpr (NB == 4) {
+      const int q = wv & 3;
+      mat = wv >> 2;
+      bi = 2 * (q >> 1) + (i >> 1);
+      bj = 2 * (q & 1) + (i & 1);
+      return true;
+    } else {
+      const int blk = wv * BLK_PER_WAVE + i;
+      mat = blk / (NB * NB);
+      bi = (blk / NB) % NB;
+      bj = blk % NB;
+      return blk < NBLK;
+    }
+  };
+  f32x16 acc[BLK_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < BLK_PER_WAVE; ++i) acc[i] = f32x16{};
+
+  for (int t0 = 0; t0 < ntok; t0 += BT) {
+    __syncthreads();                          // previous tile fully consumed
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int blk = ii * NW + wv;
+      if (blk * 64 >= BT * KCH) break;
+      const int p = blk * 64 + lane;
+      const int row = p / KCH, pch = p % KCH;
+      const int ch = pch ^ swz<D>(row);
+      const int tok = t0 + row < ntok ? t0 + row : 0;
+      const size_t off = ((size_t)(b * (size_t)rows_total + tok0 + tok) * H + h) * D + ch * 8;
+      if (stats) g2lds16(kb + off, Kt + blk * 1024);
+      g2lds16(vb + off, Vt + blk * 1024);
+    }
+    if (stats && tid < BT) {
+      const int tk_ = t0 + tid;
+      bsh[tid] = tk_ < ntok ? bptr[(size_t)tk_ * H] : 0.f;
+    }
+    wait_vmem();
+    __syncthreads();
+    if (vtbh) {
+      // lane l gets V[t0 + r0 + 8 (l / 32) + e][c0 + l % 32], e = 0..7: 16
+      // bytes of V^T row c0 + l % 32
+#pragma unroll
+      for (int u = 0; u < (NVT + NW - 1) / NW; ++u) {
+        const int call = u * NW + wv;
+        if (call >= NVT) break;
+        const int r0 = (call / NB) * 16, c0 = (call % NB) * 32;
+        const bf16x8 val = lds_col8<D>(Vt, r0, c0, lane);
+        const int t = t0 + r0 + 8 * (lane >> 5);
+        if (t < ntok)
+          *(bf16x8*)(vtbh + (size_t)(c0 + (lane & 31)) * nl8 + vcol0 + t) = val;
+      }
+    }
+    if (!stats) continue;
+    // beta*k -> bf16 hi / lo, same swizzled layout as K
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      if ((ii * NW + wv) * 64 >= BT * KCH) break;
+      const int p = (ii * NW + wv) * 64 + lane;
+      const float bt = bsh[p / KCH];
+      const bf16x8 kv = *(const bf16x8 VDN_LDS*)(Kt + p * 16);
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 a, c;
+        split_bf16((float)kv[e] * bt, a, c);
+        hi[e] = a;
+        lo[e] = c;
+      }
+      *(bf16x8 VDN_LDS*)(Ht + p * 16) = hi;
+      *(bf16x8 VDN_LDS*)(Lt + p * 16) = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BT / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < BLK_PER_WAVE; ++i) {
+        int mat, bi, bj;
+        if (!block_of(i, mat, bi, bj)) continue;
+        const bf16x8 a = lds_col8<D>(mat == 0 ? Kt : Vt, ks * 16, bi * 32, lane);
+        const bf16x8 bh_ = lds_col8<D>(Ht, ks * 16, bj * 32, lane);
+        const bf16x8 bl_ = lds_col8<D>(Lt, ks * 16, bj * 32, lane);
+        acc[i] = mfma32(a, bh_, acc[i]);
+        acc[i] = mfma32(a, bl_, acc[i]);
+      }
+    }
+  }
+  if (!stats) return;
+
+  // B to HBM; A into LDS (fp32, row-major) for the inverse
+  __syncthreads();                            // every wave is done with the tiles
+  float VDN_LDS* Al = (float VDN_LDS*)smem;
+  const size_t mat_off = ((size_t)bh * (g.T + 1) + slot) * D * D;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < BLK_PER_WAVE; ++i) {
+    int mat, bi, bj;
+    if (!block_of(i, mat, bi, bj)) continue;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = bi * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
+      const int c = bj * 32 + (lane & 31);
+      if (mat == 0) Al[r * D + c] = acc[i][j];
+      else Bout[mat_off + (size_t)r * D + c] = acc[i][j];
+    }
+  }
+  __syncthreads();
+
+  const int ti = tid & 15, tc = tid >> 4;     // 16 x 32 thread grid
+  const int r0 = ti * RB, c0 = tc * CB;
+  float m[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int r = r0 + i, c = c0 + j;
+      m[i][j] = Al[(r >= c ? r : c) * D + (r >= c ? c : r)] + (r == c ? 1.0f : 0.0f);
+    }
+  if (ti == 0) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) rowbuf[0][c0 + j] = m[0][j];
+  }
+  __syncthreads();
+  for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+    for (int km = 0; km < RB; ++km) {
+      const int kk = kb * RB + km;
+      const float* rk = rowbuf[kk & 1];
+      // pivots are diagonals of Schur complements of I + A: all >= 1
+      const float sk = __builtin_amdgcn_rsqf(rk[kk]);
+      float wi[RB], wc[CB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) wi[i] = rk[r0 + i] * sk;
+#pragma unroll
+      for (int j = 0; j < CB; ++j) wc[j] = rk[c0 + j] * sk;
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) m[i][j] = fmaf(-wi[i], wc[j], m[i][j]);
+      if (ti == kb) {                         // row kk: M[kk][.] / M[kk][kk]
+#pragma unroll
+        for (int j = 0; j < CB; ++j) m[km][j] = wc[j] * sk;
+      }
+      if (tc == kb * 2 + km / CB) {           // column kk (local column km % CB)
+#pragma unroll
+        for (int i = 0; i < RB; ++i) m[i][km % CB] = wi[i] * sk;
+        if (ti == kb) m[km][km % CB] = -sk * sk;
+      }
+      // the owners of row kk + 1 publish it for the next pivot
+      if (km + 1 < RB) {
+        if (ti == kb) {
+#pragma unroll
+          for (int j = 0; j < CB; ++j) rowbuf[(kk + 1) & 1][c0 + j] = m[(km + 1) % RB][j];
+        }
+      } else if (kb + 1 < 16) {
+        if (ti == kb + 1) {
+#pragma unroll
+          for (int j = 0; j < CB; ++j) rowbuf[(kk + 1) & 1][c0 + j] = m[0][j];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // G = (I + A)^-1 = -M, as bf16 hi and lo planes
+  bf16* gh = Gp + 2 * mat_off;
+  bf16* gl = gh + (size_t)D * D;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    bf16 hv[CB], lv[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) split_bf16(-m[i][j], hv[j], lv[j]);
+    const size_t o = (size_t)(r0 + i) * D + c0;
+    if constexpr (CB == 4) {
+      *(bf16x4*)(gh + o) = bf16x4{hv[0], hv[1], hv[2], hv[3]};
+      *(bf16x4*)(gl + o) = bf16x4{lv[0], lv[1], lv[2], lv[3]};
+    } else if constexpr (CB == 2) {
+      *(bf16x2*)(gh + o) = bf16x2{hv[0], hv[1]};
+      *(bf16x2*)(gl + o) = bf16x2{lv[0], lv[1]};
+    } else {
+      gh[o] = hv[0];
+      gl[o] = lv[0];
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const void* k, const void* v, const void* tk, const void* tv,
+                    const float* beta, const vdn_layout_t& l, void* Gp, float* B, void* vt,
+                    hipStream_t s) {
+  const Geo g = make_geo(l);
+  const int nitems = vt ? g.T + 1 : count_slots(g, false);
+  const long grid = (long)l.batch * l.heads * nitems;
+  const int nl8 = (g.T * g.P + g.L + 7) / 8 * 8;
+  vda_stats_kernel<D><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
+      (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv, beta, (bf16*)Gp, B,
+      (bf16*)vt, nl8, g, l.heads, nitems);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vda_stats(const void* k, const void* v, const void* tk, const void* tv,
+                            const float* beta, const vdn_layout_t& l, void* Gp, float* B,
+                            void* vt, hipStream_t s) {
+  if (l.dtype != VDN_BF16) return hipErrorNotSupported;
+  if (vt && !softmax_uses_vt(l)) return hipErrorInvalidValue;
+  switch (l.head_dim_k) {
+    case 128: return launch_d<128>(k, v, tk, tv, beta, l, Gp, B, vt, s);
+    case 64: return launch_d<64>(k, v, tk, tv, beta, l, Gp, B, vt, s);
+    case 32: return launch_d<32>(k, v, tk, tv, beta, l, Gp, B, vt, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace vdn

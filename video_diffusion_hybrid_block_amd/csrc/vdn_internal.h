@@ -212,6 +212,17 @@ hipError_t launch_gram(const void* k, const void* v, const void* tk, const void*
                        const float* beta, const vdn_layout_t& l, bool all_frames, float* A,
                        float* B, hipStream_t s);
 hipError_t launch_factor(float* A, const vdn_layout_t& l, bool all_frames, hipStream_t s);
+// Layer forward path (bf16, d >= 32): statistics and factor in one pass.
+// Gp [B*H][T+1][2][d][d] bf16 receives G = (I + A)^-1 of every slot the scans
+// fold (and the text block) as hi and lo planes, B [B*H][T+1][d][d] fp32 the
+// writes; with vt non-null (only when softmax_uses_vt) the same pass writes
+// the softmax's V^T copy [B][H][d][nl8] (every frame, then the text).
+hipError_t launch_vda_stats(const void* k, const void* v, const void* tk, const void* tv,
+                            const float* beta, const vdn_layout_t& l, void* Gp, float* B,
+                            void* vt, hipStream_t s);
+// The bidirectional scan and R = S_f + S_b from those planes (bf16, d >= 32).
+hipError_t launch_scan_split(const void* Gp, const float* B, const float* alpha,
+                             const vdn_layout_t& l, float* Sf, float* Sb, float* R, hipStream_t s);
 // states (backward pass, bf16 MFMA path only; may be null): every chain's
 // state after each of its steps, [B*H][2][T+1][d][d] fp32, step 0 = start.
 hipError_t launch_scan(const float* G, const float* B, const float* alpha, const vdn_layout_t& l,
@@ -227,10 +238,11 @@ hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const
 // o = sigmoid(g0) softmax + sigmoid(g1) RMSNorm(R q), or with `split` the two
 // gated branches side by side, o [B][N][2][H][d] (softmax branch first).
 bool softmax_merge_fusable(const vdn_layout_t& l);
+// vt_ready: ws already holds the V^T copy (written by launch_vda_stats).
 hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
                                 const void* tv, const float* R, const float* gates,
                                 const vdn_layout_t& l, float scale, float eps, bool split, void* o,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, bool vt_ready = false);
 // Extra operands of the softmax kernel's epilogue.
 // Merge backward (backward pass): for every video token-head, dgates
 // [B,N,H,2] fp32, dos = sigmoid(l0) dO [B,N,H,d] bf16, dlin = gradient of the
@@ -275,7 +287,7 @@ hipError_t launch_softmax_branches_mxfp8(const void* q, const void* k, const voi
                                          const void* tk, const void* tv, const float* R,
                                          const float* gates, const vdn_layout_t& l, float scale,
                                          float eps, void* codes, void* scales, void* ws,
-                                         hipStream_t s);
+                                         hipStream_t s, bool vt_ready = false);
 hipError_t launch_softmax_merge_bwd(const void* q, const void* k, const void* v, const void* tk,
                                     const void* tv, const float* R, const float* gates,
                                     const vdn_layout_t& l, float scale, float eps,

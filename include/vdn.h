@@ -59,7 +59,9 @@ typedef enum {
   VDN_ERR_UNSUPPORTED = 3,         /* dtype / head size not implemented */
   VDN_ERR_MISALIGNED = 4,          /* a device pointer is not 16-byte aligned */
   VDN_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the required size */
-  VDN_ERR_HIP = 6                  /* a HIP launch failed; see vdn_last_hip_error */
+  VDN_ERR_HIP = 6,                 /* a HIP launch failed; see vdn_last_hip_error */
+  VDN_ERR_SCRATCH_TOO_SMALL = 7    /* the layout needs more than the built-in scratch of
+                                      vdn_hybrid_attn_fwd_noalloc */
 } vdn_status_t;
 
 typedef enum { VDN_F32 = 0, VDN_BF16 = 1 } vdn_dtype_t;
@@ -122,6 +124,30 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                  const vdn_layout_t* layout, void* o,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* Size of the device scratch array vdn_hybrid_attn_fwd_noalloc uses in place
+ * of a workspace (64 MiB; each GPU the library runs on holds one copy until
+ * the process ends). */
+#define VDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* vdn_hybrid_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and output, with the workspace taken from a
+ * static device array of VDN_NOALLOC_SCRATCH_BYTES instead of a caller's
+ * buffer.  The call allocates nothing (no hipMalloc, no library allocation);
+ * its first call on a device looks the array up there.  Layouts whose
+ * workspace (vdn_hybrid_attn_workspace_size) exceeds the array are rejected
+ * with VDN_ERR_SCRATCH_TOO_SMALL before anything is enqueued.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Nothing in the array needs to start at zero (every region is written
+ * before it is read). */
+vdn_status_t vdn_hybrid_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                         const void* text_k, const void* text_v,
+                                         const float* beta, const float* alpha,
+                                         const float* gate_logits,
+                                         const vdn_layout_t* layout, void* o,
+                                         hipStream_t stream);
 
 /* ---- Per-stage entry points: the same kernels the layer runs, one stage at
  * ---- a time (for checking and profiling each stage). ---- */

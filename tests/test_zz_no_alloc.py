@@ -1,0 +1,70 @@
+"""The layer entry point that allocates nothing (vdn_hybrid_attn_fwd_noalloc):
+its workspace is the library's static device scratch.  Checked through the C
+ABI against vdn_hybrid_attn_fwd (the same kernels on a caller's workspace) on
+two calls in a row, the second with a smaller input, and against the oracle's
+bound; layouts beyond the scratch are rejected on the host."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import vdn_oracle as O
+from video_diffusion_hybrid_block_amd import binding as V
+from video_diffusion_hybrid_block_amd import synth
+
+from _helpers import TOL, custom, oracle_layout, rel_err, require_gpu, to_dev
+
+
+def _geo(w):
+    return dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+                window_chunks=w.window_chunks)
+
+
+def test_noalloc_rejects_layouts_beyond_the_scratch():
+    """A layout whose workspace exceeds the scratch returns status 7 before
+    any device call (fake, never dereferenced pointers)."""
+    lay = V.make_layout(batch=1, heads=24, head_dim=128, frames=60, tokens_per_frame=1008,
+                        text_tokens=512, dtype="bf16")
+    assert V.workspace_size(lay) > V.NOALLOC_SCRATCH_BYTES
+    ok = ctypes.c_void_p(0x10000)
+    args = [ok] * 8 + [ctypes.byref(lay), ok, None]
+    assert V.lib().vdn_hybrid_attn_fwd_noalloc(*args) == 7
+    a = list(args); a[9] = None
+    assert V.lib().vdn_hybrid_attn_fwd_noalloc(*a) == 1
+    small = V.make_layout(batch=1, heads=8, head_dim=64, frames=30, tokens_per_frame=112,
+                          text_tokens=64, dtype="bf16")
+    assert V.workspace_size(small) <= V.NOALLOC_SCRATCH_BYTES
+
+
+CALLS = [
+    # the larger call first, then a smaller one (different shape and geometry)
+    dict(name="noalloc_a", batch=1, heads=8, head_dim=64, frames=30, tokens_per_frame=112,
+         text_tokens=64, dtype="bf16", seed=31),
+    dict(name="noalloc_b", batch=2, heads=3, head_dim=128, frames=9, tokens_per_frame=48,
+         text_tokens=16, dtype="bf16", chunk_frames=2, seed=32),
+]
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_entry_point_on_two_calls():
+    require_gpu()
+    for case in CALLS:
+        w = custom(**case)
+        print(f"\n[case] noalloc {case['name']}", flush=True)
+        inp = synth.make_inputs(w)
+        dev = to_dev(inp, w.dtype)
+        lay = V.make_layout(batch=w.batch, heads=w.heads, head_dim=w.head_dim, frames=w.frames,
+                            tokens_per_frame=w.tokens_per_frame, text_tokens=w.text_tokens,
+                            dtype=w.dtype, chunk_frames=w.chunk_frames)
+        assert V.workspace_size(lay) <= V.NOALLOC_SCRATCH_BYTES
+        args = (dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["beta"],
+                dev["alpha"], dev["gate_logits"])
+        got = V.hybrid_attn_noalloc(*args, **_geo(w))
+        ref = V.hybrid_attn(*args, **_geo(w))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), case["name"]
+        err = rel_err(got.float().cpu().numpy(), O.hybrid_attn(inp, oracle_layout(w)))
+        print(f"{case['name']}: rel err vs oracle {err:.3e}")
+        assert np.isfinite(got.float().cpu().numpy()).all()
+        assert err <= TOL[w.dtype]

@@ -17,7 +17,7 @@ __all__ = [
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
     "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "softmax_branches_mxfp8",
-    "vda_gram", "vda_factor_scan", "vda_branch",
+    "vda_gram", "vda_factor_scan", "vda_branch", "hybrid_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
     "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
     "train_saved_size", "hybrid_attn_fwd_train", "hybrid_attn_bwd_saved",
@@ -29,6 +29,7 @@ VDN_F32, VDN_BF16 = 0, 1
 _STATUS = {
     0: "ok", 1: "null argument", 2: "bad shape", 3: "unsupported dtype or head size",
     4: "device pointer not 16-byte aligned", 5: "workspace too small", 6: "HIP launch error",
+    7: "layout needs more than the built-in scratch",
 }
 
 EXPORTED_SYMBOLS = (
@@ -42,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
     "vdn_hybrid_attn_proj_mxfp8_fwd", "vdn_softmax_branches_mxfp8_fwd",
     "vdn_hybrid_attn_train_saved_size", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
-    "vdn_vda_branch",
+    "vdn_vda_branch", "vdn_hybrid_attn_fwd_noalloc",
 )
 
 
@@ -140,6 +141,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_proj_mxfp8_fwd.restype = ctypes.c_int
         L.vdn_vda_branch.argtypes = [vp] * 6 + [lp, vp, vp, sz, vp]
         L.vdn_vda_branch.restype = ctypes.c_int
+        L.vdn_hybrid_attn_fwd_noalloc.argtypes = [vp] * 8 + [lp, vp, vp]
+        L.vdn_hybrid_attn_fwd_noalloc.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -269,6 +272,38 @@ def hybrid_attn(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, frames,
         _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vdn_hybrid_attn_fwd")
+    return out
+
+
+# VDN_NOALLOC_SCRATCH_BYTES of include/vdn.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def hybrid_attn_noalloc(q, k, v, text_k, text_v, beta, alpha, gate_logits, *, frames,
+                        tokens_per_frame, chunk_frames=5, window_chunks=1, anchor_first=True,
+                        anchor_last=True, softmax_scale=0.0, rms_eps=0.0,
+                        out=None) -> torch.Tensor:
+    """The layer without a workspace (``vdn_hybrid_attn_fwd_noalloc``): the
+    library's built-in device scratch replaces it, so the call itself
+    allocates nothing (``out`` is allocated here when None).  Layouts whose
+    workspace exceeds ``NOALLOC_SCRATCH_BYTES`` raise (status 7)."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    _check_inputs(lay, q, k, v, text_k, text_v)
+    B, N, H, _ = q.shape
+    L = lay.text_tokens
+    _expect(beta, (B, N + L, H), torch.float32, "beta")
+    _expect(alpha, (B, frames, H), torch.float32, "alpha")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    st = lib().vdn_hybrid_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(text_k if L else None), _ptr(text_v if L else None),
+        _ptr(beta), _ptr(alpha), _ptr(gate_logits), ctypes.byref(lay), _ptr(out), _stream())
+    _check(st, "vdn_hybrid_attn_fwd_noalloc")
     return out
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "vdn_internal.h"
 
 using namespace vdn;
@@ -86,6 +88,73 @@ hipError_t vda_forward(const void* k, const void* v, const void* text_k, const v
   return e;
 }
 
+// Host-side checks of the layer's arguments (everything but the workspace).
+vdn_status_t check_layer_args(const void* q, const void* k, const void* v, const void* text_k,
+                              const void* text_v, const float* beta, const float* alpha,
+                              const float* gate_logits, const vdn_layout_t* layout,
+                              const void* o) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!q || !k || !v || !beta || !alpha || !gate_logits || !o || !text_ok(*layout, text_k, text_v))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
+      !aligned16(gate_logits) || !aligned16(o) || !text_aligned(text_k, text_v))
+    return VDN_ERR_MISALIGNED;
+  return VDN_OK;
+}
+
+// The layer on a workspace of at least make_plan(l).total bytes: the VDA
+// branch, then the softmax with the merge in its epilogue.
+hipError_t layer_forward(const void* q, const void* k, const void* v, const void* text_k,
+                         const void* text_v, const float* beta, const float* alpha,
+                         const float* gate_logits, const vdn_layout_t& l, void* o, char* ws,
+                         hipStream_t stream) {
+  const Plan p = make_plan(l);
+  float* R = (float*)(ws + p.r_off);
+  bool vt_done = false;
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
+  if (e != hipSuccess) return e;
+  if (softmax_merge_fusable(l))
+    return launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                eff_eps(l), false, o, ws + p.vt_off, stream, vt_done);
+  e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
+  if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
+  return e;
+}
+
+}  // namespace
+
+// Workspace of vdn_hybrid_attn_fwd_noalloc.  In host code `scratch` names a
+// host-side stand-in, not the device array: the device address comes from
+// hipGetSymbolAddress, once per device (each GPU holds its own copy), and
+// only that address is handed to kernels.
+static __device__ __align__(256) char scratch[VDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there, with that device current).
+hipError_t scratch_on_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +170,7 @@ const char* vdn_status_str(vdn_status_t s) {
     case VDN_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
     case VDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case VDN_ERR_HIP: return "HIP launch error";
+    case VDN_ERR_SCRATCH_TOO_SMALL: return "layout needs more than the built-in scratch";
   }
   return "unknown status";
 }
@@ -306,29 +376,28 @@ vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, co
                                  const void* text_v, const float* beta, const float* alpha,
                                  const float* gate_logits, const vdn_layout_t* layout, void* o,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  vdn_status_t st = check_layout(layout);
+  vdn_status_t st = check_layer_args(q, k, v, text_k, text_v, beta, alpha, gate_logits, layout, o);
   if (st != VDN_OK) return st;
-  if (!q || !k || !v || !beta || !alpha || !gate_logits || !o || !workspace ||
-      !text_ok(*layout, text_k, text_v))
-    return VDN_ERR_NULL_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
-      !aligned16(gate_logits) || !aligned16(o) || !aligned16(workspace) ||
-      !text_aligned(text_k, text_v))
-    return VDN_ERR_MISALIGNED;
-  const Plan p = make_plan(*layout);
-  if (workspace_bytes < p.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
-  char* ws = (char*)workspace;
-  float* R = (float*)(ws + p.r_off);
-  const vdn_layout_t& l = *layout;
-  bool vt_done = false;
-  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
+  if (!workspace) return VDN_ERR_NULL_ARG;
+  if (!aligned16(workspace)) return VDN_ERR_MISALIGNED;
+  if (workspace_bytes < make_plan(*layout).total) return VDN_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(layer_forward(q, k, v, text_k, text_v, beta, alpha, gate_logits, *layout, o,
+                                  (char*)workspace, stream));
+}
+
+vdn_status_t vdn_hybrid_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                         const void* text_k, const void* text_v,
+                                         const float* beta, const float* alpha,
+                                         const float* gate_logits, const vdn_layout_t* layout,
+                                         void* o, hipStream_t stream) {
+  vdn_status_t st = check_layer_args(q, k, v, text_k, text_v, beta, alpha, gate_logits, layout, o);
+  if (st != VDN_OK) return st;
+  if (make_plan(*layout).total > (size_t)VDN_NOALLOC_SCRATCH_BYTES) return VDN_ERR_SCRATCH_TOO_SMALL;
+  char* ws = nullptr;
+  hipError_t e = scratch_on_current_device(&ws);
   if (e != hipSuccess) return hip_status(e);
-  if (softmax_merge_fusable(l))
-    return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                           eff_eps(l), false, o, ws + p.vt_off, stream, vt_done));
-  e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
-  if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
-  return hip_status(e);
+  return hip_status(layer_forward(q, k, v, text_k, text_v, beta, alpha, gate_logits, *layout, o,
+                                  ws, stream));
 }
 
 }  // extern "C"

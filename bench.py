@@ -3,16 +3,19 @@
 forward on one MI355X, at the 768p shape (B=1, H=24, d=128, 60 latent frames x
 1008 tokens = 60,480 video tokens, 512 text tokens, bf16).
 
-A step is one call of the whole layer (vdn_hybrid_attn_fwd: Gram/write,
-factor, scan, then the block-sparse softmax with the merge fused into its
-epilogue) on synthetic inputs already resident in HBM.  Prints one JSON line:
-layer throughput in video tokens/s, the roofline of the dominant kernel (the
-fused softmax + merge stage, timed alone with HIP events on its stream), and
-the CPU oracle timed on a bounded sample of the same workload.  It also times
-the layer followed by the two branches' separate output projections
-(d_model = H*d), the projection product alone, and the library matmul on the
-same operands for comparison, and the backward pass (gradients of every input
-given an upstream gradient of O).
+A step is one call of the whole layer (vdn_hybrid_attn_fwd: the VDA branch -
+statistics, factor and V^T copy in one pass, then the bidirectional scan -
+followed by the block-sparse softmax with the merge fused into its epilogue)
+on synthetic inputs already resident in HBM.  Prints one JSON line: layer
+throughput in video tokens/s (warm; cold runs with the caches flushed are
+reported beside it), the roofline of the dominant kernel (the fused softmax +
+merge, launched alone as the layer's second stage and timed with HIP events
+on its stream), the VDA branch against the HBM roof, the same layer on the
+long (120-frame) and the stress (batch 2, ill-conditioned) shapes, and the
+CPU oracle timed on a bounded sample of the 768p workload.  It also times the
+layer followed by the two branches' separate output projections (d_model =
+H*d), the projection product alone and the library matmul on the same
+operands, and the backward pass.
 """
 from __future__ import annotations
 
@@ -31,6 +34,11 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k1_softmax_768p_hbm_traffic.md")
+VDA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vda_branch_768p_hbm_traffic.md")
+VDA_SOURCES = ["video_diffusion_hybrid_block_amd/csrc/k_vda_stats.hip",
+               "video_diffusion_hybrid_block_amd/csrc/k_scan.hip",
+               "video_diffusion_hybrid_block_amd/csrc/vdn_device.h",
+               "video_diffusion_hybrid_block_amd/csrc/vdn_internal.h"]
 K1_SOURCES = ["video_diffusion_hybrid_block_amd/csrc/k_softmax.hip",
               "video_diffusion_hybrid_block_amd/csrc/vdn_device.h",
               "video_diffusion_hybrid_block_amd/csrc/vdn_internal.h"]
@@ -71,82 +79,151 @@ def sources_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per softmax launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE, sources=K1_SOURCES, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].split(": ", 1)
                 vals[k.strip()] = v.strip().strip("`")
-    if vals.get("sources_sha256_16") != sources_hash(K1_SOURCES):
+    if vals.get("sources_sha256_16") != sources_hash(sources):
         return None
     try:
-        return int(float(vals["traffic_bytes_per_launch"]))
+        return int(float(vals[key]))
     except (KeyError, ValueError):
         return None
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
-    """The float64 oracle on a bounded sample: every token of five frames
-    (both anchors and three interior frames), head after head of batch 0,
-    until about budget_s seconds of CPU work (at least one head)."""
+def scan_frames(w):
+    """Frames the forward and the backward state fold (non-anchor frames
+    before the window of the last chunk that has a non-anchor frame, resp.
+    after the window of the first one)."""
+    T, C, wc = w.frames, w.chunk_frames, w.window_chunks
+    nc = -(-T // C)
+    anchors = {0, T - 1}
+    win_lo = lambda c: max(0, (c - wc) * C)
+    win_hi = lambda c: min(T, (c + wc + 1) * C) - 1
+    has_query = lambda c: any(t not in anchors for t in range(c * C, min((c + 1) * C, T)))
+    fend = next((win_lo(c) for c in reversed(range(nc)) if has_query(c)), 0)
+    fbeg = next((win_hi(c) for c in range(nc) if has_query(c)), T - 1)
+    fwd = [f for f in range(T) if f < fend and f not in anchors]
+    bwd = [f for f in range(T) if f > fbeg and f not in anchors]
+    return fwd, bwd, nc
+
+
+def vda_bytes(w):
+    """Bytes the VDA branch must move as built, all batches and heads, each
+    counted once: K, V and beta of the frames it folds (V of every frame and
+    the text, for the V^T copy), the V^T copy written, G (bf16 hi + lo) and B
+    written by the statistics pass and read once per fold step by the scan,
+    the chunk snapshots written, and the combine's reads and writes."""
+    fwd, bwd, nc = scan_frames(w)
+    stat = len(set(fwd) | set(bwd))
+    P, L, T, d = w.tokens_per_frame, w.text_tokens, w.frames, w.head_dim
+    mat = d * d * 4
+    stats = (T * P + L) * d * 2 + (stat * P + L) * d * 2 + (stat * P + L) * 4 \
+        + (T * P + L) * d * 2 + (stat + 1) * 2 * mat
+    text_step = 1 if L else 0
+    scan = (len(fwd) + len(bwd) + 2 * text_step) * 2 * mat + 2 * (nc + 1) * mat
+    combine = 3 * (nc + 1) * mat
+    return (stats + scan + combine) * w.batch * w.heads
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def cpu_baseline(w, inp, budget_s=20.0):
+    """The float64 oracle on a bounded sample of whole heads: heads of batch 0
+    in turn, each its complete forward (every video token: the softmax of
+    every frame, the frame statistics and every frame's state folds), until
+    about budget_s seconds of CPU work; the layer's time is the mean head's
+    time x B x H (heads are independent and of equal size)."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import vdn_oracle as O
     from video_diffusion_hybrid_block_amd import synth
     lay = O.Layout(**synth.layout_kwargs(w))
-    frames = sorted({0, w.frames // 4, w.frames // 2, (3 * w.frames) // 4, w.frames - 1})
-    P = w.tokens_per_frame
-    import numpy as np
-    tokens = np.concatenate([np.arange(f * P, (f + 1) * P) for f in frames])
-    t0 = time.perf_counter()
-    heads = 0
-    while heads < w.heads:
-        O.hybrid_attn_rows(inp, lay, 0, heads, tokens)
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    tokens = np.arange(w.video_tokens)
+    t_start = time.perf_counter()
+    per_head = []
+    while len(per_head) < w.heads and (not per_head or time.perf_counter() - t_start < budget_s):
+        t0 = time.perf_counter()
+        O.hybrid_attn_rows(inp, lay, 0, len(per_head), tokens)
+        per_head.append(time.perf_counter() - t0)
+    layer_s = sum(per_head) / len(per_head) * w.batch * w.heads
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    # one video token of the layer = all heads of that token
-    tok_equiv = len(tokens) * heads / w.heads
-    return {"value": tok_equiv / dt, "unit": "video tokens/s", "cores": threads,
+    return {"value": w.batch * w.video_tokens / layer_s, "unit": "video tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(tokens)} query tokens (frames {frames}) x {heads} of {w.heads} heads, "
-                      f"batch 0; {dt:.1f} s; counted as {len(tokens)}*{heads}/{w.heads} "
-                      f"layer tokens"}
+            "sample": f"{len(per_head)} of {w.batch * w.heads} (batch, head) pairs, each the "
+                      f"oracle's complete forward of one head ({w.video_tokens} queries), "
+                      f"{sum(per_head):.1f} s; layer time = mean head x {w.batch * w.heads} = "
+                      f"{layer_s:.0f} s",
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_info()}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="768p")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-proj", action="store_true",
-                    help="skip the layer-with-output-projections timing")
-    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
-    ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a 1 GiB device copy (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(the layer shards by head; see the design notes). Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def time_calls(fn, steps, warmup, stream, flush=None):
+    """Warm: `steps` back-to-back calls between two events (mean) and each
+    call between its own events (median, min).  Cold (flush given): each call
+    after the flush, its own events around the call only."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in ev)
+    out = {"mean": mean, "median": each[len(each) // 2], "min": each[0]}
+    if flush is not None:
+        cold = []
+        for _ in range(steps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        cold.sort()
+        out["cold_median"] = cold[len(cold) // 2]
+        out["cold_min"] = cold[0]
+    return out
 
-    import numpy as np
+
+def layer_figures(w, steps, warmup, flush=None, keep=False):
+    """The layer on workload w: warm (and cold) call times, and its two
+    stages launched alone - the VDA branch (vdn_vda_branch, writing the V^T
+    copy) and the fused softmax + merge (vdn_softmax_merge_fwd_vt)."""
     import torch
 
     from video_diffusion_hybrid_block_amd import binding as V
     from video_diffusion_hybrid_block_amd import synth
-
-    w = synth.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -164,48 +241,83 @@ def main():
                         chunk_frames=w.chunk_frames, window_chunks=w.window_chunks)
     ws = torch.empty(V.workspace_size(lay), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dev["q"])
-    o_fused = torch.empty_like(dev["q"])
     tk, tv = (dev["text_k"], dev["text_v"]) if L else (None, None)
-    # the summed VDA states the fused stage reads (computed once, untimed)
-    A, Bm = V.vda_gram(dev["k"], dev["v"], tk, tv, dev["beta"], **geo)
-    R = V.vda_factor_scan(A, Bm, dev["alpha"], dtype=w.dtype, text_tokens=L, **geo)
-    sws = torch.empty(max(V.softmax_workspace_size(lay), 1), dtype=torch.uint8, device="cuda")
+    R, vt = V.vda_branch(dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"], want_vt=True,
+                         workspace=ws, **geo)
 
     def layer():
         V.hybrid_attn(dev["q"], dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"],
                       dev["gate_logits"], **geo, out=out, workspace=ws)
 
-    def fused_stage():
-        V.softmax_merge_fwd(dev["q"], dev["k"], dev["v"], tk, tv, R, dev["gate_logits"], **geo,
-                            out=o_fused, workspace=sws)
+    def vda():
+        V.vda_branch(dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"], out=R, vt_out=vt,
+                     workspace=ws, **geo)
+
+    def softmax_stage():
+        V.softmax_merge_fwd_vt(dev["q"], dev["k"], tk, vt, R, dev["gate_logits"], **geo, out=out)
 
     stream = torch.cuda.current_stream()
-    print(f"[bench] warmup {args.warmup}, timing {args.steps} layer steps", file=sys.stderr,
+    print(f"[bench] {w.name}: warmup {warmup}, timing {steps} layer steps", file=sys.stderr,
           flush=True)
-    for _ in range(args.warmup):
-        layer()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        layer()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    t0 = time.perf_counter()
+    lay_t = time_calls(layer, steps, warmup, stream, flush)
+    wall = time.perf_counter() - t0
+    vda_t = time_calls(vda, steps, 2, stream)
+    k1_t = time_calls(softmax_stage, steps, 2, stream)
+    res = {"w": w, "layer": lay_t, "vda": vda_t, "k1": k1_t, "wall": wall}
+    if keep:
+        res.update(inp=inp, dev=dev, lay=lay, geo=geo, R=R, stream=stream, tk=tk, tv=tv)
+    else:
+        del dev, ws, out, R, vt
+        torch.cuda.empty_cache()
+    return res
 
-    # dominant kernel alone, same stream, same launch configuration (the
-    # stage also runs the V^T copy that feeds it: ~1% of its time)
-    for _ in range(2):
-        fused_stage()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        fused_stage()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    k1_ms = e0.elapsed_time(e1) / args.steps
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="768p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-proj", action="store_true",
+                    help="skip the layer-with-output-projections timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long and stress workloads")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the layer shards by head; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from video_diffusion_hybrid_block_amd import binding as V
+    from video_diffusion_hybrid_block_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    # cold runs: a 512 MiB write between calls evicts the L2s and the MALL
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_buf.fill_(1)
+
+    head = layer_figures(w, args.steps, args.warmup, flush=flush, keep=True)
+    del flush_buf
+    torch.cuda.empty_cache()
+    inp, dev, lay, geo, R, stream = (head[k] for k in ("inp", "dev", "lay", "geo", "R", "stream"))
+    tk, tv = head["tk"], head["tv"]
+    L = w.text_tokens
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = head["layer"]["mean"]
+    k1_ms = head["k1"]["mean"]
+    vda_ms = head["vda"]["mean"]
+    sws = torch.empty(max(V.softmax_workspace_size(lay), 1), dtype=torch.uint8, device="cuda")
 
     # the step after the layer: both gated branches through their own output
     # projections (d_model = H*d), as one product (bf16 layouts only)
@@ -368,11 +480,34 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # the long and the stress workloads: the same figures, fewer steps
+    extra = {}
+    if not args.no_extra and args.workload == "768p":
+        del dev, R, sws
+        head.pop("dev")
+        head.pop("R")
+        torch.cuda.empty_cache()
+        for name in ("long_120f", "stress_lowrank"):
+            xw = synth.WORKLOADS[name]
+            f = layer_figures(xw, max(5, args.steps // 4), 2)
+            xfl = softmax_flops(xw)
+            extra[name] = {
+                "workload": f"B={xw.batch} H={xw.heads} d={xw.head_dim} T={xw.frames} "
+                            f"P={xw.tokens_per_frame} L={xw.text_tokens}",
+                "layer_ms": round(f["layer"]["mean"], 4),
+                "layer_median_ms": round(f["layer"]["median"], 4),
+                "video_tokens_per_s": round(xw.batch * xw.video_tokens / (f["layer"]["mean"] / 1e3), 1),
+                "softmax_ms": round(f["k1"]["mean"], 4),
+                "softmax_frac_bf16_peak": round(xfl / (f["k1"]["mean"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "vda_ms": round(f["vda"]["mean"], 4),
+                "vda_frac_hbm": round(vda_bytes(xw) / (f["vda"]["mean"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     video_tokens = w.batch * w.video_tokens
     value = video_tokens / (ms / 1e3)
     k1_flops = softmax_flops(w)
     achieved = k1_flops / (k1_ms / 1e3) / 1e12
-    traffic = measured_traffic()
+    vbytes = vda_bytes(w)
+    lt = head["layer"]
     result = {
         "metric": "hybrid-attn layer ms & video tokens/s at 768p shape; % MFMA/HBM roofline",
         "value": round(value, 1),
@@ -390,12 +525,25 @@ def main():
                                f"T={w.frames} P={w.tokens_per_frame} L={w.text_tokens} "
                                f"chunk={w.chunk_frames} window=+-{w.window_chunks}",
                    "video_tokens": video_tokens, "parallelism": "single GPU"},
-        "roofline": {"kernel": "softmax_vt_kernel<128, 1> (merge fused; + vt_transpose pre-pass)",
+        "layer_ms": {"warm_mean": round(lt["mean"], 4), "warm_median": round(lt["median"], 4),
+                     "warm_min": round(lt["min"], 4), "cold_median": round(lt["cold_median"], 4),
+                     "cold_min": round(lt["cold_min"], 4),
+                     "cold": "a 512 MiB write between calls (evicts L2 and MALL); events "
+                             "around the layer call only"},
+        "roofline": {"kernel": "softmax_vt_kernel<128, 1> (softmax + merge; the layer's second "
+                               "stage, launched alone)",
                      "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "algorithmic_flops_per_launch": k1_flops, "ms_per_launch": round(k1_ms, 4)},
-        "wall_s_timed_region": round(wall, 3),
+        "vda": {"kernels": "vda_stats_kernel<128> + scan_split_kernel<128> + combine_kernel "
+                           "(the layer's first stage, launched alone)",
+                "bound": "hbm", "ms": round(vda_ms, 4), "algorithmic_bytes": vbytes,
+                "achieved_gbs": round(vbytes / (vda_ms / 1e3) / 1e9, 1), "peak_gbs": PEAK_HBM_GBS,
+                "frac": round(vbytes / (vda_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(VDA_TRAFFIC_FILE, VDA_SOURCES)},
+        "other_workloads": extra or None,
+        "wall_s_timed_region": round(head["wall"], 3),
         "output_projections": proj,
         "backward": bwd,
     }

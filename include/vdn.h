@@ -385,21 +385,32 @@ vdn_status_t vdn_vda_factor_scan(float* A_io, const float* B, const float* alpha
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
-/* The layer's whole VDA branch as the layer runs it, up to the summed
- * states: for bf16 layouts with d >= 32 one pass computes every frame's
- * statistics and factor (A stays on chip; G = (I + A)^-1 is kept as bf16 hi
- * and lo planes) and, when the softmax reads a V^T copy (P and L multiples of
- * 8), also writes that copy into the workspace; then the bidirectional scan
- * and the sum of the two states.  Other layouts run vdn_vda_gram's and
- * vdn_vda_factor_scan's kernels.  R_out: float32 [B, H, nc+1, d, d], as
- * vdn_vda_factor_scan's.  Inputs as vdn_hybrid_attn_fwd's; workspace as
+/* The layer's first stage, the whole VDA branch as the layer runs it, up to
+ * the summed states: for bf16 layouts with d >= 32 one pass computes every
+ * frame's statistics and factor (A stays on chip; G = (I + A)^-1 is kept as
+ * bf16 hi and lo planes), then the bidirectional scan and the sum of the two
+ * states; other layouts run vdn_vda_gram's and vdn_vda_factor_scan's
+ * kernels.  R_out: float32 [B, H, nc+1, d, d], as vdn_vda_factor_scan's.
+ * vt_out (may be NULL; only for the layouts vdn_softmax_merge_fwd covers):
+ * the V^T copy the layer's softmax reads, bf16 [B, H, d, T*P + L] (row d of
+ * head h: value d of every video token, then of every text token), written
+ * by the same pass.  Inputs as vdn_hybrid_attn_fwd's; workspace as
  * vdn_hybrid_attn_fwd's (vdn_hybrid_attn_workspace_size bytes, caller-owned,
- * contents undefined afterwards).  R_out must not alias the workspace.
+ * contents undefined afterwards).  Outputs must not alias the workspace.
  * [deepmagic blog, 用兩條分支取代一條; PaperDaily §三, §四] */
 vdn_status_t vdn_vda_branch(const void* k, const void* v, const void* text_k,
                             const void* text_v, const float* beta, const float* alpha,
-                            const vdn_layout_t* layout, float* R_out, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream);
+                            const vdn_layout_t* layout, float* R_out, void* vt_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The layer's second stage: vdn_softmax_merge_fwd with V given as the V^T
+ * copy vdn_vda_branch wrote (vt, bf16 [B, H, d, T*P + L]) instead of v and
+ * text_v; one kernel, no workspace.  vdn_vda_branch followed by this call is
+ * vdn_hybrid_attn_fwd, bit for bit.  [PaperDaily §二, §三] */
+vdn_status_t vdn_softmax_merge_fwd_vt(const void* q, const void* k, const void* text_k,
+                                      const void* vt, const float* R,
+                                      const float* gate_logits, const vdn_layout_t* layout,
+                                      void* o, hipStream_t stream);
 
 /* Read + RMSNorm + gates + merge: o = sigmoid(g0) * o_soft
  *   + sigmoid(g1) * RMSNorm(R[c] q), with R from vdn_vda_factor_scan

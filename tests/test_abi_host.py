@@ -120,15 +120,26 @@ def test_entry_points_reject_bad_arguments_before_launch():
     a = list(sm); a[10] = 16
     assert lib.vdn_softmax_merge_fwd(*a) == 5
     # the layer's VDA branch: same argument checks as the layer
-    vb = [ok, ok, nul, nul, ok, ok, ref, ok, ok, 1 << 40, nul]
+    vb = [ok, ok, nul, nul, ok, ok, ref, ok, nul, ok, 1 << 40, nul]
     a = list(vb); a[7] = nul
     assert lib.vdn_vda_branch(*a) == 1
     a = list(vb); a[5] = odd
     assert lib.vdn_vda_branch(*a) == 4
-    a = list(vb); a[9] = 16
+    a = list(vb); a[10] = 16
     assert lib.vdn_vda_branch(*a) == 5
     a = list(vb); a[6] = ctypes.byref(lay_t)
     assert lib.vdn_vda_branch(*a) == 1                  # text tensors missing
+    a = list(vb); a[8] = ok                              # V^T copy: fused layouts only
+    assert lib.vdn_vda_branch(*a) == 3
+    a = list(vb); a[8] = odd; a[6] = ctypes.byref(lay_vt)
+    assert lib.vdn_vda_branch(*a) == 4
+    # the second stage from a V^T copy
+    sv = [ok, ok, nul, ok, ok, ok, ctypes.byref(lay_vt), ok, nul]
+    assert lib.vdn_softmax_merge_fwd_vt(*sv[:6], ref, *sv[7:]) == 3
+    a = list(sv); a[3] = nul
+    assert lib.vdn_softmax_merge_fwd_vt(*a) == 1
+    a = list(sv); a[7] = odd
+    assert lib.vdn_softmax_merge_fwd_vt(*a) == 4
 
 
 def test_backward_and_training_entry_points_reject_bad_arguments_before_launch():

@@ -292,6 +292,38 @@ def test_stage_vda_branch(case):
     assert max(errs) <= 2e-3
 
 
+TWO_STAGE = [
+    dict(name="two_stage_d64", batch=1, heads=8, head_dim=64, frames=30, tokens_per_frame=112,
+         text_tokens=64, dtype="bf16"),
+    dict(name="two_stage_d128_b2", batch=2, heads=3, head_dim=128, frames=11, tokens_per_frame=264,
+         text_tokens=24, dtype="bf16", chunk_frames=3),
+    dict(name="two_stage_d32_no_text", batch=1, heads=4, head_dim=32, frames=7, tokens_per_frame=40,
+         text_tokens=0, dtype="bf16", chunk_frames=2),
+]
+
+
+@pytest.mark.parametrize("case", TWO_STAGE, ids=[c["name"] for c in TWO_STAGE])
+def test_two_stages_equal_the_layer(case):
+    """vdn_vda_branch (with the V^T copy) followed by vdn_softmax_merge_fwd_vt
+    runs the layer's kernels in the layer's order: the output is the layer's
+    bit for bit, and the V^T copy is V transposed exactly."""
+    require_gpu()
+    w = custom(**case)
+    _announce(f"two stages {case['name']}")
+    inp = synth.make_inputs(w)
+    dev = to_dev(inp, w.dtype)
+    L = w.text_tokens
+    tk, tv = (dev["text_k"], dev["text_v"]) if L else (None, None)
+    R, vt = V.vda_branch(dev["k"], dev["v"], tk, tv, dev["beta"], dev["alpha"], want_vt=True,
+                         **geo_kw(w))
+    out = V.softmax_merge_fwd_vt(dev["q"], dev["k"], tk, vt, R, dev["gate_logits"], **geo_kw(w))
+    ref = run_layer(w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    vall = dev["v"] if not L else torch.cat([dev["v"], dev["text_v"]], dim=1)
+    assert torch.equal(vt, vall.permute(0, 2, 3, 1).contiguous())
+
+
 @pytest.mark.parametrize("name", STAGE_CASES + ["768p"])
 def test_stage_softmax(name):
     """Softmax branch alone: bf16 P and bf16 output rounding (~2^-9) bound the

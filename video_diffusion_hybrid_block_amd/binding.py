@@ -17,7 +17,8 @@ __all__ = [
     "num_chunks", "workspace_size", "softmax_workspace_size", "factor_scan_workspace_size",
     "hybrid_attn",
     "softmax_fwd", "softmax_merge_fwd", "softmax_branches_fwd", "softmax_branches_mxfp8",
-    "vda_gram", "vda_factor_scan", "vda_branch", "hybrid_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "vda_gram", "vda_factor_scan", "vda_branch", "softmax_merge_fwd_vt", "hybrid_attn_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "merge", "out_proj", "hybrid_attn_proj", "proj_workspace_size", "hybrid_attn_bwd",
     "bwd_workspace_size", "mxfp8_quantize", "out_proj_mxfp8", "hybrid_attn_proj_mxfp8",
     "train_saved_size", "hybrid_attn_fwd_train", "hybrid_attn_bwd_saved",
@@ -43,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "vdn_out_proj_mxfp8", "vdn_hybrid_attn_proj_mxfp8_workspace_size",
     "vdn_hybrid_attn_proj_mxfp8_fwd", "vdn_softmax_branches_mxfp8_fwd",
     "vdn_hybrid_attn_train_saved_size", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
-    "vdn_vda_branch", "vdn_hybrid_attn_fwd_noalloc",
+    "vdn_vda_branch", "vdn_hybrid_attn_fwd_noalloc", "vdn_softmax_merge_fwd_vt",
 )
 
 
@@ -139,7 +140,9 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_proj_mxfp8_workspace_size.restype = sz
         L.vdn_hybrid_attn_proj_mxfp8_fwd.argtypes = [vp] * 10 + [ctypes.c_int32, lp, vp, vp, sz, vp]
         L.vdn_hybrid_attn_proj_mxfp8_fwd.restype = ctypes.c_int
-        L.vdn_vda_branch.argtypes = [vp] * 6 + [lp, vp, vp, sz, vp]
+        L.vdn_vda_branch.argtypes = [vp] * 6 + [lp, vp, vp, vp, sz, vp]
+        L.vdn_softmax_merge_fwd_vt.argtypes = [vp] * 6 + [lp, vp, vp]
+        L.vdn_softmax_merge_fwd_vt.restype = ctypes.c_int
         L.vdn_vda_branch.restype = ctypes.c_int
         L.vdn_hybrid_attn_fwd_noalloc.argtypes = [vp] * 8 + [lp, vp, vp]
         L.vdn_hybrid_attn_fwd_noalloc.restype = ctypes.c_int
@@ -701,10 +704,12 @@ def vda_factor_scan(A, Bm, alpha, *, dtype, text_tokens, frames, tokens_per_fram
 
 
 def vda_branch(k, v, text_k, text_v, beta, alpha, *, frames, tokens_per_frame, chunk_frames=5,
-               window_chunks=1, anchor_first=True, anchor_last=True, out=None,
-               workspace=None) -> torch.Tensor:
-    """The layer's VDA branch up to the summed states (``vdn_vda_branch``):
-    returns R, float32 [B, H, nc+1, d, d] (slot nc = text write)."""
+               window_chunks=1, anchor_first=True, anchor_last=True, out=None, vt_out=None,
+               want_vt=False, workspace=None):
+    """The layer's first stage (``vdn_vda_branch``): returns R, float32
+    [B, H, nc+1, d, d] (slot nc = text write), or (R, vt) with ``want_vt`` or
+    a ``vt_out`` buffer: vt the V^T copy the layer's softmax reads, bf16
+    [B, H, d, T*P + L]."""
     lay = _layout_from(k, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
                        window_chunks=window_chunks, anchor_first=anchor_first,
                        anchor_last=anchor_last)
@@ -718,11 +723,42 @@ def vda_branch(k, v, text_k, text_v, beta, alpha, *, frames, tokens_per_frame, c
     if out is None:
         out = torch.empty((B, H, nc + 1, d, d), dtype=torch.float32, device=k.device)
     _expect(out, (B, H, nc + 1, d, d), torch.float32, "out")
+    if want_vt and vt_out is None:
+        vt_out = torch.empty((B, H, d, N + L), dtype=k.dtype, device=k.device)
+    if vt_out is not None:
+        _expect(vt_out, (B, H, d, N + L), k.dtype, "vt_out")
     workspace = _workspace(workspace, workspace_size(lay), k.device)
     _check(lib().vdn_vda_branch(_ptr(k), _ptr(v), _ptr(text_k if L else None),
                                 _ptr(text_v if L else None), _ptr(beta), _ptr(alpha),
-                                ctypes.byref(lay), _ptr(out), _ptr(workspace),
+                                ctypes.byref(lay), _ptr(out), _ptr(vt_out), _ptr(workspace),
                                 workspace.numel(), _stream()), "vdn_vda_branch")
+    return (out, vt_out) if vt_out is not None else out
+
+
+def softmax_merge_fwd_vt(q, k, text_k, vt, R, gate_logits, *, frames, tokens_per_frame,
+                         chunk_frames=5, window_chunks=1, anchor_first=True, anchor_last=True,
+                         softmax_scale=0.0, rms_eps=0.0, out=None) -> torch.Tensor:
+    """The layer's second stage (``vdn_softmax_merge_fwd_vt``): softmax and
+    merge from the V^T copy ``vda_branch`` returns."""
+    lay = _layout_from(q, text_k, frames, tokens_per_frame, chunk_frames=chunk_frames,
+                       window_chunks=window_chunks, anchor_first=anchor_first,
+                       anchor_last=anchor_last, softmax_scale=softmax_scale, rms_eps=rms_eps)
+    _check(validate_layout(lay), "layout")
+    B, N, H, d = q.shape
+    L = lay.text_tokens
+    _expect(q, (B, N, H, d), q.dtype, "q")
+    _expect(k, (B, N, H, d), q.dtype, "k")
+    if L:
+        _expect(text_k, (B, L, H, d), q.dtype, "text_k")
+    _expect(vt, (B, H, d, N + L), q.dtype, "vt")
+    _expect(R, (B, H, num_chunks(lay) + 1, d, d), torch.float32, "R")
+    _expect(gate_logits, (B, N, H, 2), torch.float32, "gate_logits")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    _check(lib().vdn_softmax_merge_fwd_vt(_ptr(q), _ptr(k), _ptr(text_k if L else None), _ptr(vt),
+                                          _ptr(R), _ptr(gate_logits), ctypes.byref(lay), _ptr(out),
+                                          _stream()), "vdn_softmax_merge_fwd_vt")
     return out
 
 

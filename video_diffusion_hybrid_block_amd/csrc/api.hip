@@ -64,9 +64,11 @@ bool text_aligned(const void* tk, const void* tv) {
 // also writes the softmax's V^T copy when the softmax reads one; *vt_done
 // tells), then the scan from the pre-split G planes.  Other layouts take the
 // separate gram, factor and scan kernels.
+// vt_dst: where the V^T copy goes (the workspace's region for the layer,
+// the caller's buffer for vdn_vda_branch, or null: not written).
 hipError_t vda_forward(const void* k, const void* v, const void* text_k, const void* text_v,
                        const float* beta, const float* alpha, const vdn_layout_t& l, char* ws,
-                       hipStream_t stream, bool* vt_done, float* R_out = nullptr) {
+                       hipStream_t stream, bool* vt_done, float* R_out, void* vt_dst) {
   const Plan p = make_plan(l);
   float* A = (float*)(ws + p.a_off);
   float* B = (float*)(ws + p.b_off);
@@ -75,8 +77,8 @@ hipError_t vda_forward(const void* k, const void* v, const void* text_k, const v
   float* R = R_out ? R_out : (float*)(ws + p.r_off);
   *vt_done = false;
   if (l.dtype == VDN_BF16 && l.head_dim_k >= 32) {
-    const bool vt = softmax_uses_vt(l);
-    hipError_t e = launch_vda_stats(k, v, text_k, text_v, beta, l, A, B, vt ? ws + p.vt_off : nullptr,
+    const bool vt = softmax_uses_vt(l) && vt_dst;
+    hipError_t e = launch_vda_stats(k, v, text_k, text_v, beta, l, A, B, vt ? vt_dst : nullptr,
                                     stream);
     if (e == hipSuccess) e = launch_scan_split(A, B, alpha, l, Sf, Sb, R, stream);
     *vt_done = vt && e == hipSuccess;
@@ -112,7 +114,8 @@ hipError_t layer_forward(const void* q, const void* k, const void* v, const void
   const Plan p = make_plan(l);
   float* R = (float*)(ws + p.r_off);
   bool vt_done = false;
-  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done, nullptr,
+                             ws + p.vt_off);
   if (e != hipSuccess) return e;
   if (softmax_merge_fusable(l))
     return launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
@@ -356,20 +359,44 @@ vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R, const 
 
 vdn_status_t vdn_vda_branch(const void* k, const void* v, const void* text_k, const void* text_v,
                             const float* beta, const float* alpha, const vdn_layout_t* layout,
-                            float* R_out, void* workspace, size_t workspace_bytes,
+                            float* R_out, void* vt_out, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   vdn_status_t st = check_layout(layout);
   if (st != VDN_OK) return st;
   if (!k || !v || !beta || !alpha || !R_out || !workspace || !text_ok(*layout, text_k, text_v))
     return VDN_ERR_NULL_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(alpha) ||
-      !aligned16(R_out) || !aligned16(workspace) || !text_aligned(text_k, text_v))
+      !aligned16(R_out) || !aligned16(workspace) || !text_aligned(text_k, text_v) ||
+      (vt_out && !aligned16(vt_out)))
     return VDN_ERR_MISALIGNED;
+  if (vt_out && !softmax_merge_fusable(*layout)) return VDN_ERR_UNSUPPORTED;
   const Plan p = make_plan(*layout);
   if (workspace_bytes < p.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
   bool vt_done = false;
-  return hip_status(
-      vda_forward(k, v, text_k, text_v, beta, alpha, *layout, (char*)workspace, stream, &vt_done, R_out));
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, *layout, (char*)workspace, stream,
+                             &vt_done, R_out, vt_out);
+  if (e == hipSuccess && vt_out && !vt_done)   // layouts without the fused statistics pass
+    e = launch_transpose(v, text_v, layout->batch, layout->heads, layout->head_dim_k,
+                         layout->frames * layout->tokens_per_frame, layout->text_tokens, vt_out,
+                         stream);
+  return hip_status(e);
+}
+
+vdn_status_t vdn_softmax_merge_fwd_vt(const void* q, const void* k, const void* text_k,
+                                      const void* vt, const float* R, const float* gate_logits,
+                                      const vdn_layout_t* layout, void* o, hipStream_t stream) {
+  vdn_status_t st = check_layout(layout);
+  if (st != VDN_OK) return st;
+  if (!softmax_merge_fusable(*layout)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !vt || !R || !gate_logits || !o || (layout->text_tokens > 0 && !text_k))
+    return VDN_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(R) || !aligned16(gate_logits) ||
+      !aligned16(o) || (text_k && !aligned16(text_k)))
+    return VDN_ERR_MISALIGNED;
+  // the kernel reads V only through vt; v / text_v are not needed
+  return hip_status(launch_softmax_merge(q, k, nullptr, text_k, nullptr, R, gate_logits, *layout,
+                                         eff_scale(*layout), eff_eps(*layout), false, o,
+                                         (void*)vt, stream, true));
 }
 
 vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_k,
@@ -708,7 +735,8 @@ vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const 
   char* xq = ws + fp8_codes_off(l);
   char* xs = ws + fp8_scales_off(l);
   bool vt_done = false;
-  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done, nullptr,
+                             ws + p.vt_off);
   if (e == hipSuccess)
     e = launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
                                       eff_eps(l), xq, xs, ws + p.vt_off, stream, vt_done);
@@ -747,7 +775,8 @@ vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* 
   float* R = (float*)(ws + p.r_off);
   void* x2 = ws + proj_x2_off(l);
   bool vt_done = false;
-  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done);
+  hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done, nullptr,
+                             ws + p.vt_off);
   if (e == hipSuccess)
     e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
                              true, x2, ws + p.vt_off, stream, vt_done);

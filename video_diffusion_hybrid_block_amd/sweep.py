@@ -20,6 +20,10 @@ Inputs are synthetic, drawn on the device from a seeded generator with the
 beta = sigmoid(N(0,1)); alpha ~ U[0.9, 1); gate logits ~ N(0,1)).
 
     python -m video_diffusion_hybrid_block_amd.sweep [--frames 42 60 81 102] [--reps 5]
+
+``--tiles-only`` prints the same densities at the kernel's own granularity
+(256-query work items x 64-key tiles, partial tiles counted whole) without
+touching the GPU.
 """
 from __future__ import annotations
 
@@ -48,6 +52,51 @@ def visible_frame_counts(frames: int, chunk: int, window: int, anchors: bool) ->
 def density(frames: int, chunk: int = 5, window: int = 1, anchors: bool = True) -> float:
     """Share of video (query frame, key frame) pairs the softmax handles."""
     return sum(visible_frame_counts(frames, chunk, window, anchors)) / float(frames * frames)
+
+
+# Work item of the softmax kernel: 256 queries of one frame against its
+# visible keys (the window's frames, the anchors, then the text), packed
+# back to back and taken 64 keys at a time.
+ITEM_QUERIES, TILE_KEYS = 256, 64
+
+
+def tile_count(frames: int, P: int, L: int, chunk: int = 5, window: int = 1,
+               anchors: bool = True, text: bool = True) -> int:
+    """(256-query item, 64-key tile) pairs the softmax kernel runs for one
+    head: every frame has ceil(P / 256) items, each with ceil(n / 64) key
+    tiles for its n visible keys (text keys counted when `text`)."""
+    items = -(-P // ITEM_QUERIES)
+    return sum(items * (-(-(v * P + (L if text else 0)) // TILE_KEYS))
+               for v in visible_frame_counts(frames, chunk, window, anchors))
+
+
+def tile_density(frames: int, P: int, L: int, chunk: int = 5, window: int = 1,
+                 anchors: bool = True, text: bool = False) -> float:
+    """The softmax density at the kernel's granularity: its (item, key tile)
+    pairs over those of dense attention on the same frames (a window that
+    covers every chunk), video keys only unless `text`."""
+    nc = -(-frames // chunk)
+    return (tile_count(frames, P, L, chunk, window, anchors, text)
+            / float(tile_count(frames, P, L, chunk, nc, anchors, text)))
+
+
+def tile_rows(frame_counts, P: int = 1008, L: int = 512, chunk: int = 5, window: int = 1):
+    """Frame-pair and tile-granularity density and anchor increment per frame
+    count (no GPU)."""
+    rows = []
+    for T in frame_counts:
+        row = {"frames": T,
+               "density_pct": round(100 * density(T, chunk, window, True), 3),
+               "anchor_increment_pct": round(100 * (density(T, chunk, window, True)
+                                                    - density(T, chunk, window, False)), 3)}
+        for text in (False, True):
+            tag = "_with_text" if text else ""
+            a = tile_density(T, P, L, chunk, window, True, text)
+            na = tile_density(T, P, L, chunk, window, False, text)
+            row[f"tile_density{tag}_pct"] = round(100 * a, 3)
+            row[f"tile_anchor_increment{tag}_pct"] = round(100 * (a - na), 3)
+        rows.append(row)
+    return rows
 
 
 def softmax_flops(frames: int, P: int, L: int, H: int, d: int, chunk: int, window: int) -> float:
@@ -106,7 +155,26 @@ def main(argv=None):
     ap.add_argument("--text-tokens", type=int, default=512)
     ap.add_argument("--heads", type=int, default=24)
     ap.add_argument("--json", action="store_true", help="one JSON object per frame count")
+    ap.add_argument("--tiles-only", action="store_true",
+                    help="print the frame-pair and tile-granularity densities only (no GPU)")
     args = ap.parse_args(argv)
+
+    if args.tiles_only:
+        rows = tile_rows(args.frames, args.tokens_per_frame, args.text_tokens)
+        if args.json:
+            for r in rows:
+                print(json.dumps(r))
+            return
+        print("| frames | density (frame pairs) | anchor incr. (frame pairs) | density (tiles) | "
+              "anchor incr. (tiles) | density (tiles, text keys incl.) | "
+              "anchor incr. (tiles, text keys incl.) |")
+        print("|" + "---|" * 7)
+        for r in rows:
+            print(f"| {r['frames']} | {r['density_pct']} % | {r['anchor_increment_pct']} % | "
+                  f"{r['tile_density_pct']} % | {r['tile_anchor_increment_pct']} % | "
+                  f"{r['tile_density_with_text_pct']} % | "
+                  f"{r['tile_anchor_increment_with_text_pct']} % |")
+        return
 
     import torch
 

@@ -16,10 +16,13 @@
 // (batch, head, slot); two workgroups per CU, so one streams its tiles while
 // the other inverts.
 //  * Tiles of 64 tokens go global -> LDS with 16-byte direct-to-LDS loads into
-//    an XOR-swizzled [token][d] layout.  beta*k is formed in fp32 and split
-//    into bf16 hi + lo, so A = K^T (bK)_hi + K^T (bK)_lo and B likewise with V
-//    (two bf16 MFMA passes; a single rounding of beta*k moves the small
-//    eigen-directions of I + A on ill-conditioned key sets).
+//    an XOR-swizzled [token][d] layout, two tiles in a ring: tile t+1 is in
+//    flight while tile t is used, one barrier per tile.  beta*k is formed in
+//    fp32 and split into bf16 hi + lo in registers, from the K fragment the
+//    wave reads for its block column, so A = K^T (bK)_hi + K^T (bK)_lo and B
+//    likewise with V (two bf16 MFMA passes; a single rounding of beta*k moves
+//    the small eigen-directions of I + A on ill-conditioned key sets).  At
+//    d = 128 a wave owns one block column (four 32 x 32 blocks of A or B).
 //  * V^T: ds_read_b64_tr_b16 pairs give each lane 8 consecutive tokens of one
 //    d, stored as 16 bytes into row d of the copy.
 //  * Inverse: I + A is read from A's lower triangle (exactly symmetric) into
@@ -38,33 +41,59 @@ namespace vdn {
 
 namespace {
 
+// Direct-to-LDS copies (lane l's bytes land at lds + size * l) from a
+// wave-uniform global base plus a 32-bit byte offset per lane, written as
+// asm so that the compiler does not order LDS reads after them: it cannot
+// tell which LDS bytes a copy writes, and before a transposed LDS read it
+// would wait for every copy in flight, the ones prefetched for later tiles
+// included.  Completion is the kernel's own vmcnt wait plus a barrier.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, char VDN_LDS* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase),
+                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, float VDN_LDS* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase),
+                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+
 template <int D>
-__global__ void __launch_bounds__(512, 2)
+__global__ void __launch_bounds__(512, 4)
 vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
                  const bf16* __restrict__ tk, const bf16* __restrict__ tv,
                  const float* __restrict__ beta, bf16* __restrict__ Gp, float* __restrict__ Bout,
                  bf16* __restrict__ vt, int nl8, Geo g, int H, int nitems) {
   constexpr int BT = 64;                     // tokens per tile
+  constexpr int NBUF = 2;                    // K / V / beta ring depth
   constexpr int KCH = D / 8;                 // 16-byte chunks per token row
   constexpr int TILE = BT * D * 2;
   constexpr int NW = 8, NT = 64 * NW;
-  constexpr int NI = (BT * KCH + NT - 1) / NT;   // DMA instructions per thread per operand
+  constexpr int NCH = BT * KCH;              // 16-byte chunks per operand tile
+  constexpr int NLW = NCH >= NT ? NW : NCH / 64;   // waves that copy an operand tile
+  constexpr int NI = NCH >= NT ? NCH / NT : 1;     // copies per lane per operand
+  static_assert(NCH % 64 == 0 && (NCH < NT || NCH % NT == 0), "copy split");
   constexpr int NB = D / 32;
   constexpr int NBLK = 2 * NB * NB;          // 32 x 32 blocks of A and B
   constexpr int BLK_PER_WAVE = NBLK >= NW ? NBLK / NW : 1;
   constexpr int ABYTES = D * D * 4;
-  constexpr int SMEM = 4 * TILE > ABYTES ? 4 * TILE : ABYTES;
-  constexpr int NVT = 4 * NB;                // 16-token x 32-d transposed reads per tile
+  constexpr int BOFF = 2 * NBUF * TILE;      // after the K and V rings: beta ring
+  constexpr int ROWOFF = ABYTES;             // sweep's pivot rows, after A
+  constexpr int SMEM_T = BOFF + NBUF * BT * 4;
+  constexpr int SMEM_S = ROWOFF + 2 * D * 4;
+  constexpr int SMEM = SMEM_T > SMEM_S ? SMEM_T : SMEM_S;
+  constexpr int NVT = (BT / 16) * NB;        // 16-token x 32-d transposed reads per tile
   constexpr int RB = D / 16, CB = D / 32;    // sweep: rows / columns per thread
   static_assert(RB == 2 * CB, "sweep grid");
+  constexpr int BETA_WAVE = NW - 1;          // the wave that copies beta
+  // One array for everything: with a second __shared__ array the compiler
+  // orders LDS reads after every direct-to-LDS copy in flight.
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  __shared__ float bsh[BT];
-  __shared__ __attribute__((aligned(16))) float rowbuf[2][D];
   char VDN_LDS* lds = (char VDN_LDS*)smem;
-  char VDN_LDS* Kt = lds;
-  char VDN_LDS* Vt = lds + TILE;
-  char VDN_LDS* Ht = lds + 2 * TILE;         // (beta k) hi
-  char VDN_LDS* Lt = lds + 3 * TILE;         // (beta k) lo
+  float VDN_LDS* bring = (float VDN_LDS*)(lds + BOFF);
+  float VDN_LDS* rowbuf = (float VDN_LDS*)(lds + ROWOFF);   // [2][D], sweep only
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -85,18 +114,18 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
   // V^T row d of this head; the slot's tokens start at column vcol0
   bf16* vtbh = vt ? vt + (size_t)bh * D * nl8 : nullptr;
   const int vcol0 = text ? N : slot * g.P;
+  const int ntiles = (ntok + BT - 1) / BT;
 
   // 32 x 32 output blocks of this wave: matrix (0: A, rows from K; 1: B,
-  // rows from V), block row bi, block column bj.  At d = 128 a wave owns a
-  // 2 x 2 square of one matrix, so per 16 tokens it reads 2 row-side and 2
-  // column-side (hi, lo) fragments instead of 1 + 4 (transposed LDS reads
-  // bound this loop); otherwise block wv.
+  // rows from V), block row bi, block column bj.  A wave keeps one block
+  // column, so per 16 tokens it forms one column-side operand, beta k split
+  // into bf16 hi + lo, in registers, and reads one row-side fragment per
+  // block.
   auto block_of = [&](int i, int& mat, int& bi, int& bj) {
     if constexpr (NB == 4) {
-      const int q = wv & 3;
       mat = wv >> 2;
-      bi = 2 * (q >> 1) + (i >> 1);
-      bj = 2 * (q & 1) + (i & 1);
+      bi = i;
+      bj = wv & 3;
       return true;
     } else {
       const int blk = wv * BLK_PER_WAVE + i;
@@ -106,30 +135,62 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
       return blk < NBLK;
     }
   };
+  int mat0, bi0, bj0;
+  const bool has_blk = block_of(0, mat0, bi0, bj0);
   f32x16 acc[BLK_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < BLK_PER_WAVE; ++i) acc[i] = f32x16{};
 
-  for (int t0 = 0; t0 < ntok; t0 += BT) {
-    __syncthreads();                          // previous tile fully consumed
+  // Copies of tile t into ring slot t % NBUF: waves 0 .. NLW-1 NI 16-byte
+  // chunks of K (statistics slots only) and of V per lane, rows past the
+  // slot's end reading its first token; BETA_WAVE the tile's beta values (4
+  // bytes per lane; lanes past the end write 0 instead).  Tile t+1 is issued
+  // once every wave is done with tile t-1 and lands while tile t is used.
+  const bool copier = sgpr(wv) < NLW;
+  const bool beta_wave = stats && sgpr(wv) == BETA_WAVE;
+  // this lane's chunks: row (token in the tile) and swizzled 16-byte chunk
+  const uint32_t rstride = (uint32_t)H * D * 2;      // bytes between tokens
+  uint32_t coff[NI];
+  int crow[NI];
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int blk = ii * NW + wv;
-      if (blk * 64 >= BT * KCH) break;
-      const int p = blk * 64 + lane;
-      const int row = p / KCH, pch = p % KCH;
-      const int ch = pch ^ swz<D>(row);
-      const int tok = t0 + row < ntok ? t0 + row : 0;
-      const size_t off = ((size_t)(b * (size_t)rows_total + tok0 + tok) * H + h) * D + ch * 8;
-      if (stats) g2lds16(kb + off, Kt + blk * 1024);
-      g2lds16(vb + off, Vt + blk * 1024);
+  for (int ii = 0; ii < NI; ++ii) {
+    const int p = (ii * NLW + wv) * 64 + lane;
+    crow[ii] = p / KCH;
+    coff[ii] = (uint32_t)(((p % KCH) ^ swz<D>(crow[ii])) * 16);
+  }
+  const size_t slot_row0 = (size_t)b * rows_total + tok0;
+  auto issue = [&](int t) {
+    const int t0 = t * BT, sl = t % NBUF;
+    const int last = sgpr(ntok - 1 - t0);           // rows past it read it
+    if (beta_wave) {
+      float VDN_LDS* bs = bring + sl * BT;
+      const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      if ((int)ln <= last) dma4(sgpr_ptr(bptr + (size_t)t0 * H), ln * (uint32_t)(H * 4), bs);
+      else bs[ln] = 0.f;
     }
-    if (stats && tid < BT) {
-      const int tk_ = t0 + tid;
-      bsh[tid] = tk_ < ntok ? bptr[(size_t)tk_ * H] : 0.f;
+    if (copier) {
+      const size_t e0 = ((slot_row0 + t0) * H + h) * D;
+      const bf16* kbase = (const bf16*)sgpr_ptr(kb + e0);
+      const bf16* vbase = (const bf16*)sgpr_ptr(vb + e0);
+#pragma unroll
+      for (int ii = 0; ii < NI; ++ii) {
+        const int blk = ii * NLW + wv;
+        const uint32_t off = (uint32_t)(crow[ii] < last ? crow[ii] : last) * rstride + coff[ii];
+        if (stats) dma16(kbase, off, lds + sl * TILE + blk * 1024);
+        dma16(vbase, off, lds + (NBUF + sl) * TILE + blk * 1024);
+      }
     }
-    wait_vmem();
-    __syncthreads();
+  };
+  if (ntiles > 0) issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * BT, sl = t % NBUF;
+    const char VDN_LDS* Kt = lds + sl * TILE;
+    const char VDN_LDS* Vt = lds + (NBUF + sl) * TILE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // tile t is in LDS for every wave, and every wave is done with tile t-1,
+    // whose ring slot receives tile t+1
+    lds_barrier();
+    if (t + 1 < ntiles) issue(t + 1);
     if (vtbh) {
       // lane l gets V[t0 + r0 + 8 (l / 32) + e][c0 + l % 32], e = 0..7: 16
       // bytes of V^T row c0 + l % 32
@@ -139,49 +200,42 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
         if (call >= NVT) break;
         const int r0 = (call / NB) * 16, c0 = (call % NB) * 32;
         const bf16x8 val = lds_col8<D>(Vt, r0, c0, lane);
-        const int t = t0 + r0 + 8 * (lane >> 5);
-        if (t < ntok)
-          *(bf16x8*)(vtbh + (size_t)(c0 + (lane & 31)) * nl8 + vcol0 + t) = val;
+        const int tt = t0 + r0 + 8 * (lane >> 5);
+        if (tt < ntok)
+          *(bf16x8*)(vtbh + (size_t)(c0 + (lane & 31)) * nl8 + vcol0 + tt) = val;
       }
     }
-    if (!stats) continue;
-    // beta*k -> bf16 hi / lo, same swizzled layout as K
+    if (!stats || !has_blk) continue;
+    const float VDN_LDS* bt_ = bring + sl * BT;
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      if ((ii * NW + wv) * 64 >= BT * KCH) break;
-      const int p = (ii * NW + wv) * 64 + lane;
-      const float bt = bsh[p / KCH];
-      const bf16x8 kv = *(const bf16x8 VDN_LDS*)(Kt + p * 16);
+    for (int ks = 0; ks < BT / 16; ++ks) {
+      // column side: beta k of 8 tokens in column bj0 * 32 + l % 32, split
+      // into bf16 hi + lo
+      const bf16x8 kc = lds_col8<D>(Kt, ks * 16, bj0 * 32, lane);
+      const f32x4 b0 = *(const f32x4 VDN_LDS*)(bt_ + ks * 16 + 8 * (lane >> 5));
+      const f32x4 b1 = *(const f32x4 VDN_LDS*)(bt_ + ks * 16 + 8 * (lane >> 5) + 4);
       bf16x8 hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16 a, c;
-        split_bf16((float)kv[e] * bt, a, c);
-        hi[e] = a;
-        lo[e] = c;
+        bf16 x, y;
+        split_bf16((float)kc[e] * (e < 4 ? b0[e] : b1[e - 4]), x, y);
+        hi[e] = x;
+        lo[e] = y;
       }
-      *(bf16x8 VDN_LDS*)(Ht + p * 16) = hi;
-      *(bf16x8 VDN_LDS*)(Lt + p * 16) = lo;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BT / 16; ++ks) {
 #pragma unroll
       for (int i = 0; i < BLK_PER_WAVE; ++i) {
         int mat, bi, bj;
         if (!block_of(i, mat, bi, bj)) continue;
         const bf16x8 a = lds_col8<D>(mat == 0 ? Kt : Vt, ks * 16, bi * 32, lane);
-        const bf16x8 bh_ = lds_col8<D>(Ht, ks * 16, bj * 32, lane);
-        const bf16x8 bl_ = lds_col8<D>(Lt, ks * 16, bj * 32, lane);
-        acc[i] = mfma32(a, bh_, acc[i]);
-        acc[i] = mfma32(a, bl_, acc[i]);
+        acc[i] = mfma32(a, hi, acc[i]);
+        acc[i] = mfma32(a, lo, acc[i]);
       }
     }
   }
   if (!stats) return;
 
   // B to HBM; A into LDS (fp32, row-major) for the inverse
-  __syncthreads();                            // every wave is done with the tiles
+  lds_barrier();                              // every wave is done with the tiles
   float VDN_LDS* Al = (float VDN_LDS*)smem;
   const size_t mat_off = ((size_t)bh * (g.T + 1) + slot) * D * D;
   const int half = lane >> 5;
@@ -197,7 +251,7 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
       else Bout[mat_off + (size_t)r * D + c] = acc[i][j];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   const int ti = tid & 15, tc = tid >> 4;     // 16 x 32 thread grid
   const int r0 = ti * RB, c0 = tc * CB;
@@ -211,14 +265,14 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
     }
   if (ti == 0) {
 #pragma unroll
-    for (int j = 0; j < CB; ++j) rowbuf[0][c0 + j] = m[0][j];
+    for (int j = 0; j < CB; ++j) rowbuf[c0 + j] = m[0][j];
   }
-  __syncthreads();
+  lds_barrier();
   for (int kb = 0; kb < 16; ++kb) {
 #pragma unroll
     for (int km = 0; km < RB; ++km) {
       const int kk = kb * RB + km;
-      const float* rk = rowbuf[kk & 1];
+      const float VDN_LDS* rk = rowbuf + (kk & 1) * D;
       // pivots are diagonals of Schur complements of I + A: all >= 1
       const float sk = __builtin_amdgcn_rsqf(rk[kk]);
       float wi[RB], wc[CB];
@@ -243,15 +297,15 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
       if (km + 1 < RB) {
         if (ti == kb) {
 #pragma unroll
-          for (int j = 0; j < CB; ++j) rowbuf[(kk + 1) & 1][c0 + j] = m[(km + 1) % RB][j];
+          for (int j = 0; j < CB; ++j) rowbuf[((kk + 1) & 1) * D + c0 + j] = m[(km + 1) % RB][j];
         }
       } else if (kb + 1 < 16) {
         if (ti == kb + 1) {
 #pragma unroll
-          for (int j = 0; j < CB; ++j) rowbuf[(kk + 1) & 1][c0 + j] = m[0][j];
+          for (int j = 0; j < CB; ++j) rowbuf[((kk + 1) & 1) * D + c0 + j] = m[0][j];
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   // G = (I + A)^-1 = -M, as bf16 hi and lo planes

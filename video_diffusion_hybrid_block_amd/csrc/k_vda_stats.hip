@@ -41,25 +41,6 @@ namespace vdn {
 
 namespace {
 
-// Direct-to-LDS copies (lane l's bytes land at lds + size * l) from a
-// wave-uniform global base plus a 32-bit byte offset per lane, written as
-// asm so that the compiler does not order LDS reads after them: it cannot
-// tell which LDS bytes a copy writes, and before a transposed LDS read it
-// would wait for every copy in flight, the ones prefetched for later tiles
-// included.  Completion is the kernel's own vmcnt wait plus a barrier.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, char VDN_LDS* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase),
-                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
-               : "memory");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, float VDN_LDS* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(voff), "s"(sbase),
-                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
-               : "memory");
-}
-
 template <int D>
 __global__ void __launch_bounds__(512, 4)
 vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -165,7 +146,7 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
     if (beta_wave) {
       float VDN_LDS* bs = bring + sl * BT;
       const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-      if ((int)ln <= last) dma4(sgpr_ptr(bptr + (size_t)t0 * H), ln * (uint32_t)(H * 4), bs);
+      if ((int)ln <= last) dma4s(sgpr_ptr(bptr + (size_t)t0 * H), ln * (uint32_t)(H * 4), bs);
       else bs[ln] = 0.f;
     }
     if (copier) {
@@ -176,8 +157,8 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
       for (int ii = 0; ii < NI; ++ii) {
         const int blk = ii * NLW + wv;
         const uint32_t off = (uint32_t)(crow[ii] < last ? crow[ii] : last) * rstride + coff[ii];
-        if (stats) dma16(kbase, off, lds + sl * TILE + blk * 1024);
-        dma16(vbase, off, lds + (NBUF + sl) * TILE + blk * 1024);
+        if (stats) dma16s(kbase, off, lds + sl * TILE + blk * 1024);
+        dma16s(vbase, off, lds + (NBUF + sl) * TILE + blk * 1024);
       }
     }
   };

@@ -162,6 +162,34 @@ __device__ __forceinline__ void g2lds16(const void* gptr, char VDN_LDS* lds_wave
   __builtin_amdgcn_global_load_lds(gptr, (void VDN_LDS*)lds_wave_base, 16, 0, 0);
 }
 
+// The same copies written as asm, from a wave-uniform base plus a 32-bit
+// byte offset per lane (dma16s, dma4s) or from a 64-bit address per lane
+// (dma16v).  The compiler then does not order LDS reads after them: it cannot
+// tell which LDS bytes a copy writes, and before a transposed LDS read it
+// waits for every copy in flight, the ones prefetched for later tiles
+// included.  Completion is the kernel's own vmcnt wait plus a barrier.
+// The compiler's hazard checks do not look inside the asm, so each copy
+// starts with five wait states: enough after an SGPR written by a VALU
+// instruction (v_readfirstlane of the base) and after the M0 write.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, char VDN_LDS* lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase),
+                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, float VDN_LDS* lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase),
+                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+__device__ __forceinline__ void dma16v(const void* gptr, char VDN_LDS* lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr),
+                  "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier that orders LDS only: each wave waits for its own LDS

@@ -99,6 +99,16 @@ const char* vdn_status_str(vdn_status_t status);
 /* hipError_t of the most recent VDN_ERR_HIP on the calling thread (0 if none). */
 int vdn_last_hip_error(void);
 
+/* Diagnostics for a failing call (not part of the method).  Name of the stage
+ * (kernel launch: "vda_stats", "scan_split", "softmax_merge", ...) whose launch
+ * failed most recently on the calling thread, or NULL if none has.  With the
+ * environment variable VDN_SYNC_DEBUG=1 set before the first call, every stage
+ * synchronises its stream and checks for errors, so a fault during a kernel is
+ * reported by the call and stage that launched it (not on a stream under graph
+ * capture; slower).  With VDN_ROCTX=1, each stage is bracketed by a roctx range
+ * when the ROCm roctx library can be loaded.  The returned string is static. */
+const char* vdn_last_failed_stage(void);
+
 /* Host-only check of a layout: returns VDN_OK, VDN_ERR_NULL_ARG,
  * VDN_ERR_BAD_SHAPE or VDN_ERR_UNSUPPORTED.  Touches no device. */
 vdn_status_t vdn_validate_layout(const vdn_layout_t* layout);

@@ -34,7 +34,8 @@ _STATUS = {
 }
 
 EXPORTED_SYMBOLS = (
-    "vdn_version", "vdn_status_str", "vdn_last_hip_error", "vdn_validate_layout",
+    "vdn_version", "vdn_status_str", "vdn_last_hip_error", "vdn_last_failed_stage",
+    "vdn_validate_layout",
     "vdn_num_chunks", "vdn_hybrid_attn_workspace_size", "vdn_hybrid_attn_fwd",
     "vdn_softmax_workspace_size", "vdn_softmax_fwd", "vdn_softmax_merge_fwd", "vdn_vda_gram",
     "vdn_vda_factor_scan_workspace_size",
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_status_str.restype = ctypes.c_char_p
         L.vdn_status_str.argtypes = [ctypes.c_int]
         L.vdn_last_hip_error.restype = ctypes.c_int
+        L.vdn_last_failed_stage.restype = ctypes.c_char_p
+        L.vdn_last_failed_stage.argtypes = []
         L.vdn_validate_layout.restype = ctypes.c_int
         L.vdn_validate_layout.argtypes = [lp]
         L.vdn_num_chunks.restype = i32
@@ -168,7 +171,18 @@ def make_layout(*, batch, heads, head_dim, frames, tokens_per_frame, text_tokens
 
 def _check(status: int, what: str):
     if status != 0:
+        if status == 6:
+            stage = last_failed_stage()
+            if stage:
+                what = f"{what} (stage {stage}, hipError {lib().vdn_last_hip_error()})"
         raise VdnError(status, what)
+
+
+def last_failed_stage():
+    """Stage whose launch (or, with VDN_SYNC_DEBUG=1, execution) failed last
+    on this thread, or None (``vdn_last_failed_stage``)."""
+    s = lib().vdn_last_failed_stage()
+    return s.decode() if s else None
 
 
 def validate_layout(layout: Layout) -> int:

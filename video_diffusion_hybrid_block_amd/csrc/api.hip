@@ -1,7 +1,9 @@
 // C ABI of the hybrid layer: argument validation, workspace planning and the
 // sequence of stage launches.  Everything is enqueued on the caller's stream;
 // nothing here allocates device memory or synchronises the host.
+#include <dlfcn.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -19,6 +21,60 @@ vdn_status_t hip_status(hipError_t e) {
   g_last_hip_error = (int)e;
   return VDN_ERR_HIP;
 }
+
+// Diagnostics, read from the environment on first use; both off by default.
+// VDN_SYNC_DEBUG=1: after each stage launch the stream is synchronised and
+// checked, so an asynchronous failure is reported by the call (and stage)
+// that caused it (skipped on a stream under graph capture).  VDN_ROCTX=1:
+// each stage is a roctx range on the calling thread, when the ROCm roctx
+// library can be loaded (rocprofv3 --marker-trace records them).
+struct Diag {
+  bool sync = false;
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Diag& diag() {
+  static const Diag d = [] {
+    Diag r;
+    const char* s = getenv("VDN_SYNC_DEBUG");
+    r.sync = s && s[0] == '1';
+    const char* t = getenv("VDN_ROCTX");
+    if (t && t[0] == '1') {
+      void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_GLOBAL);
+      if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_GLOBAL);
+      if (h) {
+        r.push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+        r.pop = (int (*)())dlsym(h, "roctxRangePop");
+        if (!r.push || !r.pop) r.push = nullptr, r.pop = nullptr;
+      }
+    }
+    return r;
+  }();
+  return d;
+}
+
+thread_local const char* g_failed_stage = nullptr;
+
+// One stage: its launch, bracketed and checked as the diagnostics ask.
+template <class F>
+hipError_t stage(const char* name, hipStream_t s, F&& launch) {
+  const Diag& d = diag();
+  if (d.push) d.push(name);
+  hipError_t e = launch();
+  if (e == hipSuccess && d.sync) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      e = hipStreamSynchronize(s);
+      if (e == hipSuccess) e = hipGetLastError();
+    }
+  }
+  if (d.pop) d.pop();
+  if (e != hipSuccess) g_failed_stage = name;
+  return e;
+}
+
+#define VDN_STAGE(name, ...) stage(name, stream, [&]() -> hipError_t { return __VA_ARGS__; })
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -78,15 +134,15 @@ hipError_t vda_forward(const void* k, const void* v, const void* text_k, const v
   *vt_done = false;
   if (l.dtype == VDN_BF16 && l.head_dim_k >= 32) {
     const bool vt = softmax_uses_vt(l) && vt_dst;
-    hipError_t e = launch_vda_stats(k, v, text_k, text_v, beta, l, A, B, vt ? vt_dst : nullptr,
-                                    stream);
-    if (e == hipSuccess) e = launch_scan_split(A, B, alpha, l, Sf, Sb, R, stream);
+    hipError_t e = VDN_STAGE("vda_stats", launch_vda_stats(k, v, text_k, text_v, beta, l, A, B, vt ? vt_dst : nullptr,
+                                    stream));
+    if (e == hipSuccess) e = VDN_STAGE("scan_split", launch_scan_split(A, B, alpha, l, Sf, Sb, R, stream));
     *vt_done = vt && e == hipSuccess;
     return e;
   }
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
-  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream);
+  hipError_t e = VDN_STAGE("gram", launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream));
+  if (e == hipSuccess) e = VDN_STAGE("factor", launch_factor(A, l, false, stream));
+  if (e == hipSuccess) e = VDN_STAGE("scan", launch_scan(A, B, alpha, l, Sf, Sb, R, stream));
   return e;
 }
 
@@ -118,10 +174,10 @@ hipError_t layer_forward(const void* q, const void* k, const void* v, const void
                              ws + p.vt_off);
   if (e != hipSuccess) return e;
   if (softmax_merge_fusable(l))
-    return launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                eff_eps(l), false, o, ws + p.vt_off, stream, vt_done);
-  e = launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream);
-  if (e == hipSuccess) e = launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream);
+    return VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                eff_eps(l), false, o, ws + p.vt_off, stream, vt_done));
+  e = VDN_STAGE("softmax", launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream));
+  if (e == hipSuccess) e = VDN_STAGE("merge", launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream));
   return e;
 }
 
@@ -180,6 +236,8 @@ const char* vdn_status_str(vdn_status_t s) {
 
 int vdn_last_hip_error(void) { return g_last_hip_error; }
 
+const char* vdn_last_failed_stage(void) { return g_failed_stage; }
+
 vdn_status_t vdn_validate_layout(const vdn_layout_t* layout) { return check_layout(layout); }
 
 int32_t vdn_num_chunks(const vdn_layout_t* layout) {
@@ -214,8 +272,8 @@ vdn_status_t vdn_softmax_fwd(const void* q, const void* k, const void* v, const 
       !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
     return VDN_ERR_MISALIGNED;
   if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
-  return hip_status(launch_softmax(q, k, v, text_k, text_v, *layout, eff_scale(*layout), o_soft,
-                                   workspace, stream));
+  return hip_status(VDN_STAGE("softmax", launch_softmax(q, k, v, text_k, text_v, *layout, eff_scale(*layout), o_soft,
+                                   workspace, stream)));
 }
 
 vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
@@ -233,9 +291,9 @@ vdn_status_t vdn_softmax_merge_fwd(const void* q, const void* k, const void* v,
       !aligned16(o) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
     return VDN_ERR_MISALIGNED;
   if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
-  return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
+  return hip_status(VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
                                          eff_scale(*layout), eff_eps(*layout), false, o, workspace,
-                                         stream));
+                                         stream)));
 }
 
 vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* v,
@@ -254,9 +312,9 @@ vdn_status_t vdn_softmax_branches_fwd(const void* q, const void* k, const void* 
       !aligned16(x2) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
     return VDN_ERR_MISALIGNED;
   if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
-  return hip_status(launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
+  return hip_status(VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, *layout,
                                          eff_scale(*layout), eff_eps(*layout), true, x2, workspace,
-                                         stream));
+                                         stream)));
 }
 
 vdn_status_t vdn_softmax_branches_mxfp8_fwd(const void* q, const void* k, const void* v,
@@ -277,9 +335,9 @@ vdn_status_t vdn_softmax_branches_mxfp8_fwd(const void* q, const void* k, const 
       !aligned16(codes) || !text_aligned(text_k, text_v) || (workspace && !aligned16(workspace)))
     return VDN_ERR_MISALIGNED;
   if (workspace_bytes < need) return VDN_ERR_WORKSPACE_TOO_SMALL;
-  return hip_status(launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, *layout,
+  return hip_status(VDN_STAGE("softmax_branches_mxfp8", launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, *layout,
                                                   eff_scale(*layout), eff_eps(*layout), codes,
-                                                  scales, workspace, stream));
+                                                  scales, workspace, stream)));
 }
 
 vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, int32_t N, void* y,
@@ -289,7 +347,7 @@ vdn_status_t vdn_out_proj(const void* x, const void* w, int64_t M, int32_t K, in
   if (!proj_shape_ok(M, K, N)) return VDN_ERR_UNSUPPORTED;
   if ((M + 255) / 256 * ((N + 255) / 256) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return VDN_ERR_MISALIGNED;
-  return hip_status(launch_proj(x, w, M, K, N, y, stream));
+  return hip_status(VDN_STAGE("proj", launch_proj(x, w, M, K, N, y, stream)));
 }
 
 vdn_status_t vdn_mxfp8_quantize(const void* x, int64_t M, int32_t K, void* q, void* scales,
@@ -298,7 +356,7 @@ vdn_status_t vdn_mxfp8_quantize(const void* x, int64_t M, int32_t K, void* q, vo
   if (M < 1 || K < 1) return VDN_ERR_BAD_SHAPE;
   if (!mx_quant_shape_ok(M, K)) return VDN_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(q)) return VDN_ERR_MISALIGNED;
-  return hip_status(launch_mx_quant(x, M, K, q, scales, stream));
+  return hip_status(VDN_STAGE("mx_quant", launch_mx_quant(x, M, K, q, scales, stream)));
 }
 
 vdn_status_t vdn_out_proj_mxfp8(const void* xq, const void* xs, const void* wq, const void* ws,
@@ -310,7 +368,7 @@ vdn_status_t vdn_out_proj_mxfp8(const void* xq, const void* xs, const void* wq, 
   if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || ((uintptr_t)xs & 3u) ||
       ((uintptr_t)ws & 3u))
     return VDN_ERR_MISALIGNED;
-  return hip_status(launch_proj_mxfp8(xq, xs, wq, ws, M, K, N, y, stream));
+  return hip_status(VDN_STAGE("proj_mxfp8", launch_proj_mxfp8(xq, xs, wq, ws, M, K, N, y, stream)));
 }
 
 vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, const void* text_v,
@@ -323,7 +381,7 @@ vdn_status_t vdn_vda_gram(const void* k, const void* v, const void* text_k, cons
   if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(A_out) ||
       !aligned16(B_out) || !text_aligned(text_k, text_v))
     return VDN_ERR_MISALIGNED;
-  return hip_status(launch_gram(k, v, text_k, text_v, beta, *layout, true, A_out, B_out, stream));
+  return hip_status(VDN_STAGE("gram", launch_gram(k, v, text_k, text_v, beta, *layout, true, A_out, B_out, stream)));
 }
 
 vdn_status_t vdn_vda_factor_scan(float* A_io, const float* B, const float* alpha,
@@ -341,9 +399,9 @@ vdn_status_t vdn_vda_factor_scan(float* A_io, const float* B, const float* alpha
                           layout->head_dim_k * layout->head_dim_k * sizeof(float));
   float* Sf = (float*)workspace;
   float* Sb = (float*)((char*)workspace + snaps);
-  hipError_t e = launch_factor(A_io, *layout, false, stream);
+  hipError_t e = VDN_STAGE("factor", launch_factor(A_io, *layout, false, stream));
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(launch_scan(A_io, B, alpha, *layout, Sf, Sb, R_out, stream));
+  return hip_status(VDN_STAGE("scan", launch_scan(A_io, B, alpha, *layout, Sf, Sb, R_out, stream)));
 }
 
 vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R, const float* gate_logits,
@@ -354,7 +412,7 @@ vdn_status_t vdn_merge(const void* q, const void* o_soft, const float* R, const 
   if (!aligned16(q) || !aligned16(o_soft) || !aligned16(R) || !aligned16(gate_logits) ||
       !aligned16(o))
     return VDN_ERR_MISALIGNED;
-  return hip_status(launch_merge(q, o_soft, R, gate_logits, *layout, eff_eps(*layout), o, stream));
+  return hip_status(VDN_STAGE("merge", launch_merge(q, o_soft, R, gate_logits, *layout, eff_eps(*layout), o, stream)));
 }
 
 vdn_status_t vdn_vda_branch(const void* k, const void* v, const void* text_k, const void* text_v,
@@ -376,9 +434,9 @@ vdn_status_t vdn_vda_branch(const void* k, const void* v, const void* text_k, co
   hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, *layout, (char*)workspace, stream,
                              &vt_done, R_out, vt_out);
   if (e == hipSuccess && vt_out && !vt_done)   // layouts without the fused statistics pass
-    e = launch_transpose(v, text_v, layout->batch, layout->heads, layout->head_dim_k,
+    e = VDN_STAGE("transpose", launch_transpose(v, text_v, layout->batch, layout->heads, layout->head_dim_k,
                          layout->frames * layout->tokens_per_frame, layout->text_tokens, vt_out,
-                         stream);
+                         stream));
   return hip_status(e);
 }
 
@@ -394,9 +452,9 @@ vdn_status_t vdn_softmax_merge_fwd_vt(const void* q, const void* k, const void* 
       !aligned16(o) || (text_k && !aligned16(text_k)))
     return VDN_ERR_MISALIGNED;
   // the kernel reads V only through vt; v / text_v are not needed
-  return hip_status(launch_softmax_merge(q, k, nullptr, text_k, nullptr, R, gate_logits, *layout,
+  return hip_status(VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, nullptr, text_k, nullptr, R, gate_logits, *layout,
                                          eff_scale(*layout), eff_eps(*layout), false, o,
-                                         (void*)vt, stream, true));
+                                         (void*)vt, stream, true)));
 }
 
 vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_k,
@@ -503,24 +561,24 @@ hipError_t bwd_tail(const void* q, const void* k, const void* v, const void* tex
   float* dvec = (float*)(ws + bp.dvec);
   // transposed copies for the softmax backward
   hipError_t e =
-      launch_transpose(k, text_k, l.batch, l.heads, l.head_dim_k, N, g.L, ws + bp.kt, stream);
+      VDN_STAGE("transpose", launch_transpose(k, text_k, l.batch, l.heads, l.head_dim_k, N, g.L, ws + bp.kt, stream));
   if (e == hipSuccess)
-    e = launch_transpose(q, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.qt, stream);
+    e = VDN_STAGE("transpose", launch_transpose(q, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.qt, stream));
   if (e == hipSuccess)
-    e = launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream);
+    e = VDN_STAGE("transpose", launch_transpose(dos, nullptr, l.batch, l.heads, l.head_dim_k, N, 0, ws + bp.dost, stream));
   // linear branch: dq (its part), dA over G, dB over B, dalpha
   if (e == hipSuccess)
-    e = launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
+    e = VDN_STAGE("vda_bwd", launch_vda_bwd(q, k, v, text_k, text_v, beta, alpha, dlin, R, A, B, states,
                        (float*)(ws + bp.dRp), (float*)(ws + bp.dR), (float*)(ws + bp.dspost), dq,
-                       dalpha, l, stream);
+                       dalpha, l, stream));
   // statistics: dk, dv, dtext_k, dtext_v and dbeta (written)
   if (e == hipSuccess)
-    e = launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
-                        stream);
+    e = VDN_STAGE("gram_bwd", launch_gram_bwd(k, v, text_k, text_v, beta, A, B, dk, dv, dtext_k, dtext_v, dbeta, l,
+                        stream));
   // softmax branch: dq, dk, dv, dtext_k, dtext_v (added)
   if (e == hipSuccess)
-    e = launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
-                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream);
+    e = VDN_STAGE("attn_bwd", launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
+                        ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream));
   return e;
 }
 
@@ -602,14 +660,14 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   float* lse = (float*)(ws + bp.lse);
   float* dvec = (float*)(ws + bp.dvec);
   // forward recomputation: statistics, factor, scan (keeping every state)
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
-  if (e == hipSuccess) e = launch_scan(A, B, alpha, l, Sf, Sb, R, stream, states);
+  hipError_t e = VDN_STAGE("gram", launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream));
+  if (e == hipSuccess) e = VDN_STAGE("factor", launch_factor(A, l, false, stream));
+  if (e == hipSuccess) e = VDN_STAGE("scan", launch_scan(A, B, alpha, l, Sf, Sb, R, stream, states));
   // softmax forward with the merge backward in its epilogue
   const EpilogueIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, lse};
   if (e == hipSuccess)
-    e = launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                 eff_eps(l), io, ws + p.vt_off, stream);
+    e = VDN_STAGE("softmax_merge_bwd", launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                 eff_eps(l), io, ws + p.vt_off, stream));
   if (e == hipSuccess)
     e = bwd_tail(q, k, v, text_k, text_v, beta, alpha, l, dq, dk, dv, dtext_k, dtext_v, dbeta,
                  dalpha, ws, stream);
@@ -645,19 +703,19 @@ vdn_status_t vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void*
   float* A = (float*)(ws + p.a_off);
   float* B = (float*)(ws + p.b_off);
   float* R = (float*)(ws + p.r_off);
-  hipError_t e = launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream);
-  if (e == hipSuccess) e = launch_factor(A, l, false, stream);
+  hipError_t e = VDN_STAGE("gram", launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream));
+  if (e == hipSuccess) e = VDN_STAGE("factor", launch_factor(A, l, false, stream));
   if (e == hipSuccess)
-    e = launch_scan(A, B, alpha, l, (float*)(ws + p.sf_off), (float*)(ws + p.sb_off), R, stream,
-                    (float*)(ws + bp.states));
+    e = VDN_STAGE("scan", launch_scan(A, B, alpha, l, (float*)(ws + p.sf_off), (float*)(ws + p.sb_off), R, stream,
+                    (float*)(ws + bp.states)));
   EpilogueIO io{};
   io.lse = (float*)(ws + bp.lse);
   io.o_soft = (float*)(ws + tp.o_soft);
   io.o_lin = (float*)(ws + tp.o_lin);
   io.rinv = (float*)(ws + tp.rinv);
   if (e == hipSuccess)
-    e = launch_softmax_merge_train(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                   eff_eps(l), o, io, ws + p.vt_off, stream);
+    e = VDN_STAGE("softmax_merge_train", launch_softmax_merge_train(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                   eff_eps(l), o, io, ws + p.vt_off, stream));
   return hip_status(e);
 }
 
@@ -678,10 +736,10 @@ vdn_status_t vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void*
   if (saved_bytes < tp.total) return VDN_ERR_WORKSPACE_TOO_SMALL;
   const BwdPlan bp = make_bwd_plan(l);
   char* ws = (char*)saved;
-  hipError_t e = launch_merge_bwd_saved(
+  hipError_t e = VDN_STAGE("merge_bwd_saved", launch_merge_bwd_saved(
       dO, gate_logits, (const float*)(ws + tp.o_soft), (const float*)(ws + tp.o_lin),
       (const float*)(ws + tp.rinv), l, dgate_logits, ws + bp.dos, (float*)(ws + bp.dlin),
-      (float*)(ws + bp.dvec), stream);
+      (float*)(ws + bp.dvec), stream));
   if (e == hipSuccess)
     e = bwd_tail(q, k, v, text_k, text_v, beta, alpha, l, dq, dk, dv, dtext_k, dtext_v, dbeta,
                  dalpha, ws, stream);
@@ -738,9 +796,9 @@ vdn_status_t vdn_hybrid_attn_proj_mxfp8_fwd(const void* q, const void* k, const 
   hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done, nullptr,
                              ws + p.vt_off);
   if (e == hipSuccess)
-    e = launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
-                                      eff_eps(l), xq, xs, ws + p.vt_off, stream, vt_done);
-  if (e == hipSuccess) e = launch_proj_mxfp8(xq, xs, w_q, w_scales, M, K, d_model, y, stream);
+    e = VDN_STAGE("softmax_branches_mxfp8", launch_softmax_branches_mxfp8(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
+                                      eff_eps(l), xq, xs, ws + p.vt_off, stream, vt_done));
+  if (e == hipSuccess) e = VDN_STAGE("proj_mxfp8", launch_proj_mxfp8(xq, xs, w_q, w_scales, M, K, d_model, y, stream));
   return hip_status(e);
 }
 
@@ -778,9 +836,9 @@ vdn_status_t vdn_hybrid_attn_proj_fwd(const void* q, const void* k, const void* 
   hipError_t e = vda_forward(k, v, text_k, text_v, beta, alpha, l, ws, stream, &vt_done, nullptr,
                              ws + p.vt_off);
   if (e == hipSuccess)
-    e = launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
-                             true, x2, ws + p.vt_off, stream, vt_done);
-  if (e == hipSuccess) e = launch_proj(x2, w_o, M, 2 * l.heads * l.head_dim_k, d_model, y, stream);
+    e = VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l), eff_eps(l),
+                             true, x2, ws + p.vt_off, stream, vt_done));
+  if (e == hipSuccess) e = VDN_STAGE("proj", launch_proj(x2, w_o, M, 2 * l.heads * l.head_dim_k, d_model, y, stream));
   return hip_status(e);
 }
 

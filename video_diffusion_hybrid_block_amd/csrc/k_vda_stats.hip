@@ -47,8 +47,9 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
                  const bf16* __restrict__ tk, const bf16* __restrict__ tv,
                  const float* __restrict__ beta, bf16* __restrict__ Gp, float* __restrict__ Bout,
                  bf16* __restrict__ vt, int nl8, Geo g, int H, int nitems) {
-  constexpr int BT = 64;                     // tokens per tile
-  constexpr int NBUF = 2;                    // K / V / beta ring depth
+  constexpr int BT = 32;                     // tokens per tile
+  constexpr int NBUF = 4;                    // K / V / beta ring depth
+  constexpr int AHEAD = NBUF - 1;            // tiles in flight past the one in use
   constexpr int KCH = D / 8;                 // 16-byte chunks per token row
   constexpr int TILE = BT * D * 2;
   constexpr int NW = 8, NT = 64 * NW;
@@ -146,8 +147,10 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
     if (beta_wave) {
       float VDN_LDS* bs = bring + sl * BT;
       const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-      if ((int)ln <= last) dma4s(sgpr_ptr(bptr + (size_t)t0 * H), ln * (uint32_t)(H * 4), bs);
-      else bs[ln] = 0.f;
+      if ((int)ln < BT) {
+        if ((int)ln <= last) dma4s(sgpr_ptr(bptr + (size_t)t0 * H), ln * (uint32_t)(H * 4), bs);
+        else bs[ln] = 0.f;
+      }
     }
     if (copier) {
       const size_t e0 = ((slot_row0 + t0) * H + h) * D;
@@ -162,16 +165,31 @@ vda_stats_kernel(const bf16* __restrict__ k, const bf16* __restrict__ v,
       }
     }
   };
-  if (ntiles > 0) issue(0);
+  // Vector memory operations of this wave per tile (wave-uniform): its
+  // copies (K and V chunks, beta) and its V^T stores.  They complete in
+  // issue order, so "tile t has landed" is a wait until at most the
+  // operations issued after tile t's copies are pending: the copies of the
+  // (up to two) later tiles already issued and the stores of the last
+  // min(t, 3) tiles.  Only the last tile can skip a store (rows past the
+  // slot's end), and no wait follows it.
+  const int ncopy = sgpr((copier ? (stats ? 2 : 1) * NI : 0) + (beta_wave ? 1 : 0));
+  int nstore = 0;
+  if (vtbh) {
+#pragma unroll
+    for (int u = 0; u < (NVT + NW - 1) / NW; ++u) nstore += u * NW + wv < NVT ? 1 : 0;
+  }
+  nstore = sgpr(nstore);
+  for (int i = 0; i < AHEAD; ++i)
+    if (i < ntiles) issue(i);
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = t * BT, sl = t % NBUF;
     const char VDN_LDS* Kt = lds + sl * TILE;
     const char VDN_LDS* Vt = lds + (NBUF + sl) * TILE;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt(ncopy * ((t + 1 < ntiles) + (t + 2 < ntiles)) + nstore * (t < 3 ? t : 3));
     // tile t is in LDS for every wave, and every wave is done with tile t-1,
-    // whose ring slot receives tile t+1
+    // whose ring slot receives tile t+3
     lds_barrier();
-    if (t + 1 < ntiles) issue(t + 1);
+    if (t + AHEAD < ntiles) issue(t + AHEAD);
     if (vtbh) {
       // lane l gets V[t0 + r0 + 8 (l / 32) + e][c0 + l % 32], e = 0..7: 16
       // bytes of V^T row c0 + l % 32

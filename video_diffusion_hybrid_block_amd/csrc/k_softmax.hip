@@ -883,6 +883,241 @@ vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
   }
 }
 
+// Softmax for fp32 layouts on the fp32 matrix cores: v_mfma_f32_32x32x2_f32,
+// fp32 operands and accumulation, so nothing is rounded below fp32.
+//  * Same work items and key walk as the V^T kernel (8 waves x 32 queries,
+//    64-key tiles, segments in SGPRs, multi-segment tiles addressed per row),
+//    with K and V both in their natural [token][d] layout: K rows and V rows
+//    of a tile go global -> LDS with 16-byte direct-to-LDS copies, rows
+//    padded to 4d + 16 bytes, two stages (a tile's compute is ~16x longer
+//    than in bf16, so one tile in flight hides the copies).
+//  * Scores S^T = K Q^T, 2 d-values per MFMA: lane half h takes d in
+//    [h d/2, (h + 1) d/2), so a lane's K fragment for four consecutive steps
+//    is one 16-byte LDS read and its Q fragment 64 registers at d = 128.
+//  * Inside a 32-key block, MFMA row m holds key 8 (m / 8) + 2 (m % 4) +
+//    (m / 4) % 2: accumulator element e of lane half h is then key 2e + h,
+//    exactly the B operand of step e of O^T += V^T P^T, so the
+//    probabilities feed the second product in place.
+//  * O^T row m of d-block db is d = (d/32) m + db, so the V^T operand of
+//    one step for every block is one LDS read of d/32 consecutive floats of
+//    a V row.
+// Writes O_soft (fp32); the merge follows as its own kernel.
+template <int D>
+__global__ void __launch_bounds__(512)
+softmax_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                   const float* __restrict__ v, const float* __restrict__ tk,
+                   const float* __restrict__ tv, float* __restrict__ o, Geo g, int B, int H,
+                   int tpf, float c) {
+  constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 2;
+  constexpr int ND = D / 32;                         // 32-row blocks of O^T
+  constexpr int DCH = D / 4;                         // 16-byte data chunks per row
+  constexpr int RST = 4 * D + 16, RSL = RST / 16;    // row stride (bytes), slots
+  constexpr int TBLK = (BN * RSL + 63) / 64;         // 1 KB copy blocks per operand tile
+  constexpr int NBLK = 2 * TBLK;                     // K tile, then V tile
+  constexpr int NWH = NW / 2;                        // waves per operand
+  constexpr int NIW = (TBLK + NWH - 1) / NWH;        // copies per wave per tile
+  constexpr int VOFF = TBLK * 1024;
+  constexpr int BUFB = (NBLK + 1) * 1024;            // + one spare block
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUFB];
+  char VDN_LDS* lds = (char VDN_LDS*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, ml = lane & 31;
+  const int N = g.T * g.P;
+  WorkItem w = decode_work_xcd(g, B, H, tpf);
+  w.b = sgpr(w.b); w.h = sgpr(w.h); w.t = sgpr(w.t); w.tile = sgpr(w.tile);
+  const KeyMap km = key_map(g, w.t);
+  KeyAddr ka = key_addr(km);
+  ka.e0 = sgpr(ka.e0); ka.e1 = sgpr(ka.e1); ka.e2 = sgpr(ka.e2); ka.nkeys = sgpr(ka.nkeys);
+  ka.d0 = sgpr(ka.d0); ka.d1 = sgpr(ka.d1); ka.d2 = sgpr(ka.d2); ka.clamp_tok = sgpr(ka.clamp_tok);
+  const int nkeys = ka.nkeys;
+
+  const int qlocal = w.tile * BM + wv * 32 + ml;
+  const bool qvalid = qlocal < g.P;
+  const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
+  const size_t qoff = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * D;
+  float qreg[D / 2];
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) {
+    const f32x4 x = *(const f32x4*)(q + qoff + half * (D / 2) + 4 * j);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qreg[4 * j + u] = x[u];
+  }
+
+  const int HD = H * D;
+  const size_t hoff = ((size_t)w.b * N * H + w.h) * D, thoff = ((size_t)w.b * g.L * H + w.h) * D;
+  // waves 0 .. NWH-1 copy the K tile, the others the V tile (same rows)
+  const bool vwave = wv >= NWH;
+  const float* xbh = (vwave ? v : k) + hoff;
+  const float* txbh = (vwave ? tv : tk) + thoff;
+  const int ndma = (TBLK - (wv & (NWH - 1)) + NWH - 1) / NWH;   // NIW or NIW - 1
+  const bool full = ndma == NIW;
+  // copy i of a wave fills block NWH i + (wv % NWH) of its tile: lane slot
+  // jj = 64 blk + lane is row jj / RSL, chunk jj % RSL (the pad slot and
+  // slots past the last row repeat a real chunk into padding)
+  uint32_t offb[NIW];
+  int ldsb[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int blk = i * NWH + (wv & (NWH - 1));
+    const bool ok = blk < TBLK;
+    const int jj = (ok ? blk : 0) * 64 + lane;
+    offb[i] = (uint32_t)(imin(jj / RSL, BN - 1) * HD + imin(jj % RSL, DCH - 1) * 4) * 4u;
+    ldsb[i] = sgpr(ok ? (vwave ? VOFF : 0) + blk * 1024 : NBLK * 1024);
+  }
+  auto seg_of = [=](int kv) {
+    return (int)(((uint32_t)(ka.e0 - 1 - kv) >> 31) + ((uint32_t)(ka.e1 - 1 - kv) >> 31) +
+                 ((uint32_t)(ka.e2 - 1 - kv) >> 31) + ((uint32_t)(ka.nkeys - 1 - kv) >> 31));
+  };
+  const int ntiles = sgpr((nkeys + BN - 1) / BN);
+  auto issue = [=](int tile, int buf) {
+    char VDN_LDS* bb = lds + buf * BUFB;
+    const int kb0 = tile * BN;
+    const int s0 = seg_of(kb0), s1 = seg_of(kb0 + BN - 1);
+    if (s0 == s1 && s0 < 4) {
+      const bool txt = s0 == 3;
+      const int dl = s0 == 0 ? ka.d0 : (s0 == 1 ? ka.d1 : (s0 == 2 ? ka.d2 : -ka.e2));
+      const char* base = sgpr_ptr((txt ? txbh : xbh) + (size_t)(kb0 + dl) * HD);
+#pragma unroll
+      for (int i = 0; i < NIW; ++i)
+        if (i < NIW - 1 || full) g2lds16(base + offb[i], bb + ldsb[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        if (i == NIW - 1 && !full) break;
+        const int blk = i * NWH + (wv & (NWH - 1));
+        const int jj = (blk < TBLK ? blk : 0) * 64 + lane;
+        const int r = key_row(ka, kb0 + imin(jj / RSL, BN - 1));
+        const bool txt = (r & 0x40000000) != 0;
+        const size_t eo = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + imin(jj % RSL, DCH - 1) * 4;
+        g2lds16((txt ? txbh : xbh) + eo, bb + ldsb[i]);
+      }
+    }
+  };
+
+  const int krow = 8 * (ml >> 3) + 2 * (ml & 3) + ((ml >> 2) & 1);
+  const int kread = krow * RST + half * (D / 2) * 4;
+  const int vread = VOFF + half * RST + ml * ND * 4;
+  const bool partial = (nkeys & (BN - 1)) != 0;
+  const float thr = 8.0f / c;   // lazy-rescale margin in score units
+
+  float m_run = -1e30f, m_thr = -1e30f, l_run = 0.f;
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
+
+  issue(0, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < ntiles) issue(it + 1, buf ^ 1);
+    // S^T for the tile's two 32-key blocks
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    const char VDN_LDS* kt = lds + buf * BUFB + kread;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const f32x4 k0 = *(const f32x4 VDN_LDS*)(kt + 16 * j);
+      const f32x4 k1 = *(const f32x4 VDN_LDS*)(kt + 32 * RST + 16 * j);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0[u], qreg[4 * j + u], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1[u], qreg[4 * j + u], s[1], 0, 0, 0);
+      }
+    }
+    if (partial && it == ntiles - 1) {
+      const int lim = sgpr(nkeys - it * BN) - half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 32 + 2 * e >= lim) s[kb][e] = -INFINITY;
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = max3_raw(mx, s[kb][e], s[kb][e + 1]);
+    mx = xhalf_max_raw(mx);
+    // lazy rescale, as in the bf16 kernel: p <= 2^8 between rescales
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2((m_run - m_new) * c);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+      m_run = m_new;
+      m_thr = m_new + thr;
+    }
+    const float mc = m_run * c;
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        s[kb][e] = fast_exp2(fmaf(s[kb][e], c, -mc));
+        s[kb][e + 1] = fast_exp2(fmaf(s[kb][e + 1], c, -mc));
+        la += s[kb][e];
+        lb += s[kb][e + 1];
+      }
+    l_run += la + lb;
+    // O^T += V^T P^T: step e of block kb is keys 32 kb + 2e (lane half 0)
+    // and 32 kb + 2e + 1 (half 1)
+    const char VDN_LDS* vt = lds + buf * BUFB + vread;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const char VDN_LDS* vr = vt + (kb * 32 + 2 * e) * RST;
+        float va[ND];
+        if constexpr (ND == 4) {
+          const f32x4 x = *(const f32x4 VDN_LDS*)vr;
+          va[0] = x[0]; va[1] = x[1]; va[2] = x[2]; va[3] = x[3];
+        } else if constexpr (ND == 2) {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          const f32x2 x = *(const f32x2 VDN_LDS*)vr;
+          va[0] = x[0]; va[1] = x[1];
+        } else {
+          va[0] = *(const float VDN_LDS*)vr;
+        }
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[db], s[kb][e], oacc[db], 0, 0, 0);
+      }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const float inv = 1.0f / xhalf_sum(l_run);
+  if (qvalid) {
+    // element e of block db: O^T row m = 8 (e / 4) + 4 half + e % 4, d = ND m + db
+    float* orow = o + qoff;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      float val[4 * ND];
+#pragma unroll
+      for (int el = 0; el < 4; ++el)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) val[el * ND + db] = oacc[db][e4 * 4 + el] * inv;
+      float* dst = orow + ND * (8 * e4 + 4 * half);
+#pragma unroll
+      for (int u = 0; u < ND; ++u) *(f32x4*)(dst + 4 * u) = f32x4{val[4 * u], val[4 * u + 1], val[4 * u + 2], val[4 * u + 3]};
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_f32(const void* q, const void* k, const void* v, const void* tk, const void* tv,
+                      const vdn_layout_t& l, float scale, void* o, hipStream_t s) {
+  Geo g = make_geo(l);
+  const int tpf = (g.P + 255) / 256;
+  const long grid = (long)l.batch * l.heads * g.T * tpf;
+  softmax_f32_kernel<D><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
+      (const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
+      (float*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
@@ -951,9 +1186,9 @@ hipError_t launch_softmax(const void* q, const void* k, const void* v, const voi
     }
   } else {
     switch (d) {
-      case 128: return launch_valu<float, 128>(q, k, v, tk, tv, l, scale, o, s);
-      case 64: return launch_valu<float, 64>(q, k, v, tk, tv, l, scale, o, s);
-      case 32: return launch_valu<float, 32>(q, k, v, tk, tv, l, scale, o, s);
+      case 128: return launch_f32<128>(q, k, v, tk, tv, l, scale, o, s);
+      case 64: return launch_f32<64>(q, k, v, tk, tv, l, scale, o, s);
+      case 32: return launch_f32<32>(q, k, v, tk, tv, l, scale, o, s);
       case 16: return launch_valu<float, 16>(q, k, v, tk, tv, l, scale, o, s);
     }
   }

@@ -15,9 +15,9 @@
 // gfx950 design (bf16, d in {32, 64, 128}): one workgroup of 8 waves per
 // (batch, head, slot); two workgroups per CU, so one streams its tiles while
 // the other inverts.
-//  * Tiles of 64 tokens go global -> LDS with 16-byte direct-to-LDS loads into
-//    an XOR-swizzled [token][d] layout, two tiles in a ring: tile t+1 is in
-//    flight while tile t is used, one barrier per tile.  beta*k is formed in
+//  * Tiles of 32 tokens go global -> LDS with 16-byte direct-to-LDS loads into
+//    an XOR-swizzled [token][d] layout, four slots in a ring: tiles t+1 ..
+//    t+3 are in flight while tile t is used, one barrier per tile.  beta*k is formed in
 //    fp32 and split into bf16 hi + lo in registers, from the K fragment the
 //    wave reads for its block column, so A = K^T (bK)_hi + K^T (bK)_lo and B
 //    likewise with V (two bf16 MFMA passes; a single rounding of beta*k moves

@@ -104,6 +104,10 @@ EDGE = [
          text_tokens=13, dtype="f32", chunk_frames=2, anchor_first=False, anchor_last=False),
     dict(name="f32_d32_dense", batch=1, heads=3, head_dim=32, frames=8, tokens_per_frame=70,
          text_tokens=8, dtype="f32", chunk_frames=2, window_chunks=4),
+    dict(name="f32_one_frame", batch=1, heads=2, head_dim=128, frames=1, tokens_per_frame=130,
+         text_tokens=0, dtype="f32"),
+    dict(name="f32_one_token_frames", batch=1, heads=2, head_dim=64, frames=13, tokens_per_frame=1,
+         text_tokens=1, dtype="f32", chunk_frames=2),
 ]
 
 

@@ -233,7 +233,19 @@ def test_stage_gram_f32(case):
     _check_gram(custom(**case), 1e-5)
 
 
-@pytest.mark.parametrize("name", STAGE_CASES + ["768p", "stress_lowrank"])
+SCAN_F32 = {
+    # fp32 layouts: the scan's products on the fp32 matrix cores
+    "scan_f32_d128": dict(name="scan_f32_d128", batch=1, heads=2, head_dim=128, frames=23,
+                          tokens_per_frame=16, text_tokens=9, dtype="f32"),
+    "scan_f32_d64": dict(name="scan_f32_d64", batch=2, heads=1, head_dim=64, frames=12,
+                         tokens_per_frame=20, text_tokens=0, dtype="f32", chunk_frames=3),
+    "scan_f32_d32": dict(name="scan_f32_d32", batch=1, heads=2, head_dim=32, frames=9,
+                         tokens_per_frame=40, text_tokens=4, dtype="f32", chunk_frames=2,
+                         window_chunks=2),
+}
+
+
+@pytest.mark.parametrize("name", STAGE_CASES + ["768p", "stress_lowrank"] + list(SCAN_F32))
 def test_stage_factor_scan(name):
     """Summed states per chunk and the text write, from the GPU statistics.
     fp32 symmetric-sweep inverse (error ~cond * 6e-8) and, for bf16 layouts, a
@@ -241,7 +253,7 @@ def test_stage_factor_scan(name):
     layouts, 2e-3 for bf16 layouts (checked against the fp64 oracle on the same
     statistics)."""
     require_gpu()
-    w = workload(name)
+    w = custom(**SCAN_F32[name]) if name in SCAN_F32 else workload(name)
     _announce(f"factor_scan {name}")
     inp = synth.make_inputs(w)
     dev = to_dev(inp, w.dtype)

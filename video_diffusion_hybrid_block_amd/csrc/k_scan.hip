@@ -43,14 +43,21 @@ __device__ __forceinline__ int next_frame(const Geo& g, int dir, int f) {
   return n > fbeg ? n : -1;
 }
 
-template <int D>
+//
+// fp32 layouts (F32): the same chains, steps and snapshots with the product
+// on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, fp32 operands and
+// accumulation, no split).  X = aS + B is formed in place in the state rows
+// (padded to d + 4 floats so the row-fragment reads are conflict-free); lane
+// half h takes d in [h d/2, (h + 1) d/2), so four consecutive MFMA steps read
+// one 16-byte chunk of an X row and of a G row.
+template <int D, bool F32 = false>
 __global__ void __launch_bounds__(2 * D)
 scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
                  const float* __restrict__ alpha, float* __restrict__ Sf, float* __restrict__ Sb,
                  Geo g, int H, float* __restrict__ states) {
   constexpr int NRB = D / 32;           // row blocks per chain = waves per workgroup
   constexpr int NT = 64 * NRB;
-  constexpr int LDF = D;                // fp32 state row stride (floats)
+  constexpr int LDF = F32 ? D + 4 : D;  // fp32 state row stride (floats)
   constexpr int NCH = 32 * D / 8 / NT;  // 8-value chunks of X per thread per step
   constexpr int CPR = D / 4;            // 16-byte chunks per G row
   constexpr int GBYTES = D * D * 4;
@@ -65,7 +72,7 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   // bf16 hi / lo: with separate __shared__ arrays the compiler cannot tell
   // the direct-to-LDS copies of G from the other LDS accesses and waits for
   // the next step's copy before writing X.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * GBYTES + 32 * LDF * 4 + 2 * 32 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * GBYTES + 32 * LDF * 4 + (F32 ? 0 : 2 * 32 * D * 2)];
   char VDN_LDS* Gl = (char VDN_LDS*)smem;
   float VDN_LDS* S = (float VDN_LDS*)(smem + 2 * GBYTES);
   char VDN_LDS* Xh = (char VDN_LDS*)(smem + 2 * GBYTES + 32 * LDF * 4);
@@ -120,6 +127,44 @@ scan_mfma_kernel(const float* __restrict__ G, const float* __restrict__ Bm,
   // S <- (a S + B) G, times `post`; G from LDS buffer bi (G symmetric: its
   // B-operand columns are rows).
   auto step = [&](float a, float post, int bi) {
+    if constexpr (F32) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int q = tid + i * NT;
+        const int r = q / (D / 8), c = (q % (D / 8)) * 8;
+        f32x4 VDN_LDS* sp = (f32x4 VDN_LDS*)((float VDN_LDS*)S + r * LDF + c);
+        const float4 b0 = bcur[2 * i], b1 = bcur[2 * i + 1];
+        f32x4 s0 = sp[0], s1 = sp[1];
+        s0[0] = fmaf(a, s0[0], b0.x); s0[1] = fmaf(a, s0[1], b0.y);
+        s0[2] = fmaf(a, s0[2], b0.z); s0[3] = fmaf(a, s0[3], b0.w);
+        s1[0] = fmaf(a, s1[0], b1.x); s1[1] = fmaf(a, s1[1], b1.y);
+        s1[2] = fmaf(a, s1[2], b1.z); s1[3] = fmaf(a, s1[3], b1.w);
+        sp[0] = s0;
+        sp[1] = s1;
+      }
+      lds_barrier();
+      const int ml = lane & 31;
+      const int n = wv * 32 + ml;
+      const int x = gsw(n);
+      const char VDN_LDS* grow = Gl + bi * GBYTES + n * (4 * D);
+      const float VDN_LDS* xrow = (const float VDN_LDS*)S + ml * LDF + half * (D / 2);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) {
+        const f32x4 g4 = *(const f32x4 VDN_LDS*)(grow + (((half * (D / 8) + j) ^ x) << 4));
+        const f32x4 x4 = *(const f32x4 VDN_LDS*)(xrow + 4 * j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x4[u], g4[u], acc, 0, 0, 0);
+      }
+      lds_barrier();                        // every wave is done reading X
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = (j >> 2) * 8 + half * 4 + (j & 3);
+        S[r * LDF + wv * 32 + ml] = acc[j] * post;
+      }
+      lds_barrier();
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = tid + i * NT;
@@ -712,6 +757,12 @@ hipError_t launch_d(const float* G, const float* B, const float* alpha, const vd
     if constexpr (D >= 32) {
       scan_mfma_kernel<D><<<dim3((unsigned)(chains * (D / 32))), dim3(2 * D), 0, s>>>(
           G, B, alpha, Sf, Sb, g, l.heads, states);
+    }
+  } else if (D >= 32) {
+    if (states) return hipErrorNotSupported;
+    if constexpr (D >= 32) {
+      scan_mfma_kernel<D, true><<<dim3((unsigned)(chains * (D / 32))), dim3(2 * D), 0, s>>>(
+          G, B, alpha, Sf, Sb, g, l.heads, nullptr);
     }
   } else {
     if (states) return hipErrorNotSupported;

@@ -176,6 +176,9 @@ hipError_t layer_forward(const void* q, const void* k, const void* v, const void
   if (softmax_merge_fusable(l))
     return VDN_STAGE("softmax_merge", launch_softmax_merge(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
                                 eff_eps(l), false, o, ws + p.vt_off, stream, vt_done));
+  if (softmax_merge_f32_fusable(l))
+    return VDN_STAGE("softmax_merge_f32", launch_softmax_merge_f32(q, k, v, text_k, text_v, R, gate_logits, l,
+                                eff_scale(l), eff_eps(l), o, stream));
   e = VDN_STAGE("softmax", launch_softmax(q, k, v, text_k, text_v, l, eff_scale(l), o, ws + p.vt_off, stream));
   if (e == hipSuccess) e = VDN_STAGE("merge", launch_merge(q, o, R, gate_logits, l, eff_eps(l), o, stream));
   return e;

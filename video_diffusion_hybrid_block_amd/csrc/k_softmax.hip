@@ -901,13 +901,18 @@ vt_transpose_kernel(const bf16* __restrict__ v, const bf16* __restrict__ tv,
 //  * O^T row m of d-block db is d = (d/32) m + db, so the V^T operand of
 //    one step for every block is one LDS read of d/32 consecutive floats of
 //    a V row.
-// Writes O_soft (fp32); the merge follows as its own kernel.
-template <int D>
+// MODE 0 writes O_soft (fp32; the merge follows as its own kernel); MODE 1
+// the merged output sigmoid(l0) O_soft + sigmoid(l1) RMSNorm(R q), with
+// o_lin^T = R q^T on the same MFMA from the query registers and R staged in
+// the idle ring (its rows ordered like O^T's, so o_lin lands in O^T's
+// register layout).
+template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                    const float* __restrict__ v, const float* __restrict__ tk,
                    const float* __restrict__ tv, float* __restrict__ o, Geo g, int B, int H,
-                   int tpf, float c) {
+                   int tpf, float c, const float* __restrict__ R,
+                   const float* __restrict__ gates, float eps) {
   constexpr int NW = 8, BM = 32 * NW, BN = 64, NBUF = 2;
   constexpr int ND = D / 32;                         // 32-row blocks of O^T
   constexpr int DCH = D / 4;                         // 16-byte data chunks per row
@@ -1088,7 +1093,51 @@ softmax_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const float inv = 1.0f / xhalf_sum(l_run);
+  float inv = 1.0f / xhalf_sum(l_run);
+  float g1 = 0.f;
+  f32x16 lin[ND];
+  if constexpr (MODE == 1) {
+    // R of the state this frame reads (slot nc for anchors) into the ring:
+    // LDS row 32 db + m holds R row (d/32) m + db, rows padded to RST bytes
+    const float* Rs = R + ((size_t)(w.b * H + w.h) * (g.nc + 1) + (is_anchor(g, w.t) ? g.nc : w.t / g.C)) * D * D;
+    const float2 gl = *(const float2*)(gates + ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2);
+    constexpr int NRC = (D * D / 4 + NW * 64 - 1) / (NW * 64);   // 16-byte chunks of R per thread
+    f32x4 xr[NRC];
+#pragma unroll
+    for (int u = 0; u < NRC; ++u)
+      xr[u] = *(const f32x4*)(Rs + 4 * imin(u * NW * 64 + (int)threadIdx.x, D * D / 4 - 1));
+    __syncthreads();                                  // every wave is done with the ring
+#pragma unroll
+    for (int u = 0; u < NRC; ++u) {
+      const int ci = u * NW * 64 + threadIdx.x;
+      if (ci >= D * D / 4) break;
+      const int r = ci / (D / 4), c4 = ci % (D / 4);
+      const int lr = (r % ND) * 32 + r / ND;
+      *(f32x4 VDN_LDS*)(lds + lr * RST + c4 * 16) = xr[u];
+    }
+    __syncthreads();
+    // o_lin^T block db = R[rows (d/32) m + db] q^T: the same d split of the
+    // contraction as the scores (lane half h: d in [h d/2, (h + 1) d/2))
+    float ss = 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      lin[db] = f32x16{};
+      const char VDN_LDS* rr = lds + (db * 32 + ml) * RST + half * (D / 2) * 4;
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) {
+        const f32x4 r4 = *(const f32x4 VDN_LDS*)(rr + 16 * j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          lin[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(r4[u], qreg[4 * j + u], lin[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ss = fmaf(lin[db][e], lin[db][e], ss);
+    }
+    ss = xhalf_sum(ss);
+    const float rinv = rsqrtf(ss * (1.0f / D) + eps);
+    inv *= sigmoidf(gl.x);
+    g1 = sigmoidf(gl.y) * rinv;
+  }
   if (qvalid) {
     // element e of block db: O^T row m = 8 (e / 4) + 4 half + e % 4, d = ND m + db
     float* orow = o + qoff;
@@ -1098,7 +1147,10 @@ softmax_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
       for (int el = 0; el < 4; ++el)
 #pragma unroll
-        for (int db = 0; db < ND; ++db) val[el * ND + db] = oacc[db][e4 * 4 + el] * inv;
+        for (int db = 0; db < ND; ++db) {
+          const float x = oacc[db][e4 * 4 + el] * inv;
+          val[el * ND + db] = MODE == 1 ? fmaf(g1, lin[db][e4 * 4 + el], x) : x;
+        }
       float* dst = orow + ND * (8 * e4 + 4 * half);
 #pragma unroll
       for (int u = 0; u < ND; ++u) *(f32x4*)(dst + 4 * u) = f32x4{val[4 * u], val[4 * u + 1], val[4 * u + 2], val[4 * u + 3]};
@@ -1108,13 +1160,19 @@ softmax_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
 template <int D>
 hipError_t launch_f32(const void* q, const void* k, const void* v, const void* tk, const void* tv,
-                      const vdn_layout_t& l, float scale, void* o, hipStream_t s) {
+                      const vdn_layout_t& l, float scale, void* o, hipStream_t s,
+                      const float* R = nullptr, const float* gates = nullptr, float eps = 0.f) {
   Geo g = make_geo(l);
   const int tpf = (g.P + 255) / 256;
   const long grid = (long)l.batch * l.heads * g.T * tpf;
-  softmax_f32_kernel<D><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
-      (const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
-      (float*)o, g, l.batch, l.heads, tpf, scale * kLog2e);
+  if (R)
+    softmax_f32_kernel<D, 1><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
+        (const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
+        (float*)o, g, l.batch, l.heads, tpf, scale * kLog2e, R, gates, eps);
+  else
+    softmax_f32_kernel<D, 0><<<dim3((unsigned)grid), dim3(512), 0, s>>>(
+        (const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
+        (float*)o, g, l.batch, l.heads, tpf, scale * kLog2e, nullptr, nullptr, 0.f);
   return hipGetLastError();
 }
 
@@ -1255,6 +1313,23 @@ hipError_t launch_softmax_merge_train(const void* q, const void* k, const void* 
     case 128: return launch_mfma<128>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
     case 64: return launch_mfma<64>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
     case 32: return launch_mfma<32>(q, k, v, tk, tv, l, scale, o, ws, R, gates, eps, 5, s, io);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool softmax_merge_f32_fusable(const vdn_layout_t& l) {
+  return l.dtype == VDN_F32 && l.head_dim_k >= 32;
+}
+
+hipError_t launch_softmax_merge_f32(const void* q, const void* k, const void* v, const void* tk,
+                                    const void* tv, const float* R, const float* gates,
+                                    const vdn_layout_t& l, float scale, float eps, void* o,
+                                    hipStream_t s) {
+  if (!softmax_merge_f32_fusable(l)) return hipErrorNotSupported;
+  switch (l.head_dim_k) {
+    case 128: return launch_f32<128>(q, k, v, tk, tv, l, scale, o, s, R, gates, eps);
+    case 64: return launch_f32<64>(q, k, v, tk, tv, l, scale, o, s, R, gates, eps);
+    case 32: return launch_f32<32>(q, k, v, tk, tv, l, scale, o, s, R, gates, eps);
   }
   return hipErrorInvalidValue;
 }

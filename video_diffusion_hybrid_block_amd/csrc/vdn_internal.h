@@ -238,6 +238,13 @@ hipError_t launch_merge(const void* q, const void* o_soft, const float* R, const
 // o = sigmoid(g0) softmax + sigmoid(g1) RMSNorm(R q), or with `split` the two
 // gated branches side by side, o [B][N][2][H][d] (softmax branch first).
 bool softmax_merge_fusable(const vdn_layout_t& l);
+// fp32 layouts, d >= 32: the softmax on fp32 MFMA with the merge in its
+// epilogue, o [B][N][H][d] fp32.
+bool softmax_merge_f32_fusable(const vdn_layout_t& l);
+hipError_t launch_softmax_merge_f32(const void* q, const void* k, const void* v, const void* tk,
+                                    const void* tv, const float* R, const float* gates,
+                                    const vdn_layout_t& l, float scale, float eps, void* o,
+                                    hipStream_t s);
 // vt_ready: ws already holds the V^T copy (written by launch_vda_stats).
 hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, const void* tk,
                                 const void* tv, const float* R, const float* gates,

@@ -11,7 +11,8 @@ throughput in video tokens/s (warm; cold runs with the caches flushed are
 reported beside it), the roofline of the dominant kernel (the fused softmax +
 merge, launched alone as the layer's second stage and timed with HIP events
 on its stream), the VDA branch against the HBM roof, the same layer on the
-long (120-frame) and the stress (batch 2, ill-conditioned) shapes, and the
+long (120-frame) and the stress (batch 2, ill-conditioned) shapes, an fp32
+layer on the fp32 matrix cores (4 heads, 20 frames of the 768p frame), and the
 CPU oracle timed on a bounded sample of the 768p workload.  It also times the
 layer followed by the two branches' separate output projections (d_model =
 H*d), the projection product alone and the library matmul on the same
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k1_softmax_768p_hbm_traffic.md")
 VDA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vda_branch_768p_hbm_traffic.md")
 VDA_SOURCES = ["video_diffusion_hybrid_block_amd/csrc/k_vda_stats.hip",
@@ -214,6 +216,44 @@ def time_calls(fn, steps, warmup, stream, flush=None):
         out["cold_median"] = cold[len(cold) // 2]
         out["cold_min"] = cold[0]
     return out
+
+
+def fp32_figures(steps, warmup):
+    """An fp32 layer (softmax with the fused merge, statistics and scan on the
+    fp32 matrix cores): the whole layer and the softmax alone
+    (vdn_softmax_fwd), which carries the layer's flops."""
+    import torch
+
+    from video_diffusion_hybrid_block_amd import binding as V
+    from video_diffusion_hybrid_block_amd import synth
+    w = synth.Workload("fp32_4h_20f", 1, 4, 128, 20, 1008, 512, "f32", 2024, chunk_frames=5,
+                       window_chunks=1)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    dev = {k: torch.from_numpy(a).float().cuda() for k, a in inp.items()}
+    geo = dict(frames=w.frames, tokens_per_frame=w.tokens_per_frame, chunk_frames=w.chunk_frames,
+               window_chunks=w.window_chunks)
+    out = torch.empty_like(dev["q"])
+    o_soft = torch.empty_like(dev["q"])
+
+    def layer():
+        V.hybrid_attn(dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["beta"],
+                      dev["alpha"], dev["gate_logits"], **geo, out=out)
+
+    def softmax():
+        V.softmax_fwd(dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], **geo, out=o_soft)
+
+    stream = torch.cuda.current_stream()
+    lay_t = time_calls(layer, steps, warmup, stream)
+    sm_t = time_calls(softmax, steps, 2, stream)
+    fl = softmax_flops(w)
+    return {"workload": f"B={w.batch} H={w.heads} d={w.head_dim} T={w.frames} "
+                        f"P={w.tokens_per_frame} L={w.text_tokens} fp32",
+            "layer_ms": round(lay_t["mean"], 4),
+            "video_tokens_per_s": round(w.batch * w.video_tokens / (lay_t["mean"] / 1e3), 1),
+            "softmax_ms": round(sm_t["mean"], 4),
+            "softmax_tflops": round(fl / (sm_t["mean"] / 1e3) / 1e12, 1),
+            "softmax_frac_fp32_peak": round(fl / (sm_t["mean"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
 
 
 def layer_figures(w, steps, warmup, flush=None, keep=False):
@@ -501,6 +541,8 @@ def main():
                 "softmax_frac_bf16_peak": round(xfl / (f["k1"]["mean"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "vda_ms": round(f["vda"]["mean"], 4),
                 "vda_frac_hbm": round(vda_bytes(xw) / (f["vda"]["mean"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+        torch.cuda.empty_cache()
+        extra["fp32_4h_20f"] = fp32_figures(max(5, args.steps // 4), 2)
 
     video_tokens = w.batch * w.video_tokens
     value = video_tokens / (ms / 1e3)

@@ -483,7 +483,14 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
     if (it + 1 < ntiles) issue(it + 1, (it + 1) & 1);
     const char VDN_LDS* bb = lds + (it & 1) * BUFB;
-    const int lim = (partial && it == ntiles - 1) ? sgpr(nq - it * BM) - half * 8 : BM;
+    if (partial && it == ntiles - 1) {
+      // queries past the end read log-sum-exp +inf, so their P (and dS)
+      // vanish without a per-score mask
+      const int nv = nq - it * BM;
+      if ((int)threadIdx.x < BM && (int)threadIdx.x >= nv)
+        ((float VDN_LDS*)(lds + (it & 1) * BUFB + SOFF))[threadIdx.x] = INFINITY;
+      __syncthreads();
+    }
     bf16x8 pk[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -497,9 +504,6 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           dp = mfma32(df, vreg[ks], dp);
         }
       }
-#pragma unroll
-      for (int jr = 0; jr < 16; ++jr)
-        if (qb * 32 + ((jr >> 3) << 4) + (jr & 7) >= lim) s[jr] = -INFINITY;
       // register jr holds query qb*32 + 16*(jr/8) + 8*half + jr%8
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {

@@ -5,6 +5,8 @@
 //   dP_ij = dO_s,i . v_j,   dS_ij = P_ij (dP_ij - D_i),
 //   dq_i += scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
 //   dv_j = sum_i P_ij dO_s,i.
+// The forward's merge backward stores -D_i, and dP_ij - D_i accumulates on
+// the MFMA starting from it (no subtraction per score).
 // The keys query frame t sees are the video tokens of its visible frames and
 // the text; since frame t sees frame f exactly when f sees t, the queries that
 // see key frame f are the tokens of f's own visible frames (text keys: every
@@ -163,7 +165,11 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     dreg[ks] = *(const bf16x8*)(dos + qoff + ks * 16 + half * 8);
   }
   const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-  const float lq = lse[ri], Dq = dvec[ri];
+  const float lq = lse[ri];
+  // dvec holds -D: dP - D accumulates on the MFMA from a block of -D
+  f32x16 ndq;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ndq[e] = dvec[ri];
 
   const int HD = H * D;
   const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
@@ -243,7 +249,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         vf[ks] = *(const bf16x8 VDN_LDS*)(bb + VOFF + rread + kb * 32 * T::KST + ks * 32);
       }
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      dp[kb] = ndq;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         s[kb] = mfma32(kf[ks], qreg[ks], s[kb]);
@@ -264,7 +270,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float p = fast_exp2(fmaf(s[kb][j], c, -lq));
-        pk[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * (dp[kb][j] - Dq));
+        pk[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * dp[kb][j]);
       }
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp)
@@ -495,6 +501,21 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      if constexpr (PASS == 1) {
+        // -D of the block's query rows (register jr: query qb*32 + 16 (jr/8)
+        // + 8 half + jr%8): dP - D accumulates on the MFMA from it
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int q0 = qb * 32 + hh * 16 + half * 8;
+          const f32x4 d0 = *(const f32x4 VDN_LDS*)(bb + SOFF + 256 + q0 * 4);
+          const f32x4 d1 = *(const f32x4 VDN_LDS*)(bb + SOFF + 256 + q0 * 4 + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dp[hh * 8 + e] = d0[e];
+            dp[hh * 8 + 4 + e] = d1[e];
+          }
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 qf = *(const bf16x8 VDN_LDS*)(bb + rread + qb * 32 * T::KST + ks * 32);
@@ -515,13 +536,10 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk[qb * 2 + hh][e] = (bf16)fast_exp2(fmaf(s[hh * 8 + e], c, -lv[e]));
         } else {
-          const f32x4 d0 = *(const f32x4 VDN_LDS*)(bb + SOFF + 256 + q0 * 4);
-          const f32x4 d1 = *(const f32x4 VDN_LDS*)(bb + SOFF + 256 + q0 * 4 + 16);
-          const float dv8[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float p = fast_exp2(fmaf(s[hh * 8 + e], c, -lv[e]));
-            pk[qb * 2 + hh][e] = (bf16)(p * (dp[hh * 8 + e] - dv8[e]));
+            pk[qb * 2 + hh][e] = (bf16)(p * dp[hh * 8 + e]);
           }
         }
       }

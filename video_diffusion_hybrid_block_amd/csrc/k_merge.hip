@@ -167,7 +167,7 @@ hipError_t launch_valu(const void* q, const void* o_soft, const float* R, const 
 // Merge backward from saved residuals.  With s0, s1 the gate sigmoids, O_s
 // the softmax branch and n = RMSNorm(o_lin) = o_lin / r of one token-head:
 // dl0 = (dO . O_s) s0 (1 - s0), dl1 = (dO . n) s1 (1 - s1), dO_s = s0 dO
-// (bf16, the softmax backward's operand), D = dO_s . O_s, and through the
+// (bf16, the softmax backward's operand), -D (D = dO_s . O_s), and through the
 // normalisation do_lin = (s1 dO - n (s1 dO . n) / d) / r.  32 lanes per
 // token-head (d/32 consecutive values each, 16-byte loads for d = 128),
 // 8 token-heads per workgroup; HBM-bound.
@@ -222,7 +222,7 @@ merge_bwd_saved_kernel(const bf16* __restrict__ dO, const float* __restrict__ ga
   *(fv*)(dlin + off) = vl;
   if (l32 == 0) {
     *(float2*)(dgates + r * 2) = make_float2(dot0 * s0 * (1.0f - s0), dot1 * s1 * (1.0f - s1));
-    dvec[ri] = dsum;
+    dvec[ri] = -dsum;                       // -D: the backward's products start from it
   }
 }
 

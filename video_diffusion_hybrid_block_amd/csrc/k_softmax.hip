@@ -389,7 +389,7 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // output projections.  MODE 3 (backward pass) takes the upstream gradient dO
 // of the merged output instead and writes what the backward needs: the gate
 // logits' gradients, dO_soft = sigmoid(l0) dO (bf16), the row statistics of
-// the softmax (its log-sum-exp in exp2 units and D = dO_soft . O_soft) and
+// the softmax (its log-sum-exp in exp2 units and -D, D = dO_soft . O_soft) and
 // the gradient of the linear read before RMSNorm.  MODE 4 writes the two
 // gated branches of MODE 2 as MXFP8 codes and block scales (the activation
 // operand of the FP8 output projection), quantized from the fp32 values.
@@ -746,7 +746,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           const size_t gi = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2;
           *(float2*)(bio.dgates + gi) = make_float2(dot0 * s0 * (1.0f - s0), dot1 * s1 * (1.0f - s1));
           const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-          bio.dvec[ri] = dsum;
+          bio.dvec[ri] = -dsum;              // -D: the backward's products start from it
           bio.lse[ri] = lse2;
         }
       }

@@ -57,6 +57,9 @@ def test_validate_layout_error_codes():
     bad.softmax_scale = float("nan")
     assert V.validate_layout(bad) == 2
     assert V.validate_layout(_lay(frames=1 << 20, tokens_per_frame=1 << 12)) == 2
+    # token * H * d must stay below 2^31 within one batch element
+    assert V.validate_layout(_lay(frames=600, tokens_per_frame=1008)) == 0
+    assert V.validate_layout(_lay(frames=700, tokens_per_frame=1008)) == 2
     assert V.lib().vdn_validate_layout(None) == 1
 
 

@@ -95,6 +95,9 @@ vdn_status_t check_layout(const vdn_layout_t* l) {
   // grid sizes; element offsets are 64-bit.
   const long long N = (long long)l->frames * l->tokens_per_frame;
   if (N + l->text_tokens >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
+  // ... and a token's element offset within one batch element, token * H * d,
+  // is formed in 32 bits where a key tile's rows are resolved one by one
+  if ((N + l->text_tokens) * l->heads * (long long)d >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
   const long long bh = (long long)l->batch * l->heads;
   if (bh * l->frames * ((l->tokens_per_frame + 63) / 64) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;
   if (bh * (l->frames + 1) >= (1LL << 31)) return VDN_ERR_BAD_SHAPE;

@@ -501,15 +501,22 @@ def test_bitwise_deterministic_and_workspace_independent():
     assert torch.equal(a, b_) and torch.equal(a, c)
 
 
-def test_layer_replays_from_a_hip_graph_bit_exact():
+GRAPH_CASES = {"small_bf16": None,
+               "f32_graph": dict(name="f32_graph", batch=1, heads=2, head_dim=128, frames=10,
+                                 tokens_per_frame=64, text_tokens=16, dtype="f32")}
+
+
+@pytest.mark.parametrize("wname", list(GRAPH_CASES))
+def test_layer_replays_from_a_hip_graph_bit_exact(wname):
     """The layer enqueues only kernels on the caller's stream (no memset, no
     allocation, no host synchronisation), so it can be captured into a HIP
     graph.  Three replays, with eager layer calls on other inputs and host
     synchronisations between them, each reproduce the eager output bit for
-    bit, and the eager calls in between are unaffected."""
+    bit, and the eager calls in between are unaffected (bf16 and fp32
+    kernels)."""
     require_gpu()
-    w = workload("small_bf16")
-    _announce("graph capture small_bf16")
+    w = workload(wname) if GRAPH_CASES[wname] is None else custom(**GRAPH_CASES[wname])
+    _announce(f"graph capture {wname}")
     inp = synth.make_inputs(w)
     dev = to_dev(inp, w.dtype)
     other = dict(dev)
@@ -517,7 +524,7 @@ def test_layer_replays_from_a_hip_graph_bit_exact():
     ref = run_layer(w, dev).clone()
     ref_other = run_layer(w, other).clone()
     lay = V.make_layout(batch=w.batch, heads=w.heads, head_dim=w.head_dim, frames=w.frames,
-                        tokens_per_frame=w.tokens_per_frame, text_tokens=w.text_tokens, dtype="bf16")
+                        tokens_per_frame=w.tokens_per_frame, text_tokens=w.text_tokens, dtype=w.dtype)
     ws = torch.empty(V.workspace_size(lay), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dev["q"])
     side = torch.cuda.Stream()

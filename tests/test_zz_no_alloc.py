@@ -43,6 +43,9 @@ CALLS = [
          text_tokens=64, dtype="bf16", seed=31),
     dict(name="noalloc_b", batch=2, heads=3, head_dim=128, frames=9, tokens_per_frame=48,
          text_tokens=16, dtype="bf16", chunk_frames=2, seed=32),
+    # fp32: the fp32 matrix-core kernels on the same scratch, smaller again
+    dict(name="noalloc_c", batch=1, heads=2, head_dim=128, frames=7, tokens_per_frame=40,
+         text_tokens=8, dtype="f32", chunk_frames=2, seed=33),
 ]
 
 

@@ -19,6 +19,12 @@ from _helpers import custom, oracle_layout, rel_err, require_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+# Saved-residual backward against the recomputing one: the two compute D =
+# dO_s . O_s in different summation orders (about 1e-7 relative), and dS is
+# rounded to bf16 before the dq and dk products, so that difference flips
+# the rounding of an occasional dS element; one flip moves dq or dk by about
+# 1e-5 of its norm at these sizes.  A wrong residual moves them by far more.
+TRAIN_TOL = 1e-4
 
 CASES = [
     # far frames on both sides, anchors, text; two 256-query tiles per frame
@@ -150,7 +156,7 @@ def test_training_pair_matches_recompute_and_oracle(case):
     """vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: the output is
     vdn_hybrid_attn_fwd's bit for bit; the gradients equal
     vdn_hybrid_attn_bwd's up to the summation order of the merge backward's
-    dot products (bound 1e-5) and meet the oracle bound.  Layouts: d = 64
+    dot products (TRAIN_TOL) and meet the oracle bound.  Layouts: d = 64
     with text, d = 128 with batch 2 and a ragged tile, d = 32 without text,
     the softmax branch gated off, one frame."""
     require_gpu()
@@ -183,7 +189,7 @@ def test_training_pair_matches_recompute_and_oracle(case):
     errs = _grads_close(g_saved, g_re)
     print(case["name"], "saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
           flush=True)
-    bad = {k_: e for k_, e in errs.items() if not e <= 1e-5}
+    bad = {k_: e for k_, e in errs.items() if not e <= TRAIN_TOL}
     assert not bad, bad
     ref = G.hybrid_attn_grad({k_: np.asarray(a, np.float64) for k_, a in inp.items()}, lay, dO)
     oerr = {}
@@ -201,7 +207,7 @@ def test_training_pair_matches_recompute_and_oracle(case):
 def test_training_pair_768p_matches_recompute():
     """The 768p layer in the launch configuration bench.py times: every
     gradient of the saved-residual backward against the recomputing backward
-    over all heads (bound 1e-5), and the output bit for bit."""
+    over all heads (TRAIN_TOL), and the output bit for bit."""
     require_gpu()
     from _helpers import workload
     w = workload("768p")
@@ -225,7 +231,7 @@ def test_training_pair_768p_matches_recompute():
     errs = _grads_close(g_saved, g_re)
     print("768p saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
           flush=True)
-    bad = {k_: e for k_, e in errs.items() if not e <= 1e-5}
+    bad = {k_: e for k_, e in errs.items() if not e <= TRAIN_TOL}
     assert not bad, bad
 
 

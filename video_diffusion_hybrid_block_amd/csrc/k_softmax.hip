@@ -382,6 +382,12 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //    MFMA / VALU work instead of stalling each MFMA pair.
 //  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
 //    both read with ds_read_b128 at base + immediate, conflict-free.
+//  * q is multiplied by scale * log2(e) and rounded to bf16 once per work
+//    item, and each score chain starts from -m (the query's exponent offset)
+//    instead of 0, so the MFMAs leave s * scale * log2(e) - m and the weights
+//    are one v_exp_f32 each: no FMA per score.  The rounding of the scaled q
+//    is of the same size as the bf16 rounding of the weights the P V product
+//    takes.  The linear read R q uses q as given (reloaded in the epilogue).
 // MODE 0 writes the softmax branch O_soft; MODE 1 the merged output
 // sigmoid(l0) O_soft + sigmoid(l1) RMSNorm(R q); MODE 2 the two gated branches
 // side by side, o[b][n][0][h][:] = sigmoid(l0) O_soft and
@@ -436,9 +442,13 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bool qvalid = qlocal < g.P;
   const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
   const size_t qoff = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * D;
-  bf16x8 qreg[D / 16];
+  bf16x8 qreg[D / 16];   // the scores' B operand: q * c in bf16
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 x = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qreg[ks][e] = (bf16)((float)x[e] * c);
+  }
 
   const int HD = H * D;
   const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
@@ -489,8 +499,20 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                         : (const void*)((txt ? tkbh : kbh) + (size_t)(kb0 + dl) * HD));
 #pragma unroll
       for (int i = 0; i < NIW; ++i)
-        if (i < NIW - 1 || full) g2lds16(base + offb[i], bb + ldsb[i]);
+        if (i < NIW - 1 || full) {
+          // the first copy waits for the base (written by v_readfirstlane);
+          // the others only for their M0 write
+          if (i == 0) dma16s(base, offb[i], bb + ldsb[i]);
+          else asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                            :: "v"(offb[i]), "s"(base),
+                               "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(bb + ldsb[i])))
+                            : "memory");
+        }
     } else {
+      // tiles over a segment boundary (rare): the bases are re-read from
+      // SGPRs here, so no VGPR copies of them stay live across the loop
+      const bf16 *kbs = kbh, *tkbs = tkbh, *vtbs = vtbh;
+      asm volatile("" : "+s"(kbs), "+s"(tkbs), "+s"(vtbs));
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         if (i == NIW - 1 && !full) break;
@@ -500,13 +522,13 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           const int r = key_row(ka, kb0 + imin(jj / KSL, BN - 1));
           const bool txt = (r & 0x40000000) != 0;
           const size_t eo = (size_t)(unsigned)((r & 0x3FFFFFFF) * HD) + imin(jj % KSL, KCH - 1) * 8;
-          g2lds16((txt ? tkbh : kbh) + eo, bb + ldsb[i]);
+          g2lds16((txt ? tkbs : kbs) + eo, bb + ldsb[i]);
         } else {
           const int jj = (blk < VBLK ? blk : 0) * 64 + lane;
           const int d = imin(jj / VSL, D - 1);
           const int r = key_row(ka, kb0 + imin(jj % VSL, BN / 8 - 1) * 8);   // 8 keys, one segment
           const int tok = (r & 0x3FFFFFFF) + ((r & 0x40000000) ? N : 0);
-          g2lds16(vtbh + ((size_t)d * nl8 + tok), bb + ldsb[i]);
+          g2lds16(vtbs + ((size_t)d * nl8 + tok), bb + ldsb[i]);
         }
       }
     }
@@ -515,9 +537,11 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int kread = perm32(lane & 31) * KST + half * 16;
   const int vread = VOFF + (lane & 31) * VST + half * 16;
   const bool partial = (nkeys & (BN - 1)) != 0;
-  const float thr = 8.0f / c;   // lazy-rescale margin in score units
 
-  float m_run = -1e30f, m_thr = -1e30f, l_run = 0.f;
+  // m_run: the query's exponent offset (exp2 units); minit: -m_run in every
+  // element, the first score MFMA's accumulator input
+  float m_run = 0.f, l_run = 0.f;
+  f32x16 minit = {};
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -535,14 +559,22 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kf[kb][ks] = *(const bf16x8 VDN_LDS*)(kt + kb * 32 * KST + ks * 32);
+    // first step of both chains from minit, written as asm: from the builtin
+    // the compiler ties one chain's accumulator to its input and copies minit
+    // into it every tile (8 moves); the two products are independent and the
+    // next MFMAs read their results as accumulator inputs, which needs no
+    // wait states
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %5\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %5\n\t"
+                 "s_nop 1"
+                 : "=&v"(s[0]), "=&v"(s[1])
+                 : "v"(kf[0][0]), "v"(kf[1][0]), "v"(qreg[0]), "v"(minit));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 1; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ks], qreg[ks], s[kb]);
     __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8 - 2, 0);
   };
   // Online softmax of tile `it` (scores s, buffer buf) and O^T += V^T P^T.
   auto soft_pv = [&](int it, int buf, f32x16 (&s)[2]) {
@@ -574,22 +606,25 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     float mx = max3_raw(max3_raw(ma, mb, s[0][15]), s[1][15], s[1][15]);
     mx = xhalf_max_raw(mx);
     // Lazy rescale: the exponent offset moves only when some query's max
-    // grows by more than 2^8 (exp2 units); until then p <= 256.
-    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = fast_exp2((m_run - m_new) * c);
+    // passes it by more than 8 (exp2 units); until then p <= 256.  The first
+    // tile sets it to the tile's max.
+    if (__builtin_amdgcn_ballot_w64(mx > 8.0f) != 0 || it == 0) {
+      const float dl = it == 0 ? mx : fmaxf(mx, 0.f);
+      const float corr = it == 0 ? 0.f : fast_exp2(-dl);
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
-      m_run = m_new;
-      m_thr = m_new + thr;
+      m_run += dl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] -= dl;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) minit[j] = -m_run;
     }
-    const float mc = m_run * c;
     bf16x8 pk[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(s[kb][j], c, -mc));
+      for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(s[kb][j]);
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
       const bf16x2* p2 = (const bf16x2*)&pk[sp];
@@ -645,6 +680,14 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // all global loads of the epilogue first: gate logits and this thread's
     // share of R (NR chunks of 8 floats)
     const float2 gl = *(const float2*)(gates + ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2);
+    {
+      // reload the unscaled q (the asm keeps the compiler from reusing the
+      // first load's registers across the loop)
+      const bf16* qr = q;
+      asm volatile("" : "+s"(qr));
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *(const bf16x8*)(qr + qoff + ks * 16 + half * 8);
+    }
     constexpr int NR = (D * D / 8 + NW * 64 - 1) / (NW * 64);
     float4 xr[NR][2];
 #pragma unroll
@@ -721,7 +764,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dot0 = xhalf_sum(dot0);
       dot1 = xhalf_sum(dot1);
       dsum = xhalf_sum(dsum);
-      const float lse2 = fmaf(m_run, c, __log2f(1.0f / inv));
+      const float lse2 = m_run + __log2f(1.0f / inv);
       if (qvalid) {
         bf16* dosrow = bio.dos + qoff;
         float* dlrow = bio.dlin + qoff;
@@ -777,7 +820,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
         if (half == 0) {
           const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-          bio.lse[ri] = fmaf(m_run, c, __log2f(1.0f / inv));
+          bio.lse[ri] = m_run + __log2f(1.0f / inv);
           bio.rinv[ri] = rinv;
         }
       }

@@ -499,7 +499,7 @@ namespace {
 // their gradients, the read-slot gradients, transposed copies and the merge
 // backward's outputs.
 struct BwdPlan {
-  size_t states, dspost, dR, dRp, kt, qt, dost, dos, dlin, lse, dvec, total;
+  size_t states, dspost, dR, dRp, kt, qt, dost, dos, dlin, nlse, dvec, total;
 };
 
 BwdPlan make_bwd_plan(const vdn_layout_t& l) {
@@ -519,8 +519,8 @@ BwdPlan make_bwd_plan(const vdn_layout_t& l) {
   b.dost = align256(b.qt + bh * d * nq8 * 2);
   b.dos = align256(b.dost + bh * d * nq8 * 2);
   b.dlin = align256(b.dos + (size_t)l.batch * N * l.heads * d * 2);
-  b.lse = align256(b.dlin + (size_t)l.batch * N * l.heads * d * 4);
-  b.dvec = align256(b.lse + bh * N * 4);
+  b.nlse = align256(b.dlin + (size_t)l.batch * N * l.heads * d * 4);
+  b.dvec = align256(b.nlse + bh * N * 4);
   b.total = align256(b.dvec + bh * N * 4);
   return b;
 }
@@ -545,7 +545,7 @@ extern "C" {
 
 namespace {
 
-// The backward after the merge backward (whose dos, dlin, lse and dvec sit in
+// The backward after the merge backward (whose dos, dlin, nlse and dvec sit in
 // the backward plan's buffers, beside the statistics, factor, read slots and
 // per-step states of the forward): transposed copies, the linear branch's
 // backward, the statistics backward, then the softmax backward.
@@ -563,7 +563,7 @@ hipError_t bwd_tail(const void* q, const void* k, const void* v, const void* tex
   float* states = (float*)(ws + bp.states);
   __bf16* dos = (__bf16*)(ws + bp.dos);
   float* dlin = (float*)(ws + bp.dlin);
-  float* lse = (float*)(ws + bp.lse);
+  float* nlse = (float*)(ws + bp.nlse);
   float* dvec = (float*)(ws + bp.dvec);
   // transposed copies for the softmax backward
   hipError_t e =
@@ -583,13 +583,13 @@ hipError_t bwd_tail(const void* q, const void* k, const void* v, const void* tex
                         stream));
   // softmax branch: dq, dk, dv, dtext_k, dtext_v (added)
   if (e == hipSuccess)
-    e = VDN_STAGE("attn_bwd", launch_attn_bwd(q, k, v, text_k, text_v, dos, lse, dvec, ws + bp.kt, ws + bp.qt,
+    e = VDN_STAGE("attn_bwd", launch_attn_bwd(q, k, v, text_k, text_v, dos, nlse, dvec, ws + bp.kt, ws + bp.qt,
                         ws + bp.dost, l, eff_scale(l), dq, dk, dv, dtext_k, dtext_v, stream));
   return e;
 }
 
 // Saved residuals of the training pair: the backward plan (whose statistics,
-// factor, read slots, per-step states and lse buffers the training forward
+// factor, read slots, per-step states and nlse buffers the training forward
 // fills), then O_soft and RMSNorm(R q) (fp32, [B,N,H,d] each) and 1/r
 // ([B,H,N] fp32).
 struct TrainPlan {
@@ -663,14 +663,14 @@ vdn_status_t vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, co
   float* states = (float*)(ws + bp.states);
   __bf16* dos = (__bf16*)(ws + bp.dos);
   float* dlin = (float*)(ws + bp.dlin);
-  float* lse = (float*)(ws + bp.lse);
+  float* nlse = (float*)(ws + bp.nlse);
   float* dvec = (float*)(ws + bp.dvec);
   // forward recomputation: statistics, factor, scan (keeping every state)
   hipError_t e = VDN_STAGE("gram", launch_gram(k, v, text_k, text_v, beta, l, false, A, B, stream));
   if (e == hipSuccess) e = VDN_STAGE("factor", launch_factor(A, l, false, stream));
   if (e == hipSuccess) e = VDN_STAGE("scan", launch_scan(A, B, alpha, l, Sf, Sb, R, stream, states));
   // softmax forward with the merge backward in its epilogue
-  const EpilogueIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, lse};
+  const EpilogueIO io{(const __bf16*)dO, dgate_logits, dos, dlin, dvec, nlse};
   if (e == hipSuccess)
     e = VDN_STAGE("softmax_merge_bwd", launch_softmax_merge_bwd(q, k, v, text_k, text_v, R, gate_logits, l, eff_scale(l),
                                  eff_eps(l), io, ws + p.vt_off, stream));
@@ -715,7 +715,7 @@ vdn_status_t vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void*
     e = VDN_STAGE("scan", launch_scan(A, B, alpha, l, (float*)(ws + p.sf_off), (float*)(ws + p.sb_off), R, stream,
                     (float*)(ws + bp.states)));
   EpilogueIO io{};
-  io.lse = (float*)(ws + bp.lse);
+  io.nlse = (float*)(ws + bp.nlse);
   io.o_soft = (float*)(ws + tp.o_soft);
   io.o_lin = (float*)(ws + tp.o_lin);
   io.rinv = (float*)(ws + tp.rinv);

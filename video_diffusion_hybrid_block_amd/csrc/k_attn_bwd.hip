@@ -20,15 +20,20 @@
 //    32 queries, one lane per query) and key walk.  Per 64-key tile:
 //    S^T = K Q^T and dP^T = V dO_s^T on v_mfma_f32_32x32x16_bf16 (Q^T and
 //    dO_s^T stay in registers), P^T = exp2(scale log2e S^T - lse) with the
-//    forward's log-sum-exp, dS^T lane-local, dq^T += K^T dS^T.  K rows are
+//    forward's log-sum-exp, dS^T lane-local, dq^T += K^T dS^T.  As in the
+//    forward, q is pre-scaled by scale log2e in bf16 (the forward's score
+//    operand exactly, so P matches the forward's weights) and the score
+//    chains start from -lse: P^T is one exp2 per score.  K rows are
 //    permuted inside 32-key blocks so the dS^T registers are the B operand of
 //    the last product; K^T comes from a transposed copy.
 //  * dk/dv kernel: 256 keys of one frame (or text) per workgroup, 8 waves x 32
 //    keys, one lane per key (K^T, V^T in registers), walking the 64-query tiles
 //    that see them twice: S = Q K^T, dv^T += dO_s^T P in one pass;
 //    S, dP = dO_s V^T, dk^T += Q^T dS in the other, with Q / dO_s rows permuted
-//    the same way and Q^T / dO_s^T from transposed copies; the tile's lse and D
-//    ride along in one more direct-to-LDS block.
+//    the same way and Q^T / dO_s^T from transposed copies; the tile's -lse and -D
+//    ride along in one more direct-to-LDS block and start the score and dP
+//    accumulators.  Here k is the operand in registers, so it is the one
+//    pre-scaled by scale log2e (in bf16).
 //  * Tiles move with 16-byte direct-to-LDS loads into two buffers (the next
 //    tile in flight during this one); rows padded to 2d+16 bytes and
 //    transposed rows to 144 bytes so every ds_read_b128 is conflict-free.
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(512)
 attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const bf16* __restrict__ v, const bf16* __restrict__ tk,
                    const bf16* __restrict__ tv, const bf16* __restrict__ dos,
-                   const float* __restrict__ lse, const float* __restrict__ dvec,
+                   const float* __restrict__ nlse, const float* __restrict__ dvec,
                    const bf16* __restrict__ kt, int nl8, float* __restrict__ dq, Geo g, int B,
                    int H, int tpf, float c, float scale) {
   using T = BT<D>;
@@ -161,15 +166,20 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16x8 qreg[D / 16], dreg[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+    const bf16x8 x = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qreg[ks][e] = (bf16)((float)x[e] * c);
     dreg[ks] = *(const bf16x8*)(dos + qoff + ks * 16 + half * 8);
   }
   const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-  const float lq = lse[ri];
-  // dvec holds -D: dP - D accumulates on the MFMA from a block of -D
-  f32x16 ndq;
+  // nlse and dvec hold -lse and -D: c s - lse and dP - D accumulate on the
+  // MFMAs from blocks of them
+  f32x16 nlq, ndq;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) ndq[e] = dvec[ri];
+  for (int e = 0; e < 16; ++e) {
+    nlq[e] = nlse[ri];
+    ndq[e] = dvec[ri];
+  }
 
   const int HD = H * D;
   const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
@@ -248,7 +258,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         kf[ks] = *(const bf16x8 VDN_LDS*)(bb + rread + kb * 32 * T::KST + ks * 32);
         vf[ks] = *(const bf16x8 VDN_LDS*)(bb + VOFF + rread + kb * 32 * T::KST + ks * 32);
       }
-      s[kb] = f32x16{};
+      s[kb] = nlq;
       dp[kb] = ndq;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -269,7 +279,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(fmaf(s[kb][j], c, -lq));
+        const float p = fast_exp2(s[kb][j]);
         pk[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * dp[kb][j]);
       }
 #pragma unroll
@@ -300,7 +310,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 // ---------------------------------------------------------------------------
 // Two passes over the query tiles, 8 waves x 32 keys = 256 keys per
 // workgroup, two waves per SIMD.  PASS 0 accumulates dv^T += dO_s^T P (needs
-// Q rows, dO_s^T, lse); PASS 1 dk^T += Q^T dS (Q rows, dO_s rows, Q^T, lse, D).
+// Q rows, dO_s^T, nlse); PASS 1 dk^T += Q^T dS (Q rows, dO_s rows, Q^T, nlse, D).
 // Both add to dk / dv, which already hold the statistics' part.
 // Each pass holds one d x 32 accumulator per lane, so it fits two waves per
 // SIMD, and every query tile it streams serves 256 keys.  (A single pass
@@ -312,14 +322,14 @@ __global__ void __launch_bounds__(512)
 attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const bf16* __restrict__ tk,
                      const bf16* __restrict__ tv, const bf16* __restrict__ dos,
-                     const float* __restrict__ lse, const float* __restrict__ dvec,
+                     const float* __restrict__ nlse, const float* __restrict__ dvec,
                      const bf16* __restrict__ qt, const bf16* __restrict__ dost, int nq8,
                      float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtk,
                      float* __restrict__ dtv, Geo g, int B, int H, int tpk, int ntx, float c,
                      float scale) {
   using T = BT<D>;
   constexpr int NW = 8, BM = 64;
-  // blocks: Q rows, [dO_s rows], transposed tile (dO_s^T or Q^T), lse / D
+  // blocks: Q rows, [dO_s rows], transposed tile (dO_s^T or Q^T), nlse / D
   constexpr int DOFF = T::RBLK * 1024;
   constexpr int TOFF = (PASS == 0 ? 1 : 2) * T::RBLK * 1024;
   constexpr int SOFF = TOFF + T::TBLK * 1024;
@@ -375,7 +385,11 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16x8 kreg[D / 16], vreg[PASS == 1 ? D / 16 : 1];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    kreg[ks] = *(const bf16x8*)((text ? tk : k) + koff + ks * 16 + half * 8);
+    {
+      const bf16x8 x = *(const bf16x8*)((text ? tk : k) + koff + ks * 16 + half * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kreg[ks][e] = (bf16)((float)x[e] * c);
+    }
     if constexpr (PASS == 1) vreg[ks] = *(const bf16x8*)((text ? tv : v) + koff + ks * 16 + half * 8);
   }
 
@@ -383,12 +397,12 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bf16* qbh = q + ((size_t)b * N * H + h) * D;
   const bf16* dbh = dos + ((size_t)b * N * H + h) * D;
   const bf16* trbh = (PASS == 0 ? dost : qt) + ((size_t)b * H + h) * D * (size_t)nq8;
-  const float* lbh = lse + (size_t)(b * H + h) * N;
+  const float* lbh = nlse + (size_t)(b * H + h) * N;
   const float* dvbh = dvec + (size_t)(b * H + h) * N;
 
   const int ntiles = sgpr((nq + BM - 1) / BM);
   // Copy i of this wave fills block i * NW + wv: Q rows, [dO_s rows], the
-  // transposed tile, lse / D, or the spare block (a reload of Q block 0).
+  // transposed tile, nlse / D, or the spare block (a reload of Q block 0).
   uint32_t pk[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -490,17 +504,30 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (it + 1 < ntiles) issue(it + 1, (it + 1) & 1);
     const char VDN_LDS* bb = lds + (it & 1) * BUFB;
     if (partial && it == ntiles - 1) {
-      // queries past the end read log-sum-exp +inf, so their P (and dS)
-      // vanish without a per-score mask
+      // queries past the end read a negated log-sum-exp of -inf, so their P
+      // (and dS) vanish without a per-score mask
       const int nv = nq - it * BM;
       if ((int)threadIdx.x < BM && (int)threadIdx.x >= nv)
-        ((float VDN_LDS*)(lds + (it & 1) * BUFB + SOFF))[threadIdx.x] = INFINITY;
+        ((float VDN_LDS*)(lds + (it & 1) * BUFB + SOFF))[threadIdx.x] = -INFINITY;
       __syncthreads();
     }
     bf16x8 pk[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s, dp = f32x16{};
+      // -lse of the block's query rows (same register order as -D below):
+      // c s - lse accumulates on the MFMA from it
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int q0 = qb * 32 + hh * 16 + half * 8;
+        const f32x4 l0 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4);
+        const f32x4 l1 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4 + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[hh * 8 + e] = l0[e];
+          s[hh * 8 + 4 + e] = l1[e];
+        }
+      }
       if constexpr (PASS == 1) {
         // -D of the block's query rows (register jr: query qb*32 + 16 (jr/8)
         // + 8 half + jr%8): dP - D accumulates on the MFMA from it
@@ -528,17 +555,13 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // register jr holds query qb*32 + 16*(jr/8) + 8*half + jr%8
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int q0 = qb * 32 + hh * 16 + half * 8;
-        const f32x4 l0 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4);
-        const f32x4 l1 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4 + 16);
-        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
         if constexpr (PASS == 0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pk[qb * 2 + hh][e] = (bf16)fast_exp2(fmaf(s[hh * 8 + e], c, -lv[e]));
+          for (int e = 0; e < 8; ++e) pk[qb * 2 + hh][e] = (bf16)fast_exp2(s[hh * 8 + e]);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float p = fast_exp2(fmaf(s[hh * 8 + e], c, -lv[e]));
+            const float p = fast_exp2(s[hh * 8 + e]);
             pk[qb * 2 + hh][e] = (bf16)(p * dp[hh * 8 + e]);
           }
         }
@@ -570,7 +593,7 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, const void* tk, const void* tv,
-                    const void* dos, const float* lse, const float* dvec, const void* kt,
+                    const void* dos, const float* nlse, const float* dvec, const void* kt,
                     const void* qt, const void* dost, const vdn_layout_t& l, float scale,
                     float* dq, float* dk, float* dv, float* dtk, float* dtv, hipStream_t s) {
   Geo g = make_geo(l);
@@ -581,7 +604,7 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const void* tk,
   const int nl8 = (N + g.L + 7) / 8 * 8;
   attn_bwd_dq_kernel<D><<<dim3((unsigned)grid_q), dim3(512), 0, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
-      (const bf16*)dos, lse, dvec, (const bf16*)kt, nl8, dq, g, l.batch, l.heads, tpf, c, scale);
+      (const bf16*)dos, nlse, dvec, (const bf16*)kt, nl8, dq, g, l.batch, l.heads, tpf, c, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tpk = (g.P + 255) / 256;
@@ -590,13 +613,13 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const void* tk,
   const int nq8 = (N + 7) / 8 * 8;
   attn_bwd_dkv2_kernel<D, 0><<<dim3((unsigned)grid_k), dim3(512), 0, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
-      (const bf16*)dos, lse, dvec, (const bf16*)qt, (const bf16*)dost, nq8, dk, dv, dtk, dtv, g,
+      (const bf16*)dos, nlse, dvec, (const bf16*)qt, (const bf16*)dost, nq8, dk, dv, dtk, dtv, g,
       l.batch, l.heads, tpk, ntx, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_bwd_dkv2_kernel<D, 1><<<dim3((unsigned)grid_k), dim3(512), 0, s>>>(
       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)tk, (const bf16*)tv,
-      (const bf16*)dos, lse, dvec, (const bf16*)qt, (const bf16*)dost, nq8, dk, dv, dtk, dtv, g,
+      (const bf16*)dos, nlse, dvec, (const bf16*)qt, (const bf16*)dost, nq8, dk, dv, dtk, dtv, g,
       l.batch, l.heads, tpk, ntx, c, scale);
   return hipGetLastError();
 }
@@ -604,14 +627,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, const void* tk,
 }  // namespace
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* tk,
-                           const void* tv, const void* dos, const float* lse, const float* dvec,
+                           const void* tv, const void* dos, const float* nlse, const float* dvec,
                            const void* kt, const void* qt, const void* dost,
                            const vdn_layout_t& l, float scale, float* dq, float* dk, float* dv,
                            float* dtk, float* dtv, hipStream_t s) {
   switch (l.head_dim_k) {
-    case 128: return launch_d<128>(q, k, v, tk, tv, dos, lse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
-    case 64: return launch_d<64>(q, k, v, tk, tv, dos, lse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
-    case 32: return launch_d<32>(q, k, v, tk, tv, dos, lse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
+    case 128: return launch_d<128>(q, k, v, tk, tv, dos, nlse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
+    case 64: return launch_d<64>(q, k, v, tk, tv, dos, nlse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
+    case 32: return launch_d<32>(q, k, v, tk, tv, dos, nlse, dvec, kt, qt, dost, l, scale, dq, dk, dv, dtk, dtv, s);
   }
   return hipErrorInvalidValue;
 }

@@ -395,13 +395,14 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // output projections.  MODE 3 (backward pass) takes the upstream gradient dO
 // of the merged output instead and writes what the backward needs: the gate
 // logits' gradients, dO_soft = sigmoid(l0) dO (bf16), the row statistics of
-// the softmax (its log-sum-exp in exp2 units and -D, D = dO_soft . O_soft) and
+// the softmax (its log-sum-exp in exp2 units and D = dO_soft . O_soft, both
+// negated) and
 // the gradient of the linear read before RMSNorm.  MODE 4 writes the two
 // gated branches of MODE 2 as MXFP8 codes and block scales (the activation
 // operand of the FP8 output projection), quantized from the fp32 values.
 // MODE 5 (training forward) writes MODE 1's output and keeps, for a later
-// backward, O_soft and n = RMSNorm(R q) in fp32 and per row the log-sum-exp
-// and the RMS factor 1/r.
+// backward, O_soft and n = RMSNorm(R q) in fp32 and per row the negated
+// log-sum-exp and the RMS factor 1/r.
 template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -764,7 +765,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dot0 = xhalf_sum(dot0);
       dot1 = xhalf_sum(dot1);
       dsum = xhalf_sum(dsum);
-      const float lse2 = m_run + __log2f(1.0f / inv);
+      const float nlse2 = -(m_run + __log2f(1.0f / inv));   // -lse
       if (qvalid) {
         bf16* dosrow = bio.dos + qoff;
         float* dlrow = bio.dlin + qoff;
@@ -790,7 +791,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           *(float2*)(bio.dgates + gi) = make_float2(dot0 * s0 * (1.0f - s0), dot1 * s1 * (1.0f - s1));
           const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
           bio.dvec[ri] = -dsum;              // -D: the backward's products start from it
-          bio.lse[ri] = lse2;
+          bio.nlse[ri] = nlse2;
         }
       }
       return;
@@ -799,8 +800,8 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if constexpr (MODE == 5) {
       // Training forward: besides the merged output, keep what the merge
       // backward needs: O_s = oacc * inv and n = lin * rinv (fp32, the
-      // layout of q), and per (b, h, token) the log-sum-exp in exp2 units
-      // and 1 / r.
+      // layout of q), and per (b, h, token) the negated log-sum-exp in exp2
+      // units and 1 / r.
       if (qvalid) {
         float* osrow = bio.o_soft + qoff;
         float* onrow = bio.o_lin + qoff;
@@ -820,7 +821,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
         if (half == 0) {
           const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-          bio.lse[ri] = m_run + __log2f(1.0f / inv);
+          bio.nlse[ri] = -(m_run + __log2f(1.0f / inv));
           bio.rinv[ri] = rinv;
         }
       }

@@ -254,26 +254,27 @@ hipError_t launch_softmax_merge(const void* q, const void* k, const void* v, con
 // Merge backward (backward pass): for every video token-head, dgates
 // [B,N,H,2] fp32, dos = sigmoid(l0) dO [B,N,H,d] bf16, dlin = gradient of the
 // linear read before RMSNorm [B,N,H,d] fp32, and per (b, h, token) the
-// softmax's log-sum-exp in exp2 units (lse) and D = dos . O_soft (dvec),
-// [B,H,N] fp32.
+// softmax's log-sum-exp in exp2 units, negated (nlse = -lse), and -D with
+// D = dos . O_soft (dvec), [B,H,N] fp32: the backward's score and dP
+// products start their accumulators from them.
 // MXFP8 branches: mx_scales [B*N][2*H*d/32] receives the E8M0 block scales
 // (the E4M3 codes go to the kernel's output pointer, [B*N][2*H*d] bytes).
 // Training forward: o_soft = O_soft and o_lin = RMSNorm(R q), [B,N,H,d] fp32,
-// and per (b, h, token) lse (as above) and rinv = 1 / r, [B,H,N] fp32.
+// and per (b, h, token) nlse (as above) and rinv = 1 / r, [B,H,N] fp32.
 struct EpilogueIO {
   const __bf16* dO;
   float* dgates;
   __bf16* dos;
   float* dlin;
   float* dvec;
-  float* lse;
+  float* nlse;
   uint8_t* mx_scales;
   float* o_soft;
   float* o_lin;
   float* rinv;
 };
 // Training forward: the merged output of launch_softmax_merge plus the
-// residuals named under EpilogueIO (o_soft, o_lin, lse, rinv).
+// residuals named under EpilogueIO (o_soft, o_lin, nlse, rinv).
 hipError_t launch_softmax_merge_train(const void* q, const void* k, const void* v,
                                       const void* tk, const void* tv, const float* R,
                                       const float* gates, const vdn_layout_t& l, float scale,
@@ -307,10 +308,10 @@ hipError_t launch_transpose(const void* x, const void* tx, int B, int H, int D, 
 // dq += scale * sum_j dS_ij k_j (dq fp32, already holding the linear read's
 // part), dk/dv and dtk/dtv (text keys) added (fp32, holding the statistics'
 // part from gram_bwd), from dos,
-// the row statistics lse/dvec, and transposed copies kt (keys + text), qt and
+// the row statistics nlse/dvec, and transposed copies kt (keys + text), qt and
 // dost (video tokens).
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* tk,
-                           const void* tv, const void* dos, const float* lse, const float* dvec,
+                           const void* tv, const void* dos, const float* nlse, const float* dvec,
                            const void* kt, const void* qt, const void* dost,
                            const vdn_layout_t& l, float scale, float* dq, float* dk, float* dv,
                            float* dtk, float* dtv, hipStream_t s);

@@ -507,8 +507,8 @@ def main():
             "bwd_saved_ms": round(t_ms - ft_ms, 3),
             "video_tokens_per_s": round(w.batch * w.video_tokens / (t_ms / 1e3), 1),
             "attention_tflops": round(aflops / (t_ms / 1e3) / 1e12, 1),
-            "note": "vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: forward (same "
-                    "output) keeping O_soft, RMSNorm(R q), lse, 1/r and the scan states; "
+            "note": "vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: forward (the layer "
+                    "output to rounding, exact fp32 scores) keeping O_soft, RMSNorm(R q), lse, 1/r and the scan states; "
                     "backward from them; 14d flops per visible pair over the pair"}
         del saved, o_t, dO
 

@@ -340,8 +340,11 @@ size_t vdn_hybrid_attn_train_saved_size(const vdn_layout_t* layout);
  * (the VDA statistics, factor, read slots and every scan state; the softmax
  * branch output, the RMS-normalised linear read and the RMS factor; the
  * softmax's log-sum-exp), so that vdn_hybrid_attn_bwd_saved skips the
- * recomputation.  o is the same output as vdn_hybrid_attn_fwd's, bit for
- * bit.  Covers the layouts vdn_hybrid_attn_bwd covers; else
+ * recomputation.  o is the layer output with the softmax scores formed
+ * exactly in float32 (the backward recomputes its weights from q and k as
+ * given); vdn_hybrid_attn_fwd forms them from q scaled and rounded to bf16,
+ * so the two outputs agree to rounding (about 1e-4 relative on unit keys),
+ * not bit for bit.  Covers the layouts vdn_hybrid_attn_bwd covers; else
  * VDN_ERR_UNSUPPORTED.  saved: device memory owned by the caller, at least
  * vdn_hybrid_attn_train_saved_size(layout) bytes, 256-byte aligned; it must
  * stay untouched until the matching vdn_hybrid_attn_bwd_saved call.

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import vdn_oracle as O
 from oracle import vdn_oracle_grad as G
 from video_diffusion_hybrid_block_amd import binding as V
 from video_diffusion_hybrid_block_amd import synth
@@ -25,6 +26,20 @@ TOL = 2e-2
 # the rounding of an occasional dS element; one flip moves dq or dk by about
 # 1e-5 of its norm at these sizes.  A wrong residual moves them by far more.
 TRAIN_TOL = 1e-4
+# The training forward forms its softmax scores exactly in fp32 (its
+# log-sum-exp drives the backward); the layer forms them from q * scale *
+# log2(e) rounded to bf16.  On unit keys against N(0, 1) queries the two
+# differ by ~1e-4 before the outputs are rounded to bf16, which then flips
+# the rounding of a few per cent of the elements by one bf16 step (2^-8
+# relative): up to ~2e-3 of the norm.  Both also meet the oracle bound.
+FWD_TOL = 5e-3
+
+
+def _out_close(o, o_ref):
+    d = float(torch.linalg.vector_norm((o.double() - o_ref.double()))
+              / torch.linalg.vector_norm(o_ref.double()))
+    print(f"training forward vs layer output: {d:.2e}", flush=True)
+    return d <= FWD_TOL
 
 CASES = [
     # far frames on both sides, anchors, text; two 256-query tiles per frame
@@ -154,7 +169,8 @@ TRAIN_CASES = [CASES[0], CASES[1], CASES[2], CASES[4], CASES[5]]
 @pytest.mark.parametrize("case", TRAIN_CASES, ids=[c["name"] for c in TRAIN_CASES])
 def test_training_pair_matches_recompute_and_oracle(case):
     """vdn_hybrid_attn_fwd_train + vdn_hybrid_attn_bwd_saved: the output is
-    vdn_hybrid_attn_fwd's bit for bit; the gradients equal
+    vdn_hybrid_attn_fwd's up to its score rounding (FWD_TOL) and meets the
+    oracle bound; the gradients equal
     vdn_hybrid_attn_bwd's up to the summation order of the merge backward's
     dot products (TRAIN_TOL) and meet the oracle bound.  Layouts: d = 64
     with text, d = 128 with batch 2 and a ragged tile, d = 32 without text,
@@ -185,7 +201,10 @@ def test_training_pair_matches_recompute_and_oracle(case):
     g_saved = V.hybrid_attn_bwd_saved(*args, dOd, saved, **geo)
     g_re = V.hybrid_attn_bwd(*args, dOd, **geo)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert _out_close(o, o_ref)
+    oe = rel_err(o.float().cpu().numpy(), O.hybrid_attn(inp, lay))
+    print(case["name"], f"training forward vs oracle {oe:.2e}", flush=True)
+    assert oe <= TOL
     errs = _grads_close(g_saved, g_re)
     print(case["name"], "saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
           flush=True)
@@ -207,7 +226,8 @@ def test_training_pair_matches_recompute_and_oracle(case):
 def test_training_pair_768p_matches_recompute():
     """The 768p layer in the launch configuration bench.py times: every
     gradient of the saved-residual backward against the recomputing backward
-    over all heads (TRAIN_TOL), and the output bit for bit."""
+    over all heads (TRAIN_TOL), and the output against the layer's
+    (FWD_TOL)."""
     require_gpu()
     from _helpers import workload
     w = workload("768p")
@@ -227,7 +247,7 @@ def test_training_pair_768p_matches_recompute():
     del saved
     g_re = V.hybrid_attn_bwd(*args, dOd, **geo)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    assert _out_close(o, o_ref)
     errs = _grads_close(g_saved, g_re)
     print("768p saved vs recompute", " ".join(f"{k_} {e:.1e}" for k_, e in errs.items()),
           flush=True)

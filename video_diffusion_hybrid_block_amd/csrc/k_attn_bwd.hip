@@ -20,10 +20,9 @@
 //    32 queries, one lane per query) and key walk.  Per 64-key tile:
 //    S^T = K Q^T and dP^T = V dO_s^T on v_mfma_f32_32x32x16_bf16 (Q^T and
 //    dO_s^T stay in registers), P^T = exp2(scale log2e S^T - lse) with the
-//    forward's log-sum-exp, dS^T lane-local, dq^T += K^T dS^T.  As in the
-//    forward, q is pre-scaled by scale log2e in bf16 (the forward's score
-//    operand exactly, so P matches the forward's weights) and the score
-//    chains start from -lse: P^T is one exp2 per score.  K rows are
+//    forward's log-sum-exp (stored negated), dS^T lane-local, dq^T += K^T dS^T.
+//    The scores are exact fp32 products of q and k as given, like the
+//    training forward's, so P is consistent with its log-sum-exp.  K rows are
 //    permuted inside 32-key blocks so the dS^T registers are the B operand of
 //    the last product; K^T comes from a transposed copy.
 //  * dk/dv kernel: 256 keys of one frame (or text) per workgroup, 8 waves x 32
@@ -31,9 +30,8 @@
 //    that see them twice: S = Q K^T, dv^T += dO_s^T P in one pass;
 //    S, dP = dO_s V^T, dk^T += Q^T dS in the other, with Q / dO_s rows permuted
 //    the same way and Q^T / dO_s^T from transposed copies; the tile's -lse and -D
-//    ride along in one more direct-to-LDS block and start the score and dP
-//    accumulators.  Here k is the operand in registers, so it is the one
-//    pre-scaled by scale log2e (in bf16).
+//    ride along in one more direct-to-LDS block (-D starts the dP
+//    accumulators).
 //  * Tiles move with 16-byte direct-to-LDS loads into two buffers (the next
 //    tile in flight during this one); rows padded to 2d+16 bytes and
 //    transposed rows to 144 bytes so every ds_read_b128 is conflict-free.
@@ -166,20 +164,15 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16x8 qreg[D / 16], dreg[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 x = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qreg[ks][e] = (bf16)((float)x[e] * c);
+    qreg[ks] = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
     dreg[ks] = *(const bf16x8*)(dos + qoff + ks * 16 + half * 8);
   }
   const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-  // nlse and dvec hold -lse and -D: c s - lse and dP - D accumulate on the
-  // MFMAs from blocks of them
-  f32x16 nlq, ndq;
+  const float nlq = nlse[ri];   // -lse
+  // dvec holds -D: dP - D accumulates on the MFMA from a block of -D
+  f32x16 ndq;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    nlq[e] = nlse[ri];
-    ndq[e] = dvec[ri];
-  }
+  for (int e = 0; e < 16; ++e) ndq[e] = dvec[ri];
 
   const int HD = H * D;
   const bf16* kbh = k + ((size_t)w.b * N * H + w.h) * D;
@@ -258,7 +251,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         kf[ks] = *(const bf16x8 VDN_LDS*)(bb + rread + kb * 32 * T::KST + ks * 32);
         vf[ks] = *(const bf16x8 VDN_LDS*)(bb + VOFF + rread + kb * 32 * T::KST + ks * 32);
       }
-      s[kb] = nlq;
+      s[kb] = f32x16{};
       dp[kb] = ndq;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -279,7 +272,7 @@ attn_bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(s[kb][j]);
+        const float p = fast_exp2(fmaf(s[kb][j], c, nlq));
         pk[kb * 2 + (j >> 3)][j & 7] = (bf16)(p * dp[kb][j]);
       }
 #pragma unroll
@@ -385,11 +378,7 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   bf16x8 kreg[D / 16], vreg[PASS == 1 ? D / 16 : 1];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    {
-      const bf16x8 x = *(const bf16x8*)((text ? tk : k) + koff + ks * 16 + half * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kreg[ks][e] = (bf16)((float)x[e] * c);
-    }
+    kreg[ks] = *(const bf16x8*)((text ? tk : k) + koff + ks * 16 + half * 8);
     if constexpr (PASS == 1) vreg[ks] = *(const bf16x8*)((text ? tv : v) + koff + ks * 16 + half * 8);
   }
 
@@ -514,20 +503,7 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     bf16x8 pk[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s, dp = f32x16{};
-      // -lse of the block's query rows (same register order as -D below):
-      // c s - lse accumulates on the MFMA from it
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int q0 = qb * 32 + hh * 16 + half * 8;
-        const f32x4 l0 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4);
-        const f32x4 l1 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4 + 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[hh * 8 + e] = l0[e];
-          s[hh * 8 + 4 + e] = l1[e];
-        }
-      }
+      f32x16 s = f32x16{}, dp = f32x16{};
       if constexpr (PASS == 1) {
         // -D of the block's query rows (register jr: query qb*32 + 16 (jr/8)
         // + 8 half + jr%8): dP - D accumulates on the MFMA from it
@@ -555,13 +531,17 @@ attn_bwd_dkv2_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // register jr holds query qb*32 + 16*(jr/8) + 8*half + jr%8
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        const int q0 = qb * 32 + hh * 16 + half * 8;
+        const f32x4 l0 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4);
+        const f32x4 l1 = *(const f32x4 VDN_LDS*)(bb + SOFF + q0 * 4 + 16);
+        const float nl[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
         if constexpr (PASS == 0) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pk[qb * 2 + hh][e] = (bf16)fast_exp2(s[hh * 8 + e]);
+          for (int e = 0; e < 8; ++e) pk[qb * 2 + hh][e] = (bf16)fast_exp2(fmaf(s[hh * 8 + e], c, nl[e]));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float p = fast_exp2(s[hh * 8 + e]);
+            const float p = fast_exp2(fmaf(s[hh * 8 + e], c, nl[e]));
             pk[qb * 2 + hh][e] = (bf16)(p * dp[hh * 8 + e]);
           }
         }

@@ -382,12 +382,16 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //    MFMA / VALU work instead of stalling each MFMA pair.
 //  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
 //    both read with ds_read_b128 at base + immediate, conflict-free.
-//  * q is multiplied by scale * log2(e) and rounded to bf16 once per work
-//    item, and each score chain starts from -m (the query's exponent offset)
-//    instead of 0, so the MFMAs leave s * scale * log2(e) - m and the weights
-//    are one v_exp_f32 each: no FMA per score.  The rounding of the scaled q
-//    is of the same size as the bf16 rounding of the weights the P V product
-//    takes.  The linear read R q uses q as given (reloaded in the epilogue).
+//  * Inference modes: q is multiplied by scale * log2(e) and rounded to bf16
+//    once per work item, and each score chain starts from -m (the query's
+//    exponent offset) instead of 0, so the MFMAs leave s * scale * log2(e) - m
+//    and the weights are one v_exp_f32 each: no FMA per score.  The rounding
+//    of the scaled q perturbs each score by about 2^-9 of the size of its
+//    terms: invisible at the scale of unit keys against N(0, 1) queries, and
+//    up to 4x the layer's error against the oracle when q . k spans tens of
+//    exp2 units (still a third of the bf16 bound).  The linear read R q uses q
+//    as given (reloaded in the epilogue).  The training modes keep exact
+//    fp32 scores, since their log-sum-exp drives the backward.
 // MODE 0 writes the softmax branch O_soft; MODE 1 the merged output
 // sigmoid(l0) O_soft + sigmoid(l1) RMSNorm(R q); MODE 2 the two gated branches
 // side by side, o[b][n][0][h][:] = sigmoid(l0) O_soft and
@@ -443,12 +447,22 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const bool qvalid = qlocal < g.P;
   const int qrow = w.t * g.P + (qvalid ? qlocal : 0);
   const size_t qoff = ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * D;
-  bf16x8 qreg[D / 16];   // the scores' B operand: q * c in bf16
+  // PS: the scores' B operand is q * c rounded to bf16 and each score chain
+  // starts from -m (inference modes).  The training modes (3: merge
+  // backward, 5: training forward) keep exact fp32 scores, s * c - m by one
+  // FMA per score: their log-sum-exp feeds the backward, which recomputes
+  // the weights from q and k as given.
+  constexpr bool PS = MODE != 3 && MODE != 5;
+  bf16x8 qreg[D / 16];   // the scores' B operand
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 x = *(const bf16x8*)(q + qoff + ks * 16 + half * 8);
+    if constexpr (PS) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qreg[ks][e] = (bf16)((float)x[e] * c);
+      for (int e = 0; e < 8; ++e) qreg[ks][e] = (bf16)((float)x[e] * c);
+    } else {
+      qreg[ks] = x;
+    }
   }
 
   const int HD = H * D;
@@ -539,9 +553,10 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int vread = VOFF + (lane & 31) * VST + half * 16;
   const bool partial = (nkeys & (BN - 1)) != 0;
 
-  // m_run: the query's exponent offset (exp2 units); minit: -m_run in every
-  // element, the first score MFMA's accumulator input
-  float m_run = 0.f, l_run = 0.f;
+  // m_run: the query's exponent offset (PS: exp2 units, and minit holds
+  // -m_run in every element, the first score MFMA's accumulator input;
+  // otherwise score units, m_thr = m_run + 8 / c the lazy-rescale bound)
+  float m_run = PS ? 0.f : -1e30f, m_thr = -1e30f, l_run = 0.f;
   f32x16 minit = {};
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -565,17 +580,22 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // into it every tile (8 moves); the two products are independent and the
     // next MFMAs read their results as accumulator inputs, which needs no
     // wait states
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %5\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %5\n\t"
-                 "s_nop 1"
-                 : "=&v"(s[0]), "=&v"(s[1])
-                 : "v"(kf[0][0]), "v"(kf[1][0]), "v"(qreg[0]), "v"(minit));
+    if constexpr (PS) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %4, %5\n\t"
+                   "v_mfma_f32_32x32x16_bf16 %1, %3, %4, %5\n\t"
+                   "s_nop 1"
+                   : "=&v"(s[0]), "=&v"(s[1])
+                   : "v"(kf[0][0]), "v"(kf[1][0]), "v"(qreg[0]), "v"(minit));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][0], qreg[0], f32x16{});
+    }
 #pragma unroll
     for (int ks = 1; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ks], qreg[ks], s[kb]);
     __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 8 - 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, PS ? D / 8 - 2 : D / 8, 0);
   };
   // Online softmax of tile `it` (scores s, buffer buf) and O^T += V^T P^T.
   auto soft_pv = [&](int it, int buf, f32x16 (&s)[2]) {
@@ -609,23 +629,40 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // Lazy rescale: the exponent offset moves only when some query's max
     // passes it by more than 8 (exp2 units); until then p <= 256.  The first
     // tile sets it to the tile's max.
-    if (__builtin_amdgcn_ballot_w64(mx > 8.0f) != 0 || it == 0) {
-      const float dl = it == 0 ? mx : fmaxf(mx, 0.f);
-      const float corr = it == 0 ? 0.f : fast_exp2(-dl);
-      l_run *= corr;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
-      m_run += dl;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] -= dl;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) minit[j] = -m_run;
-    }
     bf16x8 pk[4];
+    if constexpr (PS) {
+      if (__builtin_amdgcn_ballot_w64(mx > 8.0f) != 0 || it == 0) {
+        const float dl = it == 0 ? mx : fmaxf(mx, 0.f);
+        const float corr = it == 0 ? 0.f : fast_exp2(-dl);
+        l_run *= corr;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+        m_run += dl;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(s[kb][j]);
+        for (int kb = 0; kb < 2; ++kb) s[kb] -= dl;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) minit[j] = -m_run;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(s[kb][j]);
+    } else {
+      if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = fast_exp2((m_run - m_new) * c);
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= corr;
+        m_run = m_new;
+        m_thr = m_new + 8.0f / c;
+      }
+      const float mc = m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) pk[kb * 2 + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(s[kb][j], c, -mc));
+    }
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
       const bf16x2* p2 = (const bf16x2*)&pk[sp];
@@ -681,7 +718,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // all global loads of the epilogue first: gate logits and this thread's
     // share of R (NR chunks of 8 floats)
     const float2 gl = *(const float2*)(gates + ((size_t)(w.b * (size_t)N + qrow) * H + w.h) * 2);
-    {
+    if constexpr (PS) {
       // reload the unscaled q (the asm keeps the compiler from reusing the
       // first load's registers across the loop)
       const bf16* qr = q;
@@ -765,7 +802,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dot0 = xhalf_sum(dot0);
       dot1 = xhalf_sum(dot1);
       dsum = xhalf_sum(dsum);
-      const float nlse2 = -(m_run + __log2f(1.0f / inv));   // -lse
+      const float nlse2 = -fmaf(m_run, c, __log2f(1.0f / inv));   // -lse
       if (qvalid) {
         bf16* dosrow = bio.dos + qoff;
         float* dlrow = bio.dlin + qoff;
@@ -821,7 +858,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
         if (half == 0) {
           const size_t ri = (size_t)(w.b * H + w.h) * N + qrow;
-          bio.nlse[ri] = -(m_run + __log2f(1.0f / inv));
+          bio.nlse[ri] = -fmaf(m_run, c, __log2f(1.0f / inv));
           bio.rinv[ri] = rinv;
         }
       }

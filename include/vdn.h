@@ -126,7 +126,11 @@ size_t vdn_hybrid_attn_workspace_size(const vdn_layout_t* layout);
  * VDA states of the query's chunk (the text write alone for anchor frames).
  * o must not alias any input.  workspace: device memory of at least
  * vdn_hybrid_attn_workspace_size(layout) bytes, 256-byte aligned; its contents
- * on entry are ignored.  [all sections cited above] */
+ * on entry are ignored.  Softmax scores (bf16 layouts, d >= 32, P and L
+ * multiples of 8): formed from q * scale * log2(e) rounded to bf16, which
+ * perturbs each score by about 2^-9 of its terms; with the environment
+ * variable VDN_EXACT_SCORES=1 (read at every call) they are formed exactly in
+ * float32 instead, about 4 % slower.  [all sections cited above] */
 vdn_status_t vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                  const void* text_k, const void* text_v,
                                  const float* beta, const float* alpha,

@@ -98,3 +98,39 @@ def test_backward_wide_scores(qscale):
     print(f"q x{qscale}", " ".join(f"{k_} {e:.2e}" for k_, e in errs.items()), flush=True)
     bad = {k_: e for k_, e in errs.items() if not e <= TOL["bf16"]}
     assert not bad, bad
+
+
+def test_exact_scores_switch():
+    """VDN_EXACT_SCORES=1 makes the layer form its softmax scores exactly in
+    fp32: its output is then the training forward's bit for bit, and at the
+    widest score spread its error against the oracle falls back to the FMA
+    form's.  The switch is read at every launch."""
+    import os
+    require_gpu()
+    case = dict(LAYER[0])
+    w = custom(**case)
+    print("\n[case] exact-score switch", flush=True)
+    inp = synth.make_inputs(w)
+    inp["q"] *= 128
+    inp["gate_logits"][..., 1] = -30.0
+    ref = O.hybrid_attn(inp, oracle_layout(w))
+    dev = to_dev(inp, w.dtype)
+    old = os.environ.get("VDN_EXACT_SCORES")
+    try:
+        os.environ["VDN_EXACT_SCORES"] = "1"
+        exact = V.hybrid_attn(*_args(w, dev), **_geo(w))
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["VDN_EXACT_SCORES"]
+        else:
+            os.environ["VDN_EXACT_SCORES"] = old
+    fast = V.hybrid_attn(*_args(w, dev), **_geo(w))
+    train, _ = V.hybrid_attn_fwd_train(*_args(w, dev), **_geo(w))
+    torch.cuda.synchronize()
+    assert torch.equal(exact.view(torch.int16), train.view(torch.int16))
+    e_exact = rel_err(exact.float().cpu().numpy(), ref)
+    e_fast = rel_err(fast.float().cpu().numpy(), ref)
+    print(f"q x128 softmax branch: exact scores {e_exact:.3e}, pre-scaled {e_fast:.3e}", flush=True)
+    assert e_exact <= e_fast
+    assert e_exact <= TOL[w.dtype]

@@ -23,6 +23,7 @@
 //  * exp2 with the scale * log2(e) folded into one FMA; fp32 statistics.
 //  * Work order: anchor-frame tiles (the heaviest) first; with B*H a multiple
 //    of 8 each XCD gets a fixed set of heads so K/V tiles are shared in its L2.
+#include <cstdlib>
 #include <type_traits>
 
 #include "softmax_common.h"
@@ -404,6 +405,8 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // the gradient of the linear read before RMSNorm.  MODE 4 writes the two
 // gated branches of MODE 2 as MXFP8 codes and block scales (the activation
 // operand of the FP8 output projection), quantized from the fp32 values.
+// MODE 6 is MODE 1 with exact fp32 scores (the layer's output as the
+// training forward computes it).
 // MODE 5 (training forward) writes MODE 1's output and keeps, for a later
 // backward, O_soft and n = RMSNorm(R q) in fp32 and per row the negated
 // log-sum-exp and the RMS factor 1/r.
@@ -452,7 +455,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // backward, 5: training forward) keep exact fp32 scores, s * c - m by one
   // FMA per score: their log-sum-exp feeds the backward, which recomputes
   // the weights from q and k as given.
-  constexpr bool PS = MODE != 3 && MODE != 5;
+  constexpr bool PS = MODE != 3 && MODE != 5 && MODE != 6;
   bf16x8 qreg[D / 16];   // the scores' B operand
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -894,7 +897,7 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       return;
     }
     if (qvalid) {
-      if constexpr (MODE == 1 || MODE == 5) {
+      if constexpr (MODE == 1 || MODE == 5 || MODE == 6) {
         bf16* orow = o + qoff;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -1257,6 +1260,15 @@ hipError_t launch_f32(const void* q, const void* k, const void* v, const void* t
   return hipGetLastError();
 }
 
+// VDN_EXACT_SCORES=1 in the environment (read at every launch): the layer's
+// fused softmax + merge forms its scores exactly in fp32, one FMA per score,
+// instead of from q * scale * log2(e) rounded to bf16 (about 4 % slower at
+// 768p; its output is then the training forward's, bit for bit).
+bool exact_scores() {
+  const char* e = getenv("VDN_EXACT_SCORES");
+  return e && e[0] == '1';
+}
+
 template <int D>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* tk,
                        const void* tv, const vdn_layout_t& l, float scale, void* o, void* ws,
@@ -1277,7 +1289,11 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const void* 
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    if (mode == 1)
+    if (mode == 1 && exact_scores())
+      softmax_vt_kernel<D, 6><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
+          l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, EpilogueIO{});
+    else if (mode == 1)
       softmax_vt_kernel<D, 1><<<dim3((unsigned)grid2), dim3(512), 0, s>>>(
           (const bf16*)q, (const bf16*)k, (const bf16*)tk, (const bf16*)ws, nl8, (bf16*)o, g,
           l.batch, l.heads, tpf2, scale * kLog2e, R, gates, eps, EpilogueIO{});

@@ -101,13 +101,13 @@ def max_abs_ratio(got, ref) -> float:
 
 
 def write_parity_summary(name: str, record: dict) -> None:
-    """Append one JSON line per checked configuration to
-    gpurun_out/parity_summary.jsonl under the repository root (a results
-    folder that is not part of the source tree)."""
+    """Append one JSON line per checked configuration to the file the
+    environment variable VDN_PARITY_SUMMARY names (nothing if it is unset)."""
     import json
     import os
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    out = os.path.join(root, "gpurun_out")
-    os.makedirs(out, exist_ok=True)
-    with open(os.path.join(out, "parity_summary.jsonl"), "a") as fh:
+    path = os.environ.get("VDN_PARITY_SUMMARY")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as fh:
         fh.write(json.dumps({"config": name, **record}) + "\n")

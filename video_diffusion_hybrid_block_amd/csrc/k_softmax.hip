@@ -410,6 +410,26 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // MODE 5 (training forward) writes MODE 1's output and keeps, for a later
 // backward, O_soft and n = RMSNorm(R q) in fp32 and per row the negated
 // log-sum-exp and the RMS factor 1/r.
+// Maximum of the 16 scores of one accumulator block: eight dependent
+// v_max3_f32 in one asm statement (one statement per chain: as separate
+// statements the compiler pads each with a wait state).
+__device__ __forceinline__ float max16_raw(const f32x16& x) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %0, %0, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %0, %0, %14, %15\n\t"
+      "v_max_f32 %0, %0, %16"
+      : "=&v"(r)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+        "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]),
+        "v"(x[14]), "v"(x[15]));
+  return r;
+}
+
 template <int D, int MODE>
 __global__ void __launch_bounds__(512)
 softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -621,14 +641,8 @@ softmax_vt_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           if (kb * 32 + ((j >> 3) << 4) + (j & 7) >= lim) s[kb][j] = -INFINITY;
     }
     // row max: two max3 chains over the 32 scores, then the partner half
-    float ma = max3_raw(s[0][0], s[0][1], s[0][2]), mb = max3_raw(s[1][0], s[1][1], s[1][2]);
-#pragma unroll
-    for (int j = 3; j < 15; j += 2) {
-      ma = max3_raw(ma, s[0][j], s[0][j + 1]);
-      mb = max3_raw(mb, s[1][j], s[1][j + 1]);
-    }
-    float mx = max3_raw(max3_raw(ma, mb, s[0][15]), s[1][15], s[1][15]);
-    mx = xhalf_max_raw(mx);
+    const float ma = max16_raw(s[0]), mb = max16_raw(s[1]);
+    float mx = xhalf_max_raw(max_raw(ma, mb));
     // Lazy rescale: the exponent offset moves only when some query's max
     // passes it by more than 8 (exp2 units); until then p <= 256.  The first
     // tile sets it to the tile's max.

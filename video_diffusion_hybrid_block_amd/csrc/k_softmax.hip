@@ -378,9 +378,10 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 //    tile i is processed.  A wave issues the same number of DMA instructions
 //    (NIW or NIW - 1) every tile, so "tile i+1 landed" is one s_waitcnt
 //    vmcnt on that count.
-//  * All K fragments of a tile are read from LDS before its score MFMAs and
-//    all V^T fragments before the softmax VALU work, so LDS latency overlaps
-//    MFMA / VALU work instead of stalling each MFMA pair.
+//  * All K fragments of a tile are read from LDS before its score MFMAs (the
+//    next tile's copies are issued while they are in flight) and all V^T
+//    fragments before the softmax VALU work, so LDS latency overlaps MFMA /
+//    VALU work instead of stalling each MFMA pair.
 //  * LDS rows: K padded to 2d+16 bytes, V^T (one d, 64 keys) to 144 bytes;
 //    both read with ds_read_b128 at base + immediate, conflict-free.
 //  * Inference modes: q is multiplied by scale * log2(e) and rounded to bf16
@@ -401,11 +402,10 @@ hipError_t launch_valu(const void* q, const void* k, const void* v, const void* 
 // of the merged output instead and writes what the backward needs: the gate
 // logits' gradients, dO_soft = sigmoid(l0) dO (bf16), the row statistics of
 // the softmax (its log-sum-exp in exp2 units and D = dO_soft . O_soft, both
-// negated) and
-// the gradient of the linear read before RMSNorm.  MODE 4 writes the two
-// gated branches of MODE 2 as MXFP8 codes and block scales (the activation
-// operand of the FP8 output projection), quantized from the fp32 values.
-// MODE 6 is MODE 1 with exact fp32 scores (the layer's output as the
+// negated) and the gradient of the linear read before RMSNorm.  MODE 4 writes
+// the two gated branches of MODE 2 as MXFP8 codes and block scales (the
+// activation operand of the FP8 output projection), quantized from the fp32
+// values.  MODE 6 is MODE 1 with exact fp32 scores (the layer's output as the
 // training forward computes it).
 // MODE 5 (training forward) writes MODE 1's output and keeps, for a later
 // backward, O_soft and n = RMSNorm(R q) in fp32 and per row the negated
